@@ -1,0 +1,232 @@
+"""Exact attention in numpy float64 (test infrastructure; see package docstring).
+
+The method's result is standard attention, softmax(Q K^T / sqrt(d)) V, and the
+pages state that the tiled method reaches it exactly (no approximation), so
+this oracle is that definition written out: it materialises each head's score
+matrix, applies the ordinary row softmax and multiplies by V. It contains no
+tiling, no online softmax and no split of the key axis.
+
+Sources (titles of the pages, with the part used):
+  [FIA] "FIA / FlashAttention" help-centre Q&A, section 1 (FlashAttention core
+        principle: the attention formula, exactness) and section 4 (the
+        causal flag of the packed-QKV call).
+  [FPA] "Flash Attention & Paged Attention" blog, "FA and the decode phase"
+        (Flash-Decoding: split the KV sequence, per-split partial result plus
+        LogSumExp, light reduction) and "2. PagedAttention" (fixed-size pages,
+        logical page table over non-contiguous physical memory).
+  [CRS] "FlashAttention attention inference optimisation" course, chapter 1,
+        section 1.2 (decode-time standard attention: Q [1,H,1,d], K/V
+        [1,H,seq,d], scores / sqrt(head_dim), softmax, weights @ V).
+  [ARC] "FlashAttention breakthrough architecture" article, "paged storage
+        system" (64-token blocks behind a page table).
+
+Readings where the pages leave a step open (each is stated where used):
+  * LSE is the natural log of the sum of exp over the scaled, unmasked scores
+    of one query row.
+  * Causal masking is aligned bottom-right: key j is visible to query i iff
+    j <= i + (Sk - Sq). A row with no visible key has O = 0, LSE = -inf.
+  * GQA: query head h reads KV head h // (Hq / Hkv) unless a map is given.
+  * fp8 KV values are OCP e4m3fn codes times a per-(page, KV head) scale.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+NEG_INF = -np.inf
+PAGE = 64
+
+
+# --------------------------------------------------------------------------
+# Steps of the definition, one head at a time.
+# --------------------------------------------------------------------------
+
+def scores(q: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
+    """s_ij = scale * <q_i, k_j>  ([FIA] section 1 formula; [CRS] 1.2).
+
+    ``q`` [R, D], ``k`` [Sk, D], float64. ``scale`` is the fp32 value the GPU
+    receives, widened exactly.
+    """
+    return float(scale) * (q @ k.T)
+
+
+def causal_allowed(rows: np.ndarray, Sq: int, Sk: int) -> np.ndarray:
+    """Boolean [R, Sk]: key j visible to query row i iff j <= i + (Sk - Sq).
+
+    [FIA] section 4 passes causal=True; bottom-right alignment is the reading
+    for Sq != Sk (it reduces to j <= i when Sq == Sk and to "all keys" for a
+    single decode query at the end of the context).
+    """
+    return np.arange(Sk)[None, :] <= (np.asarray(rows)[:, None] + (Sk - Sq))
+
+
+def softmax_rows(s: np.ndarray):
+    """Row softmax of a score block with -inf entries meaning "masked".
+
+    Returns (P, m, l): m_i = max_j s_ij, l_i = sum_j exp(s_ij - m_i),
+    P_ij = exp(s_ij - m_i) / l_i. Rows that are entirely masked get P = 0,
+    m = -inf, l = 0. ([CRS] 1.2: weights = softmax(scores).)
+    """
+    m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], NEG_INF)
+    empty = ~np.isfinite(m)
+    shift = np.where(empty, 0.0, m)
+    e = np.exp(s - shift[:, None])
+    l = e.sum(axis=1)
+    P = e / np.where(empty, 1.0, l)[:, None]
+    return P, m, l
+
+
+def attention_head(q, k, v, scale, causal=False, rows=None):
+    """One head of exact attention, optionally only for some query rows.
+
+    ``q`` [Sq, D], ``k`` [Sk, D], ``v`` [Sk, Dv] float64. Returns
+    (O [R, Dv], LSE [R]) for ``rows`` (default: all Sq rows).
+    O = P V ([CRS] 1.2: output = weights @ V); LSE = m + ln l.
+    """
+    Sq, Sk = q.shape[0], k.shape[0]
+    rows = np.arange(Sq) if rows is None else np.asarray(rows)
+    s = scores(q[rows], k, scale)
+    if causal:
+        s = np.where(causal_allowed(rows, Sq, Sk), s, NEG_INF)
+    P, m, l = softmax_rows(s)
+    o = P @ v if Sk else np.zeros((len(rows), v.shape[1]))
+    lse = np.where(np.isfinite(m), m + np.log(np.where(l > 0, l, 1.0)), NEG_INF)
+    return o, lse
+
+
+def kv_head_of(h: int, Hq: int, Hkv: int, kv_head_map=None) -> int:
+    """KV head read by query head h ([FIA] section 3: grouped-query attention).
+
+    Default grouping is contiguous: h // (Hq / Hkv).
+    """
+    if kv_head_map is not None:
+        return int(kv_head_map[h])
+    return h // (Hq // Hkv)
+
+
+# --------------------------------------------------------------------------
+# Prefill: B x Hq heads of the definition.
+# --------------------------------------------------------------------------
+
+def prefill(q, k, v, scale, causal, kv_head_map=None, row_block=512, heads=None,
+            rows=None):
+    """Exact attention over BHSD tensors.
+
+    q [B, Hq, Sq, D], k/v [B, Hkv, Sk, D] float64 (or anything numpy widens
+    exactly). Returns O [B, Hq, R, D] and LSE [B, Hq, R] where R = Sq, or the
+    given ``rows``. ``heads`` restricts to a list of (b, h) pairs, returned in
+    that order as O [n, R, D], LSE [n, R]. Scores are materialised
+    ``row_block`` rows at a time (memory only; every row is independent).
+    """
+    B, Hq, Sq, D = q.shape
+    Hkv = k.shape[1]
+    rows = np.arange(Sq) if rows is None else np.asarray(rows)
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
+    O = np.zeros((len(pairs), len(rows), v.shape[3]))
+    LSE = np.zeros((len(pairs), len(rows)))
+    for n, (b, h) in enumerate(pairs):
+        g = kv_head_of(h, Hq, Hkv, kv_head_map)
+        qh = np.asarray(q[b, h], dtype=np.float64)
+        kh = np.asarray(k[b, g], dtype=np.float64)
+        vh = np.asarray(v[b, g], dtype=np.float64)
+        for r0 in range(0, len(rows), row_block):
+            rr = rows[r0:r0 + row_block]
+            O[n, r0:r0 + len(rr)], LSE[n, r0:r0 + len(rr)] = attention_head(
+                qh, kh, vh, scale, causal, rr)
+    if heads is None:
+        O = O.reshape(B, Hq, len(rows), -1)
+        LSE = LSE.reshape(B, Hq, len(rows))
+    return O, LSE
+
+
+# --------------------------------------------------------------------------
+# Decode over a paged KV cache.
+# --------------------------------------------------------------------------
+
+def e4m3fn_to_float(codes) -> np.ndarray:
+    """Decode OCP 8-bit e4m3fn codes to float64 from the format's definition.
+
+    Bit layout s eeee mmm, exponent bias 7. e = 0: subnormal m/8 * 2^-6;
+    otherwise (1 + m/8) * 2^(e-7); the two codes s1111111 are NaN; there is
+    no infinity (max finite 448). The pages name FP8 KV kernels ([FIA]
+    section 3) without the format; e4m3fn is the reading because a scale of
+    max|x|/448 maps the largest value onto this format's largest finite value.
+    """
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def gather_pages(pool, table_row, L: int, g: int, scale=None):
+    """Logical token sequence of one request and KV head from a paged pool.
+
+    ``pool`` [P, Hkv, 64, D] (float values, or uint8 e4m3fn codes when
+    ``scale`` [P, Hkv] is given). Logical page j of the request is physical
+    page ``table_row[j]`` ([FPA] "2. PagedAttention": fixed-size pages and a
+    logical-to-physical table; [ARC]: 64-token blocks). Returns [L, D] float64,
+    the pages concatenated in logical order and cut to L tokens.
+    """
+    n = (L + PAGE - 1) // PAGE
+    if n == 0:
+        return np.zeros((0, pool.shape[3]))
+    ids = np.asarray(table_row[:n], dtype=np.int64)
+    blocks = np.asarray(pool[ids, g])  # [n, 64, D]
+    if scale is not None:
+        vals = e4m3fn_to_float(blocks) * np.asarray(scale, dtype=np.float64)[ids, g][:, None, None]
+    else:
+        vals = blocks.astype(np.float64)
+    return vals.reshape(n * PAGE, -1)[:L]
+
+
+def paged_decode(q, k_pages, v_pages, page_table, seqlens, scale,
+                 k_scale=None, v_scale=None, requests=None):
+    """Single-token decode attention against each request's whole cache.
+
+    q [B, Hq, D]; pools [P, Hkv, 64, D]; page_table [B, max_pages]; seqlens [B].
+    For each request b and query head h: gather the L_b cached tokens of KV
+    head g(h), then one query row of exact attention over all of them, no mask
+    ([CRS] 1.2: the current query sees the whole cache). Returns O [B, Hq, D],
+    LSE [B, Hq] (or [n, Hq, D] / [n, Hq] for ``requests``).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv = k_pages.shape[1]
+    reqs = range(B) if requests is None else list(requests)
+    O = np.zeros((len(reqs), Hq, v_pages.shape[3]))
+    LSE = np.zeros((len(reqs), Hq))
+    for n, b in enumerate(reqs):
+        L = int(seqlens[b])
+        for g in range(Hkv):
+            kb = gather_pages(k_pages, page_table[b], L, g, k_scale)
+            vb = gather_pages(v_pages, page_table[b], L, g, v_scale)
+            for h in range(Hq):
+                if kv_head_of(h, Hq, Hkv) != g:
+                    continue
+                o, lse = attention_head(q[b, h][None, :], kb, vb, scale, False)
+                O[n, h], LSE[n, h] = o[0], lse[0]
+    return O, LSE
+
+
+def lse_merge(partial_o, partial_lse):
+    """Merge per-split attention results by their LogSumExp ([FPA] Flash-Decoding).
+
+    Split s holds O_s (normalised over its own keys) and lse_s. The exact
+    result over the union of the splits is lse = ln sum_s exp(lse_s) and
+    O = sum_s exp(lse_s - lse) O_s. Splits with lse_s = -inf (no keys) weigh 0;
+    if every split is empty the result is O = 0, lse = -inf.
+    ``partial_o`` [n, D], ``partial_lse`` [n].
+    """
+    lse_s = np.asarray(partial_lse, dtype=np.float64)
+    o_s = np.asarray(partial_o, dtype=np.float64)
+    finite = np.isfinite(lse_s)
+    if not finite.any():
+        return np.zeros(o_s.shape[1]), NEG_INF
+    mx = lse_s[finite].max()
+    w = np.where(finite, np.exp(np.where(finite, lse_s, 0.0) - mx), 0.0)
+    tot = w.sum()
+    lse = mx + np.log(tot)
+    o = (w / tot) @ o_s
+    return o, lse

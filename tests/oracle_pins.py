@@ -1,0 +1,371 @@
+"""Pins that tie the fp64 oracle to facts other than itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+a closed form, an invariant of exact attention, a hand-derived worked example
+(``tests/golden/hand_examples.json``), brute force on tiny inputs or a library
+routine that computes the same quantity. The functions look up the oracle's
+steps through the module object at call time, so ``test_oracle_mutations``
+can plant a mistake in one step and check that some pin fails.
+
+Tolerances: closed forms and identities hold to ~1e-12 in fp64; "bitwise"
+pins compare exact equality.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+from oracle import attention as A
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")
+
+
+def _ev(expr):
+    return float(eval(expr, {"__builtins__": {}}, {"log": math.log, "inf": math.inf,
+                                                   "nan": math.nan}))
+
+
+def _arr(rows):
+    return np.array([[_ev(x) for x in r] for r in rows], dtype=np.float64)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
+    with np.errstate(invalid="ignore"):
+        err = np.where(both_inf, 0.0, np.abs(a - b))
+    assert np.all(np.isfinite(err)), f"{what}: non-finite mismatch"
+    assert err.max(initial=0.0) <= tol, f"{what}: max err {err.max():.3e} > {tol:.1e}"
+
+
+# --------------------------------------------------------------------------
+# Closed forms
+# --------------------------------------------------------------------------
+
+def pin_golden_attention():
+    """Hand-derived worked examples (closed forms) for attention rows."""
+    for ex in json.load(open(GOLDEN))["attention"]:
+        q, k, v = _arr(ex["q"]), _arr(ex["k"]), _arr(ex["v"])
+        o, lse = A.attention_head(q, k, v, _ev(ex["scale"]), ex["causal"])
+        _close(o, _arr(ex["o"]), 1e-12, ex["name"] + " O")
+        _close(lse, [_ev(x) for x in ex["lse"]], 1e-12, ex["name"] + " LSE")
+        # the same example through the batched prefill entry
+        O, L = A.prefill(q[None, None], k[None, None], v[None, None], _ev(ex["scale"]), ex["causal"])
+        _close(O[0, 0], _arr(ex["o"]), 1e-12, ex["name"] + " prefill O")
+        _close(L[0, 0], [_ev(x) for x in ex["lse"]], 1e-12, ex["name"] + " prefill LSE")
+
+
+def pin_golden_merge():
+    for ex in json.load(open(GOLDEN))["lse_merge"]:
+        o, lse = A.lse_merge(_arr(ex["partial_o"]), [_ev(x) for x in ex["partial_lse"]])
+        _close(o, [_ev(x) for x in ex["o"]], 1e-12, ex["name"] + " O")
+        _close(lse, _ev(ex["lse"]), 1e-12, ex["name"] + " LSE")
+
+
+def pin_golden_e4m3fn():
+    codes = json.load(open(GOLDEN))["e4m3fn"]["codes"]
+    for c, expr in codes.items():
+        got = float(A.e4m3fn_to_float(np.array([int(c)], dtype=np.uint8))[0])
+        want = _ev(expr)
+        if math.isnan(want):
+            assert math.isnan(got), f"code {c}: {got} is not NaN"
+        else:
+            assert got == want and math.copysign(1, got) == math.copysign(1, want), \
+                f"code {c}: {got} != {want}"
+
+
+def pin_golden_gather():
+    ex = json.load(open(GOLDEN))["paged_gather"]
+    P = ex["num_pages"]
+    pool = (100.0 * np.arange(P)[:, None] + np.arange(64)[None, :])[:, None, :, None]  # [P,1,64,1]
+    got = A.gather_pages(pool, np.array(ex["table"]), ex["L"], 0)[:, 0]
+    assert got.shape == (ex["L"],)
+    assert list(got[:3]) == ex["expected_first"]
+    assert got[63] == ex["expected_at_63"]
+    assert list(got[64:]) == ex["expected_tail"]
+
+
+def pin_identical_keys():
+    """All keys equal -> uniform weights -> O = mean(V) (causal: prefix mean)."""
+    g = _rng(1)
+    Sq = Sk = 9
+    q = g.standard_normal((Sq, 5))
+    k = np.repeat(g.standard_normal((1, 5)), Sk, axis=0)
+    v = g.standard_normal((Sk, 3))
+    o, lse = A.attention_head(q, k, v, 0.7, False)
+    _close(o, np.repeat(v.mean(axis=0, keepdims=True), Sq, axis=0), 1e-12, "identical keys")
+    s0 = 0.7 * q @ k[0]
+    _close(lse, s0 + math.log(Sk), 1e-12, "identical keys LSE")
+    o, lse = A.attention_head(q, k, v, 0.7, True)
+    pref = np.cumsum(v, axis=0) / np.arange(1, Sk + 1)[:, None]
+    _close(o, pref, 1e-12, "identical keys causal")
+    _close(lse, s0 + np.log(np.arange(1, Sk + 1)), 1e-12, "identical keys causal LSE")
+
+
+def pin_dominant_score():
+    """One key far ahead of the rest (gap >= 60 in the exponent) -> O = that V row."""
+    g = _rng(2)
+    D, Sk = 8, 20
+    q = g.standard_normal((1, D))
+    k = g.standard_normal((Sk, D)) * 0.1
+    j = 13
+    k[j] = 200.0 * q[0] / np.linalg.norm(q[0])
+    v = g.standard_normal((Sk, 4))
+    o, lse = A.attention_head(q, k, v, 1.0, False)
+    gap = float(q[0] @ k[j]) - max(float(q[0] @ k[i]) for i in range(Sk) if i != j)
+    assert gap > 60
+    _close(o[0], v[j], 1e-12, "dominant score")
+    _close(lse[0], float(q[0] @ k[j]), 1e-12, "dominant LSE")
+
+
+def pin_single_key():
+    g = _rng(3)
+    q, k, v = g.standard_normal((4, 6)), g.standard_normal((1, 6)), g.standard_normal((1, 6))
+    o, lse = A.attention_head(q, k, v, 0.3, False)
+    _close(o, np.repeat(v, 4, axis=0), 0.0, "single key O")
+    _close(lse, 0.3 * (q @ k[0]), 1e-12, "single key LSE")
+
+
+def pin_causal_row0():
+    g = _rng(4)
+    q, k, v = g.standard_normal((7, 6)), g.standard_normal((7, 6)), g.standard_normal((7, 6))
+    o, lse = A.attention_head(q, k, v, 0.5, True)
+    _close(o[0], v[0], 0.0, "causal row 0")
+    _close(lse[0], 0.5 * float(q[0] @ k[0]), 1e-12, "causal row 0 LSE")
+
+
+def pin_empty_rows():
+    """Causal with Sq > Sk: rows with no visible key are O = 0, LSE = -inf (reading)."""
+    g = _rng(5)
+    q, k, v = g.standard_normal((5, 4)), g.standard_normal((3, 4)), g.standard_normal((3, 4))
+    o, lse = A.attention_head(q, k, v, 1.0, True)
+    assert np.all(o[:2] == 0) and np.all(np.isneginf(lse[:2]))
+    _close(o[2], v[0], 0.0, "first visible row")
+    o, lse = A.attention_head(q, k[:0], v[:0], 1.0, False)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+# --------------------------------------------------------------------------
+# Brute force
+# --------------------------------------------------------------------------
+
+def _brute(q, k, v, scale, causal):
+    """Pure-Python triple loops, math.fsum / math.exp: the textbook formula."""
+    Sq, Sk, D = len(q), len(k), len(q[0])
+    O, L = [], []
+    for i in range(Sq):
+        s = []
+        for j in range(Sk):
+            if causal and j > i + (Sk - Sq):
+                continue
+            s.append((j, scale * math.fsum(q[i][d] * k[j][d] for d in range(D))))
+        if not s:
+            O.append([0.0] * len(v[0]))
+            L.append(-math.inf)
+            continue
+        mx = max(x for _, x in s)
+        w = [(j, math.exp(x - mx)) for j, x in s]
+        tot = math.fsum(x for _, x in w)
+        O.append([math.fsum(x * v[j][d] for j, x in w) / tot for d in range(len(v[0]))])
+        L.append(mx + math.log(tot))
+    return np.array(O), np.array(L)
+
+
+def pin_brute_force():
+    g = _rng(6)
+    for Sq, Sk, D, causal in [(1, 1, 1, False), (3, 5, 2, False), (5, 5, 4, True),
+                              (4, 7, 3, True), (8, 8, 4, False), (6, 3, 4, True)]:
+        q, k, v = g.standard_normal((Sq, D)), g.standard_normal((Sk, D)), g.standard_normal((Sk, D))
+        o, lse = A.attention_head(q, k, v, 0.8, causal)
+        bo, bl = _brute(q.tolist(), k.tolist(), v.tolist(), 0.8, causal)
+        _close(o, bo, 1e-13, f"brute O {Sq}x{Sk}")
+        _close(lse, bl, 1e-13, f"brute LSE {Sq}x{Sk}")
+
+
+# --------------------------------------------------------------------------
+# Invariants
+# --------------------------------------------------------------------------
+
+def pin_causal_dependency():
+    """Perturbing K/V at positions j > i leaves causal row i bit-identical."""
+    g = _rng(7)
+    S, D = 16, 8
+    q, k, v = g.standard_normal((S, D)), g.standard_normal((S, D)), g.standard_normal((S, D))
+    o, lse = A.attention_head(q, k, v, 0.4, True)
+    for i in (0, 5, 11):
+        k2, v2 = k.copy(), v.copy()
+        k2[i + 1:] += g.standard_normal((S - i - 1, D)) * 3
+        v2[i + 1:] += g.standard_normal((S - i - 1, D)) * 3
+        o2, lse2 = A.attention_head(q, k2, v2, 0.4, True)
+        assert np.array_equal(o2[i], o[i]) and lse2[i] == lse[i], f"row {i} changed"
+        assert not np.array_equal(o2[i + 1:], o[i + 1:]), "later rows must change"
+
+
+def pin_shift_invariance():
+    """k_j -> k_j + u for all j: O unchanged, LSE shifts by scale * q.u."""
+    g = _rng(8)
+    q, k, v = g.standard_normal((6, 5)), g.standard_normal((9, 5)), g.standard_normal((9, 5))
+    u = g.standard_normal(5)
+    o, lse = A.attention_head(q, k, v, 0.6, False)
+    o2, lse2 = A.attention_head(q, k + u, v, 0.6, False)
+    _close(o2, o, 1e-12, "shift O")
+    _close(lse2, lse + 0.6 * (q @ u), 1e-12, "shift LSE")
+
+
+def pin_key_permutation():
+    g = _rng(9)
+    q, k, v = g.standard_normal((6, 5)), g.standard_normal((9, 5)), g.standard_normal((9, 3))
+    p = g.permutation(9)
+    o, lse = A.attention_head(q, k, v, 0.6, False)
+    o2, lse2 = A.attention_head(q, k[p], v[p], 0.6, False)
+    _close(o2, o, 1e-12, "perm O")
+    _close(lse2, lse, 1e-12, "perm LSE")
+
+
+def pin_convex_hull():
+    g = _rng(10)
+    q, k, v = g.standard_normal((12, 4)) * 3, g.standard_normal((12, 4)), g.standard_normal((12, 6))
+    o, _ = A.attention_head(q, k, v, 1.0, True)
+    for i in range(12):
+        lo, hi = v[:i + 1].min(axis=0), v[:i + 1].max(axis=0)
+        assert np.all(o[i] >= lo - 1e-12) and np.all(o[i] <= hi + 1e-12), f"row {i} outside hull"
+
+
+def pin_gqa_expansion():
+    """GQA equals MHA on K/V repeated per group; an explicit map is honoured."""
+    g = _rng(11)
+    B, Hq, Hkv, S, D = 2, 6, 2, 10, 4
+    q = g.standard_normal((B, Hq, S, D))
+    k = g.standard_normal((B, Hkv, S, D))
+    v = g.standard_normal((B, Hkv, S, D))
+    O, L = A.prefill(q, k, v, 0.5, True)
+    ke, ve = np.repeat(k, Hq // Hkv, axis=1), np.repeat(v, Hq // Hkv, axis=1)
+    O2, L2 = A.prefill(q, ke, ve, 0.5, True)
+    assert np.array_equal(O, O2) and np.array_equal(L, L2)
+    hmap = [1, 0, 1, 1, 0, 0]
+    O3, _ = A.prefill(q, k, v, 0.5, True, kv_head_map=hmap)
+    O4, _ = A.prefill(q, k[:, hmap], v[:, hmap], 0.5, True, kv_head_map=list(range(Hq)))
+    assert np.array_equal(O3, O4)
+
+
+def pin_lse_merge_identity():
+    """Splitting the keys into chunks and merging by LSE equals the unsplit result."""
+    g = _rng(12)
+    q, k, v = g.standard_normal((3, 8)), g.standard_normal((50, 8)), g.standard_normal((50, 8))
+    o, lse = A.attention_head(q, k, v, 0.35, False)
+    for cuts in ([10, 11, 30], [0, 25], [49], [7, 7, 7, 40]):
+        edges = [0] + list(cuts) + [50]
+        for i in range(3):
+            parts = [A.attention_head(q[i:i + 1], k[a:b], v[a:b], 0.35, False)
+                     for a, b in zip(edges[:-1], edges[1:])]
+            mo, ml = A.lse_merge(np.array([p[0][0] for p in parts]), np.array([p[1][0] for p in parts]))
+            _close(mo, o[i], 1e-12, f"merge O {cuts}")
+            _close(ml, lse[i], 1e-12, f"merge LSE {cuts}")
+
+
+def pin_paged_equals_contiguous():
+    """A randomly permuted paged pool gives results bit-identical to the contiguous layout."""
+    g = _rng(13)
+    B, Hq, Hkv, D = 3, 4, 2, 8
+    L = np.array([1, 130, 64])
+    n = (L + 63) // 64
+    P = int(n.sum())
+    perm = g.permutation(P)
+    table = np.full((B, 4), -1)
+    contig_k = [g.standard_normal((Hkv, n[b] * 64, D)) for b in range(B)]
+    contig_v = [g.standard_normal((Hkv, n[b] * 64, D)) for b in range(B)]
+    kp = np.full((P, Hkv, 64, D), np.nan)
+    vp = np.full((P, Hkv, 64, D), np.nan)
+    off = 0
+    for b in range(B):
+        for j in range(n[b]):
+            pid = perm[off + j]
+            table[b, j] = pid
+            kp[pid] = contig_k[b][:, 64 * j:64 * j + 64]
+            vp[pid] = contig_v[b][:, 64 * j:64 * j + 64]
+            if 64 * (j + 1) > L[b]:  # tail beyond the request stays NaN in the pool
+                t = L[b] - 64 * j
+                kp[pid][:, t:] = np.nan
+                vp[pid][:, t:] = np.nan
+        off += n[b]
+    q = g.standard_normal((B, Hq, D))
+    O, LSE = A.paged_decode(q, kp, vp, table, L, 0.3)
+    for b in range(B):
+        for h in range(Hq):
+            gg = h // (Hq // Hkv)
+            o, lse = A.attention_head(q[b, h][None], contig_k[b][gg, :L[b]], contig_v[b][gg, :L[b]], 0.3)
+            assert np.array_equal(O[b, h], o[0]) and LSE[b, h] == lse[0], f"paged != contiguous ({b},{h})"
+
+
+# --------------------------------------------------------------------------
+# Library routines computing the same quantity
+# --------------------------------------------------------------------------
+
+def pin_torch_sdpa():
+    """O equals torch's CPU scaled_dot_product_attention in float64 (square shapes)."""
+    g = _rng(14)
+    B, Hq, Hkv, S, D = 2, 4, 2, 33, 16
+    q = g.standard_normal((B, Hq, S, D))
+    k = g.standard_normal((B, Hkv, S, D))
+    v = g.standard_normal((B, Hkv, S, D))
+    for causal in (False, True):
+        O, _ = A.prefill(q, k, v, 0.21, causal)
+        ke = torch.from_numpy(np.repeat(k, Hq // Hkv, axis=1))
+        ve = torch.from_numpy(np.repeat(v, Hq // Hkv, axis=1))
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), ke, ve, is_causal=causal, scale=0.21).numpy()
+        _close(O, ref, 1e-12, f"sdpa causal={causal}")
+
+
+def pin_torch_logsumexp():
+    """LSE equals torch.logsumexp of torch-computed scaled scores (masked entries dropped)."""
+    g = _rng(15)
+    Sq, Sk, D = 6, 11, 8
+    q, k, v = g.standard_normal((Sq, D)), g.standard_normal((Sk, D)), g.standard_normal((Sk, D))
+    for causal in (False, True):
+        _, lse = A.attention_head(q, k, v, 0.9, causal)
+        s = 0.9 * torch.from_numpy(q) @ torch.from_numpy(k).T
+        if causal:
+            keep = torch.arange(Sk)[None, :] <= torch.arange(Sq)[:, None] + (Sk - Sq)
+            s = s.masked_fill(~keep, float("-inf"))
+        _close(lse, torch.logsumexp(s, dim=1).numpy(), 1e-12, f"logsumexp causal={causal}")
+
+
+def pin_e4m3fn_vs_torch():
+    """All 256 e4m3fn codes decode like torch's float8_e4m3fn -> float32 cast."""
+    codes = np.arange(256, dtype=np.uint8)
+    mine = A.e4m3fn_to_float(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(mine[~nan]), np.signbit(ref[~nan]))
+
+
+def pin_fp8_paged_dequant():
+    """The fp8 paged gather equals torch's dequantisation codes.float() * scale."""
+    g = _rng(16)
+    P, Hkv, D = 5, 2, 8
+    codes = g.integers(0, 256, size=(P, Hkv, 64, D)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38  # no NaN codes in this check
+    scale = g.uniform(0.01, 2.0, size=(P, Hkv)).astype(np.float32)
+    table = np.array([3, 0, 4])
+    L = 150
+    for gg in range(Hkv):
+        got = A.gather_pages(codes, table, L, gg, scale)
+        t = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64)
+        ref = (t[table, gg] * torch.from_numpy(scale).double()[table, gg][:, None, None]).reshape(-1, D)[:L]
+        _close(got, ref.numpy(), 0.0, f"fp8 gather head {gg}")
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

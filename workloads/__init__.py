@@ -1,0 +1,232 @@
+"""Seeded synthetic inputs for the exact-attention workloads.
+
+This module only draws random numbers and lays them out; it holds none of the
+attention arithmetic. Both the fp64 oracle (via the tests) and the HIP path
+(via the tests and the benchmark) receive exactly the tensors built here.
+
+Recipe (every tensor is reproducible from ``(workload id, stream)``):
+
+* ``numpy.random.default_rng([workload_id, stream])`` with streams
+  0 = context lengths, 1 = physical page permutation, 2 = Q, 3 = K, 4 = V.
+* Values are i.i.d. standard normal drawn in float32, then rounded to bf16 with
+  round-to-nearest-even (torch's CPU cast) for the bf16 workloads; the fp32
+  workload keeps the float32 draw.
+* Paged KV pools are ``[num_pages, H_kv, 64, D]``; request ``b``'s logical
+  page ``j`` lives at physical page ``perm[offset_b + j]`` where ``perm`` is a
+  random permutation of all pages and ``offset_b`` the sum of the earlier
+  requests' page counts. Unused page-table entries are ``-1``.
+* Token slots past a request's length on its last page are filled with NaN
+  when ``nan_tails`` is set, so that a kernel that reads them without masking
+  produces NaN.
+* fp8 pools: float32 N(0,1) data, one fp32 scale per (page, KV head) equal to
+  ``max|x| / 448`` over that page's valid tokens (1.0 if that max is 0), codes
+  = OCP e4m3fn round-to-nearest-even of ``x / scale`` (torch's CPU cast),
+  stored as uint8.
+
+Workload ids 1..5 are the five configurations the pages' workloads suggest:
+a tiny fp32 case, a 4096-token causal bf16 prefill, a 32768-token GQA prefill
+(about the ~30K-token document of the FlashAttention course's case study), a
+64-request ragged paged decode and an 8-request long-context fp8 paged decode.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+PAGE = 64  # tokens per KV page
+
+STREAM_LENGTHS, STREAM_PERM, STREAM_Q, STREAM_K, STREAM_V = 0, 1, 2, 3, 4
+
+
+@dataclass(frozen=True)
+class PrefillWorkload:
+    wid: int
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    S: int
+    D: int
+    dtype: str  # "f32" | "bf16"
+    causal: tuple = (True,)
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.D)))
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    wid: int
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    kv_dtype: str  # "bf16" | "fp8"
+    lengths: tuple = field(default=("uniform", 512, 16384))
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.D)))
+
+
+WORKLOADS = {
+    1: PrefillWorkload(1, "tiny_fp32_b1_h2_s128_d64", 1, 2, 2, 128, 64, "f32", (False, True)),
+    2: PrefillWorkload(2, "causal_prefill_bf16_b4_h32_s4096_d128", 4, 32, 32, 4096, 128, "bf16", (True,)),
+    3: PrefillWorkload(3, "gqa_prefill_bf16_b1_hq32_hkv8_s32768_d128", 1, 32, 8, 32768, 128, "bf16", (True,)),
+    4: DecodeWorkload(4, "paged_decode_bf16_b64_hq32_hkv8_d128_L512-16384", 64, 32, 8, 128, "bf16",
+                      ("uniform", 512, 16384)),
+    5: DecodeWorkload(5, "paged_decode_fp8_b8_hq32_hkv8_d128_L4096-131072", 8, 32, 8, 128, "fp8",
+                      ("loguniform", 4096, 131072)),
+}
+
+
+def rng(wid: int, stream: int) -> np.random.Generator:
+    return np.random.default_rng([wid, stream])
+
+
+def normal(wid: int, stream: int, shape, dtype: str) -> torch.Tensor:
+    """i.i.d. N(0,1) drawn in float32, then cast (RNE) to ``dtype`` on the CPU."""
+    x = rng(wid, stream).standard_normal(size=shape, dtype=np.float32)
+    t = torch.from_numpy(x)
+    if dtype == "f32":
+        return t
+    if dtype == "bf16":
+        return t.to(torch.bfloat16)
+    raise ValueError(dtype)
+
+
+def prefill_inputs(B, Hq, Hkv, Sq, Sk, D, dtype, wid):
+    """Contiguous BHSD q [B,Hq,Sq,D], k/v [B,Hkv,Sk,D] on the CPU."""
+    q = normal(wid, STREAM_Q, (B, Hq, Sq, D), dtype)
+    k = normal(wid, STREAM_K, (B, Hkv, Sk, D), dtype)
+    v = normal(wid, STREAM_V, (B, Hkv, Sk, D), dtype)
+    return q, k, v
+
+
+def workload_prefill_inputs(w: PrefillWorkload):
+    return prefill_inputs(w.B, w.Hq, w.Hkv, w.S, w.S, w.D, w.dtype, w.wid)
+
+
+def context_lengths(wid: int, B: int, spec) -> np.ndarray:
+    """Per-request context lengths, int32 [B].
+
+    ("uniform", lo, hi): integers uniform on [lo, hi] inclusive.
+    ("loguniform", lo, hi): rint(exp(U(ln lo, ln hi))) clipped to [lo, hi].
+    ("fixed", L): every request has length L (L may be 0).
+    ("list", [...]): the given lengths.
+    """
+    kind = spec[0]
+    g = rng(wid, STREAM_LENGTHS)
+    if kind == "uniform":
+        L = g.integers(spec[1], spec[2], size=B, endpoint=True)
+    elif kind == "loguniform":
+        u = g.uniform(math.log(spec[1]), math.log(spec[2]), size=B)
+        L = np.clip(np.rint(np.exp(u)), spec[1], spec[2])
+    elif kind == "fixed":
+        L = np.full(B, spec[1])
+    elif kind == "list":
+        L = np.asarray(spec[1])
+        assert L.shape == (B,)
+    else:
+        raise ValueError(kind)
+    return L.astype(np.int32)
+
+
+@dataclass
+class PagedKV:
+    """A paged decode batch, all host (CPU) tensors."""
+    q: torch.Tensor            # [B, Hq, D] bf16
+    k_pages: torch.Tensor      # [P, Hkv, 64, D] bf16, or uint8 e4m3fn codes
+    v_pages: torch.Tensor
+    k_scale: torch.Tensor | None  # [P, Hkv] f32 (fp8 only)
+    v_scale: torch.Tensor | None
+    page_table: torch.Tensor   # [B, max_pages] int32, -1 where unused
+    seqlens: torch.Tensor      # [B] int32
+    kv_dtype: str
+    num_pages: int
+
+    @property
+    def B(self):
+        return self.q.shape[0]
+
+
+def paged_inputs(B, Hq, Hkv, D, kv_dtype, lengths, wid, nan_tails=True,
+                 max_pages=None, extra_pages=0) -> PagedKV:
+    """Build a paged decode batch.
+
+    ``lengths`` is a length spec (see ``context_lengths``) or an int array.
+    ``max_pages`` sets the page-table row stride (default: the largest
+    request's page count, at least 1). ``extra_pages`` adds never-referenced
+    pages to the pool.
+    """
+    if isinstance(lengths, (tuple, list)) and lengths and isinstance(lengths[0], str):
+        L = context_lengths(wid, B, lengths)
+    else:
+        L = np.asarray(lengths, dtype=np.int32)
+    pages_b = (L.astype(np.int64) + PAGE - 1) // PAGE
+    P = int(pages_b.sum()) + int(extra_pages)
+    P_alloc = max(P, 1)
+    stride = int(max_pages) if max_pages is not None else max(int(pages_b.max(initial=0)), 1)
+    perm = rng(wid, STREAM_PERM).permutation(P_alloc).astype(np.int32)
+    table = np.full((B, stride), -1, dtype=np.int32)
+    # (physical page, valid tokens) for every referenced page that is only
+    # partly filled: at most one per request, its last page.
+    partial = []
+    off = 0
+    for b in range(B):
+        n = int(pages_b[b])
+        ids = perm[off:off + n]
+        table[b, :n] = ids
+        if n and int(L[b]) % PAGE:
+            partial.append((int(ids[-1]), int(L[b]) % PAGE))
+        off += n
+    shape = (P_alloc, Hkv, PAGE, D)
+    q = normal(wid, STREAM_Q, (B, Hq, D), "bf16")
+    k32 = rng(wid, STREAM_K).standard_normal(size=shape, dtype=np.float32)
+    v32 = rng(wid, STREAM_V).standard_normal(size=shape, dtype=np.float32)
+    if kv_dtype == "bf16":
+        k = torch.from_numpy(k32).to(torch.bfloat16)
+        v = torch.from_numpy(v32).to(torch.bfloat16)
+        del k32, v32
+        if nan_tails:
+            for p, n in partial:
+                k[p, :, n:, :] = float("nan")
+                v[p, :, n:, :] = float("nan")
+        ks = vs = None
+    elif kv_dtype == "fp8":
+        k, ks = _quantise_e4m3fn(k32, partial, nan_tails)
+        v, vs = _quantise_e4m3fn(v32, partial, nan_tails)
+        del k32, v32
+    else:
+        raise ValueError(kv_dtype)
+    return PagedKV(q, k, v, ks, vs, torch.from_numpy(table), torch.from_numpy(L.copy()),
+                   kv_dtype, P_alloc)
+
+
+def _quantise_e4m3fn(x: np.ndarray, partial, nan_tails: bool):
+    """Input preparation for the fp8 workload: per-(page, head) scale and codes.
+
+    The scale is taken over the valid tokens only; tail slots of partly
+    filled pages become NaN codes when ``nan_tails`` is set.
+    """
+    P, H = x.shape[0], x.shape[1]
+    amax = np.abs(x).reshape(P, H, -1).max(axis=2).astype(np.float32)
+    for p, n in partial:
+        amax[p] = np.abs(x[p, :, :n, :]).reshape(H, -1).max(axis=1) if n > 0 else 0.0
+    scale = (amax / np.float32(448.0)).astype(np.float32)
+    scale[scale == 0] = np.float32(1.0)
+    x /= scale[:, :, None, None]
+    if nan_tails:
+        for p, n in partial:
+            x[p, :, n:, :] = np.nan
+    codes = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, torch.from_numpy(scale)
+
+
+def workload_paged_inputs(w: DecodeWorkload, nan_tails=True) -> PagedKV:
+    return paged_inputs(w.B, w.Hq, w.Hkv, w.D, w.kv_dtype, w.lengths, w.wid, nan_tails)
