@@ -1,0 +1,311 @@
+// C ABI of libfa.so: argument validation, plan objects and kernel dispatch.
+// The public contract (argument meaning, layouts, ownership, errors) is in
+// include/fa.h; this file implements it. No device work is enqueued until
+// every check has passed.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return FA_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(FA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int device_cus(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  e = hipDeviceGetAttribute(out, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(CU count)");
+  return FA_OK;
+}
+
+}  // namespace
+
+struct fa_decode_plan_s {
+  int B, stride, num_pages, Hq, Hkv, D, kv_dtype, num_splits, chunk_pages;
+  std::vector<fa::WorkItem> items;
+  std::vector<int32_t> splits;
+  fa::WorkspaceLayout layout;
+};
+
+extern "C" {
+
+const char* fa_last_error(void) { return g_err.c_str(); }
+
+int fa_abi_version(void) { return 1; }
+
+int fa_prefill_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                   int Hq, int Hkv, int Sq, int Sk, int D, int dtype, int causal, float scale,
+                   const int32_t* kv_head_map, void* stream) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 0 || Sk < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_fwd: need B,Hq,Hkv >= 1 and Sq,Sk >= 0 (got B=%d Hq=%d Hkv=%d Sq=%d Sk=%d)", B, Hq, Hkv, Sq, Sk);
+  if (Hq > fa::kMaxHeads || Hkv > fa::kMaxHeads)
+    return fail(FA_ERR_UNSUPPORTED, "fa_prefill_fwd: Hq and Hkv must be <= %d", fa::kMaxHeads);
+  if (causal != 0 && causal != 1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_fwd: causal must be 0 or 1");
+  if (!(std::isfinite(scale)))
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_fwd: scale is not finite");
+  if (dtype == FA_DTYPE_F32) {
+    if (D != 64 && D != 128)
+      return fail(FA_ERR_UNSUPPORTED, "fa_prefill_fwd: fp32 supports D in {64,128} (got %d)", D);
+  } else if (dtype == FA_DTYPE_BF16) {
+    if (D != 128) return fail(FA_ERR_UNSUPPORTED, "fa_prefill_fwd: bf16 supports D=128 (got %d)", D);
+  } else {
+    return fail(FA_ERR_UNSUPPORTED, "fa_prefill_fwd: dtype %d not supported (F32 or BF16)", dtype);
+  }
+  fa::PrefillArgs a;
+  std::memset(&a, 0, sizeof a);
+  if (kv_head_map) {
+    for (int h = 0; h < Hq; ++h) {
+      if (kv_head_map[h] < 0 || kv_head_map[h] >= Hkv)
+        return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_fwd: kv_head_map[%d]=%d outside [0,%d)", h, kv_head_map[h], Hkv);
+      a.kv_map[h] = (uint8_t)kv_head_map[h];
+    }
+    a.has_map = 1;
+  } else if (Hq % Hkv != 0) {
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_fwd: Hq %% Hkv != 0 (%d, %d) and no kv_head_map", Hq, Hkv);
+  }
+  if (Sq == 0) return ok();
+  if (!q || !out || !lse || (Sk > 0 && (!k || !v)))
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_fwd: null tensor pointer");
+  a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Sk = Sk; a.D = D;
+  a.causal = causal;
+  a.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)D));
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = dtype == FA_DTYPE_F32 ? fa::launch_prefill_f32(a, s) : fa::launch_prefill_bf16(a, s);
+  if (e != hipSuccess) return hip_fail(e, "fa_prefill_fwd launch");
+  return ok();
+}
+
+static int check_decode_shape(int B, int Hq, int Hkv, int D) {
+  if (B < 1 || Hq < 1 || Hkv < 1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "decode: need B, Hq, Hkv >= 1");
+  if (Hq > fa::kMaxHeads || Hkv > fa::kMaxHeads)
+    return fail(FA_ERR_UNSUPPORTED, "decode: Hq and Hkv must be <= %d", fa::kMaxHeads);
+  if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARGUMENT, "decode: Hq %% Hkv != 0 (%d, %d)", Hq, Hkv);
+  int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(FA_ERR_UNSUPPORTED, "decode: group size Hq/Hkv=%d not in {1,2,4,8}", G);
+  if (D != 128) return fail(FA_ERR_UNSUPPORTED, "decode: D=%d not supported (128)", D);
+  return FA_OK;
+}
+
+size_t fa_decode_workspace_size(const int32_t* seqlens_host, int B, int Hq, int Hkv, int D,
+                                int num_splits_request, int num_cus) {
+  if (!seqlens_host || check_decode_shape(B, Hq, Hkv, D) != FA_OK || num_splits_request < 0) return 0;
+  if (num_cus == 0 && device_cus(&num_cus) != FA_OK) return 0;
+  int stride = 1;
+  for (int b = 0; b < B; ++b) {
+    if (seqlens_host[b] < 0) return 0;
+    stride = std::max(stride, (int)(((int64_t)seqlens_host[b] + fa::kPage - 1) / fa::kPage));
+  }
+  fa::PlanResult r;
+  if (fa::plan_decode_host(seqlens_host, B, stride, Hkv, num_splits_request, num_cus, nullptr, 0,
+                           nullptr, &r) != 0)
+    return 0;
+  return fa::workspace_layout(r.n_items, B, Hq, D, r.num_splits).total;
+}
+
+int fa_decode_plan_host(const int32_t* seqlens_host, int B, int max_pages_per_req, int Hq, int Hkv,
+                        int num_splits_request, int num_cus, int32_t* items_out, int capacity,
+                        int32_t* splits_out, int* num_splits_out, int* chunk_pages_out) {
+  if (!seqlens_host || B < 1 || Hkv < 1 || Hq < 1 || max_pages_per_req < 1 || num_cus < 1 ||
+      capacity < 0 || num_splits_request < 0) {
+    fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan_host: invalid argument");
+    return -FA_ERR_INVALID_ARGUMENT;
+  }
+  fa::PlanResult r;
+  std::vector<fa::WorkItem> tmp;
+  if (items_out && capacity > 0) tmp.resize(capacity);
+  if (fa::plan_decode_host(seqlens_host, B, max_pages_per_req, Hkv, num_splits_request, num_cus,
+                           tmp.empty() ? nullptr : tmp.data(), capacity, splits_out, &r) != 0) {
+    fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan_host: bad lengths or page-table stride");
+    return -FA_ERR_INVALID_ARGUMENT;
+  }
+  if (items_out) {
+    int n = std::min(capacity, r.n_items);
+    for (int i = 0; i < n; ++i) {
+      items_out[4 * i + 0] = tmp[i].b;
+      items_out[4 * i + 1] = tmp[i].g_split;
+      items_out[4 * i + 2] = tmp[i].page_begin;
+      items_out[4 * i + 3] = tmp[i].page_end;
+    }
+  }
+  if (num_splits_out) *num_splits_out = r.num_splits;
+  if (chunk_pages_out) *chunk_pages_out = r.chunk_pages;
+  ok();
+  return r.n_items;
+}
+
+int fa_decode_plan(const int32_t* seqlens_host, const int32_t* page_table_host, int B,
+                   int max_pages_per_req, int num_pages, int Hq, int Hkv, int D, int kv_dtype,
+                   int num_splits_request, int num_cus, void* workspace, size_t workspace_bytes,
+                   void* stream, fa_decode_plan_t** plan_out, int* num_splits_out) {
+  if (!plan_out || !num_splits_out)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan: plan_out and num_splits_out must be non-null");
+  *plan_out = nullptr;
+  int st = check_decode_shape(B, Hq, Hkv, D);
+  if (st != FA_OK) return st;
+  if (!seqlens_host) return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan: seqlens_host is null");
+  if (max_pages_per_req < 1 || num_pages < 1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan: need max_pages_per_req >= 1 and num_pages >= 1");
+  if (kv_dtype != FA_DTYPE_BF16 && kv_dtype != FA_DTYPE_FP8_E4M3FN)
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode_plan: kv_dtype %d not supported (BF16 or FP8_E4M3FN)", kv_dtype);
+  if (num_splits_request < 0) return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan: num_splits_request < 0");
+  if (num_cus < 0) return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan: num_cus < 0");
+  for (int b = 0; b < B; ++b) {
+    if (seqlens_host[b] < 0) return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan: seqlens[%d] < 0", b);
+    int64_t n = ((int64_t)seqlens_host[b] + fa::kPage - 1) / fa::kPage;
+    if (n > max_pages_per_req)
+      return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan: request %d needs %lld pages > max_pages_per_req %d", b, (long long)n, max_pages_per_req);
+    if (page_table_host) {
+      for (int64_t j = 0; j < n; ++j) {
+        int32_t id = page_table_host[(int64_t)b * max_pages_per_req + j];
+        if (id < 0 || id >= num_pages)
+          return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan: page_table[%d][%lld]=%d outside [0,%d)", b, (long long)j, id, num_pages);
+      }
+    }
+  }
+  if (num_cus == 0) {
+    st = device_cus(&num_cus);
+    if (st != FA_OK) return st;
+  }
+  fa::PlanResult r;
+  if (fa::plan_decode_host(seqlens_host, B, max_pages_per_req, Hkv, num_splits_request, num_cus,
+                           nullptr, 0, nullptr, &r) != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan: planning failed");
+  fa_decode_plan_t* p = new (std::nothrow) fa_decode_plan_t;
+  if (!p) return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan: out of host memory");
+  p->items.resize(std::max(r.n_items, 1));
+  p->splits.resize(B);
+  fa::plan_decode_host(seqlens_host, B, max_pages_per_req, Hkv, num_splits_request, num_cus,
+                       p->items.data(), r.n_items, p->splits.data(), &r);
+  p->B = B; p->stride = max_pages_per_req; p->num_pages = num_pages;
+  p->Hq = Hq; p->Hkv = Hkv; p->D = D; p->kv_dtype = kv_dtype;
+  p->num_splits = r.num_splits; p->chunk_pages = r.chunk_pages;
+  p->items.resize(r.n_items);
+  p->layout = fa::workspace_layout(r.n_items, B, Hq, D, r.num_splits);
+  if (!workspace || workspace_bytes < p->layout.total) {
+    size_t need = p->layout.total;
+    delete p;
+    return fail(FA_ERR_WORKSPACE, "fa_decode_plan: workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  }
+  // Work list and split counts into one host staging block, one upload.
+  std::vector<char> stage(p->layout.part_o_off, 0);
+  if (r.n_items) std::memcpy(stage.data() + p->layout.items_off, p->items.data(), sizeof(fa::WorkItem) * r.n_items);
+  std::memcpy(stage.data() + p->layout.splits_off, p->splits.data(), sizeof(int32_t) * B);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(workspace, stage.data(), stage.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);  // staging block is freed on return
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "fa_decode_plan upload");
+  }
+  *plan_out = p;
+  *num_splits_out = r.num_splits;
+  return ok();
+}
+
+void fa_decode_plan_destroy(fa_decode_plan_t* plan) { delete plan; }
+
+int fa_decode_plan_items(const fa_decode_plan_t* plan, int32_t* items_out, int capacity,
+                         int32_t* splits_out, int* chunk_pages_out) {
+  if (!plan) return -1;
+  int n = std::min<int>(capacity, (int)plan->items.size());
+  for (int i = 0; items_out && i < n; ++i) {
+    items_out[4 * i + 0] = plan->items[i].b;
+    items_out[4 * i + 1] = plan->items[i].g_split;
+    items_out[4 * i + 2] = plan->items[i].page_begin;
+    items_out[4 * i + 3] = plan->items[i].page_end;
+  }
+  if (splits_out) std::memcpy(splits_out, plan->splits.data(), sizeof(int32_t) * plan->B);
+  if (chunk_pages_out) *chunk_pages_out = plan->chunk_pages;
+  return (int)plan->items.size();
+}
+
+int fa_decode_run(const fa_decode_plan_t* plan, const void* q, const void* k_pages,
+                  const void* v_pages, const float* k_scale, const float* v_scale,
+                  const int32_t* page_table, const int32_t* seqlens, int num_splits, float scale,
+                  void* out, float* lse, void* workspace, void* stream) {
+  if (!plan) return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_run: plan is null");
+  if (num_splits != plan->num_splits)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_run: num_splits %d != plan's %d", num_splits, plan->num_splits);
+  if (!q || !out || !lse || !workspace || !seqlens)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_run: null pointer (q/out/lse/workspace/seqlens)");
+  if (!plan->items.empty() && (!k_pages || !v_pages || !page_table))
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_run: null KV pool or page table");
+  bool fp8 = plan->kv_dtype == FA_DTYPE_FP8_E4M3FN;
+  if (fp8 && !plan->items.empty() && (!k_scale || !v_scale))
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_run: fp8 KV needs k_scale and v_scale");
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_run: scale is not finite");
+  char* ws = (char*)workspace;
+  fa::DecodeArgs a;
+  a.items = (const fa::WorkItem*)(ws + plan->layout.items_off);
+  a.n_items = (int)plan->items.size();
+  a.splits_per_req = (const int32_t*)(ws + plan->layout.splits_off);
+  a.q = q; a.k_pages = k_pages; a.v_pages = v_pages; a.k_scale = k_scale; a.v_scale = v_scale;
+  a.page_table = page_table; a.seqlens = seqlens;
+  a.stride = plan->stride; a.num_pages = plan->num_pages;
+  a.B = plan->B; a.Hq = plan->Hq; a.Hkv = plan->Hkv; a.D = plan->D;
+  a.num_splits = plan->num_splits;
+  a.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)plan->D));
+  a.part_o = (float*)(ws + plan->layout.part_o_off);
+  a.part_lse = (float*)(ws + plan->layout.part_lse_off);
+  a.out = out; a.lse = lse;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (a.n_items > 0) e = fa::launch_decode_split(a, plan->Hq / plan->Hkv, fp8 ? 1 : 0, s);
+  if (e != hipSuccess) return hip_fail(e, "fa_decode_run split launch");
+  e = fa::launch_lse_merge(a, s);
+  if (e != hipSuccess) return hip_fail(e, "fa_decode_run merge launch");
+  return ok();
+}
+
+int fa_debug_gather_kv(const void* pages, int kv_dtype, const int32_t* page_table,
+                       int max_pages_per_req, int num_pages, int Hkv, int D, int b, int L_b,
+                       int kv_head, void* dst, void* stream) {
+  if (kv_dtype != FA_DTYPE_BF16 && kv_dtype != FA_DTYPE_FP8_E4M3FN)
+    return fail(FA_ERR_UNSUPPORTED, "fa_debug_gather_kv: kv_dtype %d not supported", kv_dtype);
+  if (D != 128 || Hkv < 1 || b < 0 || L_b < 0 || kv_head < 0 || kv_head >= Hkv ||
+      max_pages_per_req < 1 || num_pages < 1 ||
+      ((int64_t)L_b + fa::kPage - 1) / fa::kPage > max_pages_per_req)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_debug_gather_kv: invalid shape arguments");
+  if (L_b == 0) return ok();
+  if (!pages || !page_table || !dst) return fail(FA_ERR_INVALID_ARGUMENT, "fa_debug_gather_kv: null pointer");
+  hipError_t e = fa::launch_gather_kv(pages, kv_dtype == FA_DTYPE_BF16 ? 2 : 1, page_table,
+                                      max_pages_per_req, num_pages, Hkv, D, b, L_b, kv_head, dst,
+                                      (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fa_debug_gather_kv launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Internal declarations shared by the host ABI (abi.cpp) and the kernel
+// launchers (*.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+constexpr int kPage = 64;         // tokens per KV page
+constexpr int kMaxHeads = 256;    // limit on Hq and Hkv (head map travels in kernel args)
+
+// ---------------------------------------------------------------- prefill
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  int B, Hq, Hkv, Sq, Sk, D;
+  int causal;
+  float scale;        // score multiplier (already defaulted)
+  int has_map;        // 0: contiguous groups h / (Hq/Hkv)
+  uint8_t kv_map[kMaxHeads];
+};
+
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- decode
+// One work item of the split-KV decode: pages [page_begin, page_end) of
+// request b, KV head g, partial-result slot `split`.
+struct WorkItem {
+  int32_t b;
+  int32_t g_split;   // g | (split << 8)
+  int32_t page_begin;
+  int32_t page_end;
+};
+
+struct DecodeArgs {
+  const WorkItem* items;
+  int n_items;
+  const int32_t* splits_per_req;  // [B]
+  const void* q;                  // [B, Hq, D] bf16
+  const void* k_pages;            // [P, Hkv, 64, D]
+  const void* v_pages;
+  const float* k_scale;           // [P, Hkv] (fp8)
+  const float* v_scale;
+  const int32_t* page_table;      // [B, stride]
+  const int32_t* seqlens;         // [B]
+  int stride;                     // page-table row stride
+  int num_pages;
+  int B, Hq, Hkv, D;
+  int num_splits;                 // partial-buffer stride
+  float scale;
+  float* part_o;                  // [B, Hq, num_splits, D]
+  float* part_lse;                // [B, Hq, num_splits]
+  void* out;                      // [B, Hq, D] bf16
+  float* lse;                     // [B, Hq]
+};
+
+hipError_t launch_decode_split(const DecodeArgs& a, int group, int fp8, hipStream_t s);
+hipError_t launch_lse_merge(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_gather_kv(const void* pages, int elem_bytes, const int32_t* page_table,
+                            int stride, int num_pages, int Hkv, int D, int b, int L, int g,
+                            void* dst, hipStream_t s);
+
+// ---------------------------------------------------------------- plan (pure host)
+struct PlanResult {
+  int num_splits = 0;   // max split count over requests
+  int chunk_pages = 0;  // target pages per work item (auto mode)
+  int n_items = 0;
+};
+
+// Returns 0 or a negative fa_status. `items` (capacity entries) and
+// `splits` (B entries) may be null to only count.
+int plan_decode_host(const int32_t* seqlens, int B, int stride, int Hkv, int num_splits_request,
+                     int num_cus, WorkItem* items, int capacity, int32_t* splits,
+                     PlanResult* res);
+
+// Workspace layout for a plan: work items, per-request split counts, partials.
+struct WorkspaceLayout {
+  size_t items_off, splits_off, part_o_off, part_lse_off, total;
+};
+WorkspaceLayout workspace_layout(int n_items, int B, int Hq, int D, int num_splits);
+
+}  // namespace fa

@@ -1,0 +1,214 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library (libfa.so).
+ *
+ * Exact attention O = softmax(Q K^T / sqrt(d)) V, forward only, in two forms:
+ *   - prefill: every query row of a [B, Hq, Sq, D] block against its KV head,
+ *     optionally causal, tiled so the score matrix never reaches HBM;
+ *   - paged Flash-Decoding: one query token per request against a KV cache
+ *     held in 64-token pages behind a page table, split along the sequence,
+ *     partial results merged by their LogSumExp.
+ *
+ * Sources (titles of the pages this follows):
+ *   "FIA / FlashAttention" help-centre Q&A: section 1 (the attention formula,
+ *     exactness, IO-aware tiling with online softmax), section 2 (FIA: a plan
+ *     step that preprocesses ragged lengths and balances load, then a run
+ *     step), section 3 (GQA, FP8 inference kernels), section 4 (the causal
+ *     packed-QKV call and the plan/run decode calls).
+ *   "Flash Attention & Paged Attention" blog: "FA and the decode phase"
+ *     (Flash-Decoding) and "2. PagedAttention" (pages + logical page table).
+ *   "FasterTransformer vs FlashAttention" article, section 3 (the blocked
+ *     loop: Q block outer, K/V blocks inner, running max and normaliser).
+ *   "FlashAttention breakthrough architecture" article: 64-token pages,
+ *     num_splits as the split-KV parallelism knob, cache_seqlens.
+ *
+ * Conventions for every call:
+ *   - Tensor arguments are raw DEVICE pointers unless marked "host". The
+ *     caller owns all device memory (inputs, outputs and the decode
+ *     workspace); the library allocates only the small host-side plan object.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default
+ *     stream. All device work is enqueued asynchronously on it; faults in
+ *     device code surface at the caller's next synchronisation.
+ *   - Return value: FA_OK or an fa_status error code. Every argument check
+ *     happens before any device work is enqueued, so an error return means
+ *     nothing was launched. fa_last_error() gives a message (thread-local).
+ *   - No call throws across the ABI. Calls are re-entrant; concurrent decode
+ *     runs need distinct workspaces.
+ *   - LSE outputs are natural-log LogSumExp of the scaled, unmasked scores of
+ *     a query row: LSE_i = ln sum_j exp(scale * q_i . k_j).
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, inconsistent shapes */
+  FA_ERR_UNSUPPORTED = 2,      /* valid request outside what the kernels cover */
+  FA_ERR_WORKSPACE = 3,        /* decode workspace too small */
+  FA_ERR_HIP = 4               /* a HIP runtime call failed (message has the HIP error) */
+} fa_status;
+
+typedef enum {
+  FA_DTYPE_F32 = 0,
+  FA_DTYPE_BF16 = 1,
+  FA_DTYPE_FP8_E4M3FN = 2 /* OCP e4m3fn codes (uint8), KV cache only */
+} fa_dtype;
+
+/* Message for the last error on the calling thread ("" after success). */
+const char* fa_last_error(void);
+
+/* Library ABI version (bumped on any signature change). */
+int fa_abi_version(void);
+
+/*
+ * fa_prefill_fwd -- exact attention forward over contiguous BHSD tensors.
+ * (FIA / FlashAttention Q&A, sections 1 and 4; FasterTransformer vs
+ * FlashAttention, section 3: the Q-block-outer, KV-block-inner loop.)
+ *
+ *   q    [B, Hq,  Sq, D]  dtype, contiguous
+ *   k, v [B, Hkv, Sk, D]  dtype, contiguous
+ *   out  [B, Hq,  Sq, D]  dtype (bf16 rounded to nearest even), written
+ *   lse  [B, Hq,  Sq]     fp32 natural-log LSE per query row, written
+ *   dtype        FA_DTYPE_F32 (D = 64 or 128) or FA_DTYPE_BF16 (D = 128);
+ *                accumulation is fp32 in both.
+ *   causal       0/1. Causal masking is aligned bottom-right: key j is
+ *                visible to query i iff j <= i + (Sk - Sq). A query row that
+ *                sees no key gets out = 0 and lse = -inf.
+ *   scale        score multiplier; <= 0 selects 1/sqrt(D).
+ *   kv_head_map  host int32[Hq]: KV head read by each query head (GQA), or
+ *                NULL for contiguous groups h / (Hq / Hkv) (then Hq % Hkv
+ *                must be 0). Entries must lie in [0, Hkv).
+ * Limits: B, Hq, Hkv >= 1; Hq, Hkv <= 256; Sq, Sk >= 0 (0 is a no-op for
+ * Sq = 0; Sk = 0 gives out = 0, lse = -inf); B*Hq*Sq*D and B*Hkv*Sk*D must fit in
+ * int64 and Sq, Sk < 2^31.
+ */
+int fa_prefill_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                   int B, int Hq, int Hkv, int Sq, int Sk, int D, int dtype, int causal,
+                   float scale, const int32_t* kv_head_map, void* stream);
+
+/*
+ * Paged Flash-Decoding: plan once per batch composition, then run.
+ * ("FIA / FlashAttention" Q&A, section 2: plan preprocesses ragged lengths
+ * and balances load, run executes the batch; "Flash Attention & Paged
+ * Attention", Flash-Decoding and PagedAttention sections.)
+ *
+ * KV cache layout: k_pages / v_pages are pools [P, Hkv, 64, D] (one 64-token
+ * page of one KV head is a contiguous [64, D] block); page_table is int32
+ * [B, max_pages_per_req], logical page j of request b at physical page
+ * page_table[b * max_pages_per_req + j]; only entries j < ceil(L_b / 64) are
+ * read. Tokens past L_b on the last page are never read into the result
+ * (their contents may be anything, NaN included).
+ */
+typedef struct fa_decode_plan_s fa_decode_plan_t;
+
+/*
+ * Bytes of device workspace a plan for this batch shape needs; pass the same
+ * arguments later to fa_decode_plan. Returns 0 on invalid arguments.
+ * num_splits_request as in fa_decode_plan; num_cus = 0 means "the current
+ * device's CU count" (a HIP query), else the value given.
+ */
+size_t fa_decode_workspace_size(const int32_t* seqlens_host, int B, int Hq, int Hkv, int D,
+                                int num_splits_request, int num_cus);
+
+/*
+ * fa_decode_plan -- split every request's pages into chunks and balance them.
+ *   seqlens_host       host int32[B], context length L_b >= 0 of each request
+ *   page_table_host    host int32[B * max_pages_per_req] or NULL. When given,
+ *                      every entry the run will read is checked to lie in
+ *                      [0, num_pages); violations return
+ *                      FA_ERR_INVALID_ARGUMENT (the device kernel also skips
+ *                      out-of-range ids, so a bad table cannot fault).
+ *   max_pages_per_req  row stride of the page table; ceil(L_b/64) must fit.
+ *   num_pages          P, pages in each pool.
+ *   Hq, Hkv, D         heads and head size; Hq % Hkv == 0, Hq/Hkv in
+ *                      {1, 2, 4, 8}, D = 128.
+ *   kv_dtype           FA_DTYPE_BF16 or FA_DTYPE_FP8_E4M3FN.
+ *   num_splits_request 0 = let the plan choose the chunk size for the
+ *                      device's CUs; k > 0 = split every request into
+ *                      min(k, pages_b) near-equal page ranges.
+ *   num_cus            0 = query the current device, else use this count.
+ *   workspace          device buffer of >= fa_decode_workspace_size bytes; the
+ *                      plan uploads its work list there with one
+ *                      hipMemcpyAsync on `stream`.
+ *   plan_out           receives a host plan object (free with
+ *                      fa_decode_plan_destroy, after the runs that use it).
+ *   num_splits_out     receives the largest split count of any request: the
+ *                      stride of the partial-result buffers, to be passed to
+ *                      fa_decode_run.
+ */
+int fa_decode_plan(const int32_t* seqlens_host, const int32_t* page_table_host, int B,
+                   int max_pages_per_req, int num_pages, int Hq, int Hkv, int D, int kv_dtype,
+                   int num_splits_request, int num_cus, void* workspace,
+                   size_t workspace_bytes, void* stream, fa_decode_plan_t** plan_out,
+                   int* num_splits_out);
+
+void fa_decode_plan_destroy(fa_decode_plan_t* plan);
+
+/*
+ * Host view of a plan, for inspection and tests. Copies up to `capacity`
+ * work items into items_out as int32 quadruples
+ * (request b, kv head g, first page, end page (exclusive)) and each request's
+ * split count into splits_out[B] (either pointer may be NULL).
+ * Returns the number of work items, or -1 on a NULL plan.
+ */
+int fa_decode_plan_items(const fa_decode_plan_t* plan, int32_t* items_out, int capacity,
+                         int32_t* splits_out, int* chunk_pages_out);
+
+/*
+ * Pure host planning (no device, no HIP call): the same work list
+ * fa_decode_plan computes, for a given CU count. Writes up to `capacity`
+ * quadruples as in fa_decode_plan_items and each request's split count into
+ * splits_out[B]. Returns the number of work items, or a negative fa_status
+ * on invalid arguments.
+ */
+int fa_decode_plan_host(const int32_t* seqlens_host, int B, int max_pages_per_req, int Hq,
+                        int Hkv, int num_splits_request, int num_cus, int32_t* items_out,
+                        int capacity, int32_t* splits_out, int* num_splits_out,
+                        int* chunk_pages_out);
+
+/*
+ * fa_decode_run -- split-KV decode plus LSE merge; two kernels on `stream`,
+ * no host synchronisation, no allocation (so it can be captured in a graph).
+ *   q          [B, Hq, D] bf16, one query token per request
+ *   k_pages    [P, Hkv, 64, D] bf16, or uint8 e4m3fn codes (per plan dtype)
+ *   v_pages    same as k_pages
+ *   k_scale    fp32 [P, Hkv] dequantisation scale per page and KV head
+ *              (value = code * scale); required for fp8, ignored for bf16
+ *   v_scale    same for V
+ *   page_table int32 [B, max_pages_per_req] (device copy of the plan's table)
+ *   seqlens    int32 [B] device copy of the lengths given to the plan (the
+ *              kernel masks tokens >= seqlens[b]; they must match the plan)
+ *   num_splits must equal the plan's *num_splits_out
+ *   scale      score multiplier; <= 0 selects 1/sqrt(D)
+ *   out        [B, Hq, D] bf16, written; lse [B, Hq] fp32, written. A request
+ *              with L_b = 0 gets out = 0 and lse = -inf.
+ *   workspace  the buffer given to the plan (it holds the work list and the
+ *              per-split partial results)
+ */
+int fa_decode_run(const fa_decode_plan_t* plan, const void* q, const void* k_pages,
+                  const void* v_pages, const float* k_scale, const float* v_scale,
+                  const int32_t* page_table, const int32_t* seqlens, int num_splits, float scale,
+                  void* out, float* lse, void* workspace, void* stream);
+
+/*
+ * fa_debug_gather_kv -- copy the L_b logical tokens of one request and KV
+ * head out of a paged pool, through the same page-table indexing the decode
+ * kernel uses, into dst [L_b, D] (same element type as the pool). For the
+ * bit-exact gather test. max_pages_per_req and num_pages as for the plan;
+ * ids outside [0, num_pages) leave their tokens' dst rows untouched.
+ */
+int fa_debug_gather_kv(const void* pages, int kv_dtype, const int32_t* page_table,
+                       int max_pages_per_req, int num_pages, int Hkv, int D, int b, int L_b,
+                       int kv_head, void* dst, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

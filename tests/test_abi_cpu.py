@@ -1,0 +1,193 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, rejects
+invalid arguments before touching the device, and plans correctly.
+
+No test here launches a kernel: argument checks run before any HIP call.
+"""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import exact_attention_20_amd as fa
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.lib_path()):
+        pytest.skip("libfa.so not built")
+    return fa.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("fa_prefill_fwd", "fa_decode_plan", "fa_decode_run", "fa_last_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.lib_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (fa_\w+)", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    for n in declared_functions():
+        assert hasattr(lib, n)
+    assert lib.fa_abi_version() == 1
+
+
+def _prefill(lib, **kw):
+    a = dict(q=C.c_void_p(16), k=C.c_void_p(16), v=C.c_void_p(16), out=C.c_void_p(16),
+             lse=C.c_void_p(16), B=1, Hq=2, Hkv=2, Sq=8, Sk=8, D=128, dtype=fa.BF16, causal=1,
+             scale=0.0, map=None, stream=None)
+    a.update(kw)
+    return lib.fa_prefill_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                              a["Sq"], a["Sk"], a["D"], a["dtype"], a["causal"], a["scale"], a["map"],
+                              a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), 1), (dict(Hq=0), 1), (dict(Sq=-1), 1), (dict(Sk=-2), 1),
+    (dict(causal=2), 1), (dict(scale=float("nan")), 1), (dict(Hq=3, Hkv=2), 1),
+    (dict(D=64), 2), (dict(dtype=fa.F32, D=96), 2), (dict(dtype=7), 2), (dict(dtype=fa.FP8_E4M3FN), 2),
+    (dict(Hq=300, Hkv=300), 2), (dict(q=None), 1), (dict(k=None), 1), (dict(lse=None), 1),
+])
+def test_prefill_rejects(lib, kw, code):
+    assert _prefill(lib, **kw) == code
+    assert lib.fa_last_error().decode()
+
+
+def test_prefill_bad_map(lib):
+    bad = (C.c_int32 * 2)(0, 5)
+    assert _prefill(lib, map=C.cast(bad, C.POINTER(C.c_int32))) == 1
+    assert b"kv_head_map" in lib.fa_last_error()
+
+
+def test_prefill_sq0_is_noop(lib):
+    assert _prefill(lib, Sq=0, q=None, out=None, lse=None) == 0
+
+
+def _plan(lib, seqlens, table=None, **kw):
+    a = dict(B=len(seqlens), stride=8, P=100, Hq=8, Hkv=2, D=128, dt=fa.BF16, ns=0, cus=4,
+             ws=C.c_void_p(256), wsb=1 << 30)
+    a.update(kw)
+    sl = (C.c_int32 * len(seqlens))(*seqlens)
+    tb = None if table is None else C.cast((C.c_int32 * len(table))(*table), C.POINTER(C.c_int32))
+    h, n = C.c_void_p(), C.c_int()
+    st = lib.fa_decode_plan(C.cast(sl, C.POINTER(C.c_int32)), tb, a["B"], a["stride"], a["P"], a["Hq"],
+                            a["Hkv"], a["D"], a["dt"], a["ns"], a["cus"], a["ws"], a["wsb"], None,
+                            C.byref(h), C.byref(n))
+    return st
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=6, Hkv=4), 1), (dict(Hq=24, Hkv=2), 2), (dict(D=64), 2), (dict(dt=fa.F32), 2),
+    (dict(stride=1), 1), (dict(P=0), 1), (dict(ns=-1), 1), (dict(cus=-1), 1),
+    (dict(ws=None), 3), (dict(wsb=16), 3),
+])
+def test_plan_rejects(lib, kw, code):
+    assert _plan(lib, [100, 300], **kw) == code
+
+
+def test_plan_rejects_negative_length(lib):
+    assert _plan(lib, [100, -1]) == 1
+
+
+def test_plan_checks_page_ids(lib):
+    # request 0 has 2 pages, request 1 has 5; stride 8
+    table = [0, 1] + [-1] * 6 + [2, 3, 4, 5, 100] + [-1] * 3
+    assert _plan(lib, [100, 300], table) == 1
+    assert b"page_table" in lib.fa_last_error()
+
+
+def test_run_rejects_null_plan(lib):
+    assert lib.fa_decode_run(None, None, None, None, None, None, None, None, 0, 0.0, None, None, None, None) == 1
+
+
+def test_gather_rejects(lib):
+    assert lib.fa_debug_gather_kv(C.c_void_p(16), 7, C.c_void_p(16), 4, 10, 2, 128, 0, 10, 0, C.c_void_p(16), None) == 2
+    assert lib.fa_debug_gather_kv(C.c_void_p(16), fa.BF16, C.c_void_p(16), 1, 10, 2, 128, 0, 100, 0, C.c_void_p(16), None) == 1
+    assert lib.fa_debug_gather_kv(C.c_void_p(16), fa.BF16, C.c_void_p(16), 4, 10, 2, 128, 0, 10, 2, C.c_void_p(16), None) == 1
+
+
+# ------------------------------------------------------------------ plan properties
+
+def _check_plan(seqlens, items, splits, num_splits, Hkv, forced=0):
+    L = np.asarray(seqlens)
+    pages = (L + 63) // 64
+    cover = {}
+    for b, gs, p0, p1 in items.tolist():
+        g, s = gs & 255, gs >> 8
+        assert 0 <= g < Hkv and 0 <= s < splits[b] <= num_splits
+        assert 0 <= p0 < p1 <= pages[b]
+        for p in range(p0, p1):
+            key = (b, g, p)
+            assert key not in cover, "page covered twice"
+            cover[key] = s
+    for b in range(len(L)):
+        for g in range(Hkv):
+            for p in range(pages[b]):
+                assert (b, g, p) in cover, "page not covered"
+    # splits of a request are contiguous, in order, near-equal
+    for b in range(len(L)):
+        if pages[b] == 0:
+            assert splits[b] == 0
+            continue
+        sizes = {}
+        for (bb, g, p), s in cover.items():
+            if bb == b and g == 0:
+                sizes[s] = sizes.get(s, 0) + 1
+        assert sorted(sizes) == list(range(splits[b]))
+        assert max(sizes.values()) - min(sizes.values()) <= 1
+        if forced:
+            assert splits[b] == min(forced, pages[b])
+    assert num_splits == max(splits.tolist() + [0])
+    lens = (items[:, 3] - items[:, 2]).tolist()
+    assert lens == sorted(lens, reverse=True), "longest items first"
+
+
+@pytest.mark.parametrize("wid", [4, 5])
+def test_plan_workloads(lib, wid):
+    w = workloads.WORKLOADS[wid]
+    L = workloads.context_lengths(wid, w.B, w.lengths)
+    stride = int(((L + 63) // 64).max())
+    items, splits, ns, chunk = fa.fa_decode_plan_host(L, stride, w.Hq, w.Hkv, 0, 256)
+    _check_plan(L, items, splits, ns, w.Hkv)
+    total = int(((L + 63) // 64).sum()) * w.Hkv
+    # balance: every item holds at most one chunk; enough items to fill 256 CUs
+    assert int((items[:, 3] - items[:, 2]).max()) <= chunk
+    assert len(items) >= 256 or total < 256 * 4
+
+
+@pytest.mark.parametrize("seqlens", [[1], [0, 5, 0], [64, 65, 4096, 1, 0], list(range(0, 2000, 97))])
+@pytest.mark.parametrize("forced", [0, 1, 3, 64])
+def test_plan_edge_lengths(lib, seqlens, forced):
+    L = np.asarray(seqlens, dtype=np.int32)
+    stride = max(1, int(((L + 63) // 64).max()))
+    items, splits, ns, _ = fa.fa_decode_plan_host(L, stride, 8, 2, forced, 16)
+    _check_plan(L, items, splits, ns, 2, forced)
+
+
+def test_plan_is_deterministic(lib):
+    L = workloads.context_lengths(4, 64, ("uniform", 512, 16384))
+    a = fa.fa_decode_plan_host(L, 256, 32, 8, 0, 256)
+    b = fa.fa_decode_plan_host(L, 256, 32, 8, 0, 256)
+    assert np.array_equal(a[0].numpy(), b[0].numpy()) and a[2:] == b[2:]
+
+
+def test_workspace_size(lib):
+    L = [100, 300, 0]
+    n = fa.fa_decode_workspace_size(L, 8, 2, 128, 0, 16)
+    items, splits, ns, _ = fa.fa_decode_plan_host(L, 8, 8, 2, 0, 16)
+    assert n >= len(items) * 16 + 3 * 4 + 3 * 8 * ns * 129 * 4

@@ -1,0 +1,138 @@
+"""Paged decode parity: plan + split-KV + LSE merge (through the C ABI) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import check, f64, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def to_dev(kv):
+    d = dict(q=kv.q.cuda(), k=kv.k_pages.cuda(), v=kv.v_pages.cuda(), pt=kv.page_table.cuda(),
+             sl=kv.seqlens.cuda())
+    d["ks"] = kv.k_scale.cuda() if kv.k_scale is not None else None
+    d["vs"] = kv.v_scale.cuda() if kv.v_scale is not None else None
+    return d
+
+
+def oracle_decode(kv, scale, requests=None):
+    if kv.kv_dtype == "fp8":
+        kp, vp = kv.k_pages.numpy(), kv.v_pages.numpy()
+        ks, vs = kv.k_scale.numpy(), kv.v_scale.numpy()
+    else:
+        kp, vp = kv.k_pages.float().numpy(), kv.v_pages.float().numpy()
+        ks = vs = None
+    return oracle.paged_decode(f64(kv.q), kp, vp, kv.page_table.numpy(), kv.seqlens.numpy(), scale,
+                               ks, vs, requests=requests)
+
+
+def run(fa, kv, d, num_splits=0, scale=None):
+    dt = fa.BF16 if kv.kv_dtype == "bf16" else fa.FP8_E4M3FN
+    B, Hq, D = kv.q.shape
+    Hkv = kv.k_pages.shape[1]
+    plan = fa.fa_decode_plan(kv.seqlens, kv.page_table, kv.num_pages, Hq, Hkv, D, dt, num_splits)
+    out, lse = fa.decode(plan, d["q"], d["k"], d["v"], d["pt"], d["sl"], d["ks"], d["vs"], scale)
+    torch.cuda.synchronize()
+    return out, lse, plan
+
+
+CASES = [
+    # (lengths, Hq, Hkv, kv_dtype)
+    ([1, 63, 64, 65, 1000], 8, 2, "bf16"),
+    ([1, 63, 64, 65, 1000], 8, 2, "fp8"),
+    ([700, 0, 129, 4097], 8, 8, "bf16"),
+    ([300, 2000], 4, 2, "bf16"),
+    ([5000, 17, 640], 16, 2, "bf16"),
+    ([5000, 17, 640], 16, 2, "fp8"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[3]}-G{c[1] // c[2]}-L{len(c[0])}")
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+def test_small_batches(case, num_splits):
+    fa = need_gpu()
+    L, Hq, Hkv, dt = case
+    say(f"[case] decode L={L} Hq={Hq} Hkv={Hkv} {dt} num_splits={num_splits}")
+    kv = workloads.paged_inputs(len(L), Hq, Hkv, 128, dt, L, 31, nan_tails=True, max_pages=80, extra_pages=3)
+    d = to_dev(kv)
+    scale = float(np.float32(1 / np.sqrt(128)))
+    out, lse, _ = run(fa, kv, d, num_splits, scale)
+    O, LSE = oracle_decode(kv, scale)
+    empty = kv.seqlens.numpy() == 0
+    if empty.any():
+        assert torch.all(out[torch.from_numpy(empty)] == 0)
+        assert torch.all(torch.isneginf(lse[torch.from_numpy(empty)]))
+    check(f"decode {case} splits={num_splits}", f64(out), O, f64(lse), LSE, "fp8" if dt == "fp8" else "bf16")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+def test_gather_bit_exact(dt):
+    """The kernel's page-table indexing, exported as a gather, reproduces the logical sequence exactly."""
+    fa = need_gpu()
+    L = [1, 64, 65, 3000]
+    kv = workloads.paged_inputs(4, 8, 2, 128, dt, L, 32, nan_tails=True)
+    d = to_dev(kv)
+    kdt = fa.BF16 if dt == "bf16" else fa.FP8_E4M3FN
+    for b, Lb in enumerate(L):
+        for g in range(2):
+            got = fa.fa_debug_gather_kv(d["k"], kdt, d["pt"], kv.num_pages, b, Lb, g)
+            torch.cuda.synchronize()
+            raw = kv.k_pages.float().numpy() if dt == "bf16" else kv.k_pages.numpy()
+            ref = oracle.gather_pages(raw, kv.page_table[b].numpy(), Lb, g)
+            gotn = got.cpu().float().numpy() if dt == "bf16" else got.cpu().numpy().astype(np.float64)
+            assert np.array_equal(gotn, ref), f"gather mismatch b={b} g={g}"
+
+
+def test_page_permutation_bitwise():
+    """The same logical cache under a different physical page permutation gives identical bits."""
+    fa = need_gpu()
+    L = [900, 130, 2500]
+    kv = workloads.paged_inputs(3, 8, 2, 128, "bf16", L, 33, nan_tails=True)
+    d = to_dev(kv)
+    out1, lse1, _ = run(fa, kv, d, 0)
+    P = kv.num_pages
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(P).astype(np.int64))
+    k2 = torch.empty_like(kv.k_pages)
+    v2 = torch.empty_like(kv.v_pages)
+    k2[perm] = kv.k_pages
+    v2[perm] = kv.v_pages
+    pt2 = kv.page_table.clone()
+    used = pt2 >= 0
+    pt2[used] = perm[pt2[used].long()].int()
+    kv2 = workloads.PagedKV(kv.q, k2, v2, None, None, pt2, kv.seqlens, "bf16", P)
+    out2, lse2, _ = run(fa, kv2, to_dev(kv2), 0)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_num_splits_invariance():
+    fa = need_gpu()
+    L = [4000, 10000, 64]
+    kv = workloads.paged_inputs(3, 16, 4, 128, "bf16", L, 34, nan_tails=True)
+    d = to_dev(kv)
+    res = [run(fa, kv, d, ns)[:2] for ns in (1, 2, 7, 0)]
+    for o, l in res[1:]:
+        assert (o.float() - res[0][0].float()).abs().max().item() <= 4e-3
+        assert (l - res[0][1]).abs().max().item() <= 1e-4
+
+
+@pytest.mark.parametrize("wid", [4, 5])
+def test_full_workload(wid):
+    """Full-size decode workloads in the benchmark's launch configuration (plan-chosen splits)."""
+    fa = need_gpu()
+    w = workloads.WORKLOADS[wid]
+    say(f"[case] full decode workload {wid} {w.name}")
+    kv = workloads.workload_paged_inputs(w, nan_tails=True)
+    d = to_dev(kv)
+    out, lse, plan = run(fa, kv, d, 0, w.scale)
+    say(f"[plan] items={len(plan.items()[0])} num_splits={plan.num_splits} pages={kv.num_pages}")
+    rng = np.random.default_rng(wid)
+    L = kv.seqlens.numpy()
+    reqs = sorted({int(np.argmax(L)), int(np.argmin(L))} |
+                  set(rng.choice(w.B, size=min(w.B, 12), replace=False).tolist()))
+    O, LSE = oracle_decode(kv, w.scale, requests=reqs)
+    check(f"decode workload {wid} ({len(reqs)} requests)", f64(out[reqs]), O, f64(lse[reqs]), LSE,
+          "fp8" if w.kv_dtype == "fp8" else "bf16")
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
