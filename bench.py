@@ -1,0 +1,288 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--only prefill|decode] [--prefill-workload 2|3] [--decode-workload 4|5]
+
+One step = one pass of the whole path over one synthetic batch:
+  * prefill: fa_prefill_fwd on the causal bf16 workload (default: B=4, 32 heads,
+    4096 tokens, head dim 128), and
+  * decode: fa_decode_run (split-KV kernel + LSE merge) on the paged bf16
+    workload (default: 64 requests, 32/8 heads, lengths U[512, 16384]),
+    planned once beforehand (the host plan is timed separately and reported).
+Inputs are resident in HBM before timing. Each kernel call is bracketed by
+HIP events on the stream it runs on; the step time is their sum.
+
+Prints ONE JSON line. ``value`` is the prefill throughput in TFLOP/s
+(algorithmic FLOPs 4*B*H*D*S(S+1)/2 over the measured time); the ``decode``
+object carries the decode HBM throughput (algorithmic bytes over the measured
+time). ``roofline`` is for the dominant kernel (the MFMA prefill), and
+``cpu_baseline`` times the fp64 oracle on a bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal bf16 prefill TFLOP/s (% MFMA peak); paged decode HBM GB/s (% peak)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+
+
+def prefill_flops(w):
+    pairs = w.S * (w.S + 1) // 2
+    return 4.0 * w.B * w.Hq * w.D * pairs
+
+
+def decode_bytes(kv, w):
+    import numpy as np
+    L = kv.seqlens.numpy().astype(np.int64)
+    pages = (L + 63) // 64
+    eb = 1 if w.kv_dtype == "fp8" else 2
+    b = int(L.sum()) * w.Hkv * w.D * 2 * eb          # K and V of the valid tokens
+    if w.kv_dtype == "fp8":
+        b += int(pages.sum()) * w.Hkv * 8             # one fp32 scale per (page, head), K and V
+    b += 2 * w.B * w.Hq * w.D * 2                     # q in, out
+    b += w.B * w.Hq * 4                               # lse
+    b += int(pages.sum()) * 4 + w.B * 4               # page-table entries read, seqlens
+    return b
+
+
+def source_sha(rel):
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(name, src_rel):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if the
+    kernel source is unchanged since the counters were taken (else None)."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != source_sha(src_rel):
+        return None
+    try:
+        return int(float(kv["fetch_bytes_per_launch"])) + int(float(kv["write_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def time_calls(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def cpu_baseline_prefill(w, q, k, v, budget_s=15.0):
+    """fp64 oracle on whole heads of the prefill workload, threads over heads."""
+    import concurrent.futures as cf
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    qn = q.double().numpy()
+    kn = k.double().numpy()
+    vn = v.double().numpy()
+    heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+
+    def one(bh):
+        oracle.prefill(qn, kn, vn, w.scale, True, heads=[bh])
+
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1), cf.ThreadPoolExecutor(cores) as ex:
+        while done < len(heads) and time.perf_counter() - t0 < budget_s:
+            batch = heads[done:done + cores]
+            list(ex.map(one, batch))
+            done += len(batch)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.D * (w.S * (w.S + 1) // 2) * done
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {len(heads)} whole heads (all {w.S} causal rows) of the prefill workload, "
+                      f"{dt:.1f} s wall, fp64 numpy, BLAS 1 thread per worker"}
+
+
+def cpu_baseline_decode(w, kv, budget_s=10.0):
+    import concurrent.futures as cf
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    q = kv.q.double().numpy()
+    if w.kv_dtype == "fp8":
+        kp, vp, ks, vs = kv.k_pages.numpy(), kv.v_pages.numpy(), kv.k_scale.numpy(), kv.v_scale.numpy()
+    else:
+        kp, vp, ks, vs = kv.k_pages.float().numpy(), kv.v_pages.float().numpy(), None, None
+    pt, sl = kv.page_table.numpy(), kv.seqlens.numpy()
+    eb = 1 if w.kv_dtype == "fp8" else 2
+
+    def one(b):
+        oracle.paged_decode(q, kp, vp, pt, sl, w.scale, ks, vs, requests=[b])
+        return int(sl[b]) * w.Hkv * w.D * 2 * eb
+
+    done, nbytes = 0, 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1), cf.ThreadPoolExecutor(cores) as ex:
+        while done < w.B and time.perf_counter() - t0 < budget_s:
+            batch = list(range(done, min(w.B, done + cores)))
+            nbytes += sum(ex.map(one, batch))
+            done += len(batch)
+    dt = time.perf_counter() - t0
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {w.B} requests of the decode workload (all heads), {dt:.1f} s wall, "
+                      f"fp64 numpy, BLAS 1 thread per worker"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--prefill-workload", type=int, default=2, choices=[2, 3])
+    ap.add_argument("--decode-workload", type=int, default=4, choices=[4, 5])
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the way it would shard is described in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_attention_20_amd as fa
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    fa.load()
+    stream = torch.cuda.current_stream()
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
+
+    res = {}
+    wp = workloads.WORKLOADS[args.prefill_workload]
+    wd = workloads.WORKLOADS[args.decode_workload]
+
+    if args.only in (None, "prefill"):
+        log(f"[bench] generating prefill workload {wp.name}")
+        q, k, v = workloads.workload_prefill_inputs(wp)
+        qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+        out = torch.empty_like(qd)
+        lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=qd.device)
+        pf = lambda: fa.fa_prefill_fwd(qd, kd, vd, out, lse, True, wp.scale, None, stream)  # noqa: E731
+        t = time_calls(pf, args.steps, args.warmup, stream)
+        res["prefill_ms"] = t
+        log(f"[bench] prefill median {statistics.median(t):.4f} ms min {min(t):.4f} ms")
+        res["prefill_cpu"] = None if args.no_cpu_baseline else cpu_baseline_prefill(wp, q, k, v)
+        del qd, kd, vd, out, lse
+
+    if args.only in (None, "decode"):
+        log(f"[bench] generating decode workload {wd.name}")
+        kv = workloads.workload_paged_inputs(wd, nan_tails=True)
+        dt = fa.BF16 if wd.kv_dtype == "bf16" else fa.FP8_E4M3FN
+        d = dict(q=kv.q.cuda(), k=kv.k_pages.cuda(), v=kv.v_pages.cuda(), pt=kv.page_table.cuda(),
+                 sl=kv.seqlens.cuda(), ks=None if kv.k_scale is None else kv.k_scale.cuda(),
+                 vs=None if kv.v_scale is None else kv.v_scale.cuda())
+        t0 = time.perf_counter()
+        plan = fa.fa_decode_plan(kv.seqlens, kv.page_table, kv.num_pages, wd.Hq, wd.Hkv, wd.D, dt, 0)
+        plan_ms = (time.perf_counter() - t0) * 1e3
+        items, _, chunk = plan.items()
+        out = torch.empty_like(d["q"])
+        lse = torch.empty(d["q"].shape[:2], dtype=torch.float32, device=d["q"].device)
+        # Rotate copies of the KV pools when they would fit in the 256 MB
+        # last-level cache, so every step reads from HBM.
+        pool_bytes = d["k"].numel() * d["k"].element_size() * 2
+        n_copies = 1 if pool_bytes > 1024 ** 3 else 4
+        pools = [(d["k"], d["v"])] + [(d["k"].clone(), d["v"].clone()) for _ in range(n_copies - 1)]
+        it = [0]
+
+        def dec():
+            kk, vv = pools[it[0] % n_copies]
+            it[0] += 1
+            fa.fa_decode_run(plan, d["q"], kk, vv, d["pt"], d["sl"], plan.num_splits, out, lse,
+                             d["ks"], d["vs"], wd.scale, stream)
+
+        t = time_calls(dec, args.steps, args.warmup, stream)
+        res["decode_ms"] = t
+        res["decode_bytes"] = decode_bytes(kv, wd)
+        res["decode_plan"] = dict(plan_ms=round(plan_ms, 3), items=int(len(items)), chunk_pages=chunk,
+                                  num_splits=plan.num_splits, pages=int(kv.num_pages),
+                                  pool_copies_rotated=n_copies)
+        log(f"[bench] decode median {statistics.median(t):.4f} ms min {min(t):.4f} ms plan {plan_ms:.2f} ms")
+        res["decode_cpu"] = None if args.no_cpu_baseline else cpu_baseline_decode(wd, kv)
+        del d, pools
+
+    line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic"}
+    ms_step = 0.0
+    if "prefill_ms" in res:
+        t_pf = statistics.mean(res["prefill_ms"])
+        ms_step += t_pf
+        flops = prefill_flops(wp)
+        tflops = flops / (t_pf * 1e-3) / 1e12
+        line.update(value=round(tflops, 2), unit="TFLOP/s")
+        line["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                            "traffic": read_traffic(f"prefill_bf16_wl{wp.wid}_traffic.txt",
+                                                    "exact_attention_20_amd/csrc/prefill_bf16.hip"),
+                            "kernel": "prefill_bf16_kernel",
+                            "launch_ms_mean": round(t_pf, 5), "launch_ms_median": round(statistics.median(res["prefill_ms"]), 5),
+                            "flops_per_launch": flops}
+        line["cpu_baseline"] = res["prefill_cpu"]
+    if "decode_ms" in res:
+        t_dc = statistics.mean(res["decode_ms"])
+        ms_step += t_dc
+        gbs = res["decode_bytes"] / (t_dc * 1e-3) / 1e9
+        dec = {"metric": "paged decode HBM GB/s (split-KV + LSE merge)", "value": round(gbs, 1),
+               "unit": "GB/s", "ms_mean": round(t_dc, 5), "ms_median": round(statistics.median(res["decode_ms"]), 5),
+               "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(gbs / PEAK_HBM_GBS, 4),
+                            "traffic": read_traffic(f"decode_wl{wd.wid}_traffic.txt",
+                                                    "exact_attention_20_amd/csrc/decode.hip"),
+                            "kernel": "decode_split_kernel + lse_merge_kernel",
+                            "bytes_per_launch": res["decode_bytes"]},
+               "plan": res["decode_plan"], "cpu_baseline": res["decode_cpu"]}
+        line["decode"] = dec
+        if "value" not in line:
+            line.update(value=dec["value"], unit="GB/s")
+            line["roofline"] = dec["roofline"]
+            line["cpu_baseline"] = dec["cpu_baseline"]
+    line["ms_per_step"] = round(ms_step, 5)
+    cfg = {"workload": " + ".join(
+        ([wp.name] if "prefill_ms" in res else []) + ([wd.name] if "decode_ms" in res else []))}
+    if "prefill_ms" in res:
+        cfg["prefill"] = dict(B=wp.B, Hq=wp.Hq, Hkv=wp.Hkv, S=wp.S, D=wp.D, causal=True, dtype="bf16")
+    if "decode_ms" in res:
+        cfg["decode"] = dict(B=wd.B, Hq=wd.Hq, Hkv=wd.Hkv, D=wd.D, kv_dtype=wd.kv_dtype, page=64,
+                             lengths=list(wd.lengths), total_tokens=int(kv.seqlens.sum()))
+    line["config"] = cfg
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

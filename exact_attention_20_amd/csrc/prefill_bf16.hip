@@ -24,8 +24,10 @@
 //    argument's FMA) and exponentiated with v_exp_f32. The running max is
 //    lazy: it moves only when a tile's max exceeds it by more than kTau, so
 //    the O^T rescale (64 multiplies per lane) happens only on the first tiles
-//    of a row. The normaliser l is summed from the bf16-rounded P that the
-//    second MFMA consumes, so the normalisation matches the weights applied.
+//    of a row. Two normalisers are kept: the sum of the bf16-rounded P that
+//    the second MFMA consumes (one v_dot2 with ones per pair) divides O, so
+//    the normalisation matches the weights applied; the fp32 sum of P gives
+//    the LSE.
 //  * K/V for tile t+1 are fetched from HBM into registers while tile t is
 //    computed; LDS writes of V go through a 16-byte XOR swizzle so the
 //    transposing stores do not collide in the same banks.
@@ -121,7 +123,8 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a, int n_
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
   float m = kNegInf;  // running max of this query row, log2 units (same in lane and lane^32)
-  float l = 0.f;      // this lane's share of the normaliser
+  float lr = 0.f;     // this lane's share of sum(bf16(p)): normalises O (matches the MFMA weights)
+  float le = 0.f;     // this lane's share of sum(p) in fp32: gives the LSE
   const float c = a.scale * kLog2e;
 
   // ---- global -> register staging of one K/V tile.
@@ -215,7 +218,8 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a, int n_
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
       const float mn = need ? mxs : m;
       const float alpha = need ? fast_exp2(m - mn) : 1.f;
-      l *= alpha;
+      lr *= alpha;
+      le *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -236,7 +240,8 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a, int n_
         const float p0 = fast_exp2(__builtin_fmaf(sv[base + 2 * j], c, -mu));
         const float p1 = fast_exp2(__builtin_fmaf(sv[base + 2 * j + 1], c, -mu));
         w[j] = pack_bf16x2(p0, p1);
-        l += __uint_as_float(w[j] << 16) + __uint_as_float(w[j] & 0xffff0000u);
+        lr = dot2_bf16(w[j], 0x3f803f80u, lr);  // + bf16(p0) + bf16(p1)
+        le += p0 + p1;
       }
       pf[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
     }
@@ -251,10 +256,11 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a, int n_
       }
   }
 
-  // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2
-  const float lt = l + shfl_xor_f32(l, 32);
+  // ---- epilogue: O = O^T / sum(bf16 p), LSE = (m + log2 sum(p)) ln 2
+  const float lrt = lr + shfl_xor_f32(lr, 32);
+  const float let_ = le + shfl_xor_f32(le, 32);
   if (qrow >= a.Sq) return;
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float inv = lrt > 0.f ? 1.f / lrt : 0.f;
   uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + ((size_t)b * a.Hq + h) * (size_t)a.Sq * kD + (size_t)qrow * kD;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -266,7 +272,7 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a, int n_
       *reinterpret_cast<uint2*>(O + d) = w;
     }
   if (hi == 0)
-    a.lse[((size_t)b * a.Hq + h) * a.Sq + qrow] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
+    a.lse[((size_t)b * a.Hq + h) * a.Sq + qrow] = let_ > 0.f ? (m + __log2f(let_)) * kLn2 : kNegInf;
 }
 
 }  // namespace
