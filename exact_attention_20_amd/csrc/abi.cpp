@@ -12,7 +12,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/fa.h"
+#include "fa.h"
 #include "fa_internal.h"
 
 namespace {

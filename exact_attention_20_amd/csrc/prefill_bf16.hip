@@ -8,18 +8,25 @@
 // leaves registers.
 //
 // gfx950 design.
-//  * Workgroup = 4 wavefronts = 128 query rows (32 per wavefront); K/V tiles
-//    of 64 keys are staged in LDS (K row-major, V transposed) and shared by
-//    the 4 wavefronts.
+//  * Workgroup = NW wavefronts x 32 query rows; K/V tiles of 64 keys are
+//    staged row-major in LDS and shared by all wavefronts. V reaches the
+//    second MFMA through gfx950's transposing LDS read (ds_read_b64_tr_b16),
+//    so no thread ever transposes data in registers.
 //  * Both contractions use v_mfma_f32_32x32x16_bf16 (fp32 accumulate) in the
 //    transposed form S^T = K Q^T and O^T = V^T P^T. In the 32x32 accumulator
 //    layout a lane then owns one query column and 16 keys of it, so the row
-//    max and row sum are in-lane plus one exchange with the partner lane
-//    (lane ^ 32), and P^T leaves the first MFMA already in the B-operand
+//    max and row sums are in-lane plus one v_permlane32_swap with the partner
+//    lane (lane ^ 32), and P^T leaves the first MFMA already in the B-operand
 //    layout of the second (no LDS round trip). To make the 8 keys a lane owns
 //    contiguous, the K rows are fed to the first MFMA in a fixed permuted
 //    order (kperm below); the order of a contraction's k index is free as
 //    long as both operands agree.
+//  * Software pipeline inside each wavefront: the scores of tile t+1 are
+//    computed (MFMA) while the softmax of tile t runs on the VALU and its P*V
+//    product is issued, so the matrix cores and the vector ALUs work at the
+//    same time. K therefore runs one tile ahead of V through two pairs of LDS
+//    buffers, and the HBM loads of the following tiles are in flight in
+//    registers meanwhile; one barrier per tile.
 //  * Scores are scaled into log2 units once (scale*log2e folded into the exp
 //    argument's FMA) and exponentiated with v_exp_f32. The running max is
 //    lazy: it moves only when a tile's max exceeds it by more than kTau, so
@@ -28,9 +35,10 @@
 //    the second MFMA consumes (one v_dot2 with ones per pair) divides O, so
 //    the normalisation matches the weights applied; the fp32 sum of P gives
 //    the LSE.
-//  * K/V for tile t+1 are fetched from HBM into registers while tile t is
-//    computed; LDS writes of V go through a 16-byte XOR swizzle so the
-//    transposing stores do not collide in the same banks.
+//  * LDS row strides (272 B for K, 320 B for V) make the 16-byte row writes,
+//    the K operand reads and the transposing V reads free of bank conflicts
+//    (measured with the LDS bank-conflict counter), and every read address is
+//    a per-lane base plus a compile-time offset.
 //  * Grid: one workgroup per (query tile, batch, head). With causal masking
 //    the heaviest query tiles (most keys) are issued first. Heads are ordered
 //    so that workgroups with equal id mod 8 -- which the dispatcher places on
@@ -42,11 +50,10 @@ namespace fa {
 
 namespace {
 
-constexpr int kD = 128;   // head dim
-constexpr int kBr = 128;  // query rows per workgroup
-constexpr int kBc = 64;   // keys per tile
-constexpr int kKst = kD + 8;   // K row stride in LDS (bf16 elements) = 272 B
-constexpr int kVst = kBc + 8;  // V^T row stride in LDS (bf16 elements) = 144 B
+constexpr int kD = 128;        // head dim
+constexpr int kBc = 64;        // keys per tile
+constexpr int kQst = kD + 8;   // Q row stride in LDS (bf16 elements) = 272 B
+constexpr int kRow = kD * 2;   // K/V row in LDS: 256 B, unpadded, 16-byte units XOR-swizzled
 constexpr float kTau = 8.0f;   // lazy max threshold (log2 units)
 
 // MFMA row r of the S^T tile reads key kperm(r): with it, accumulator
@@ -56,20 +63,42 @@ __device__ __forceinline__ int kperm(int r) {
   return 16 * (a >> 1) + 8 * hh + 4 * (a & 1) + c;
 }
 
-// Byte offset of V^T element (d, key) inside the V^T LDS tile, with the
-// 16-byte column unit XOR-swizzled by the row.
-__device__ __forceinline__ int vt_off(int d, int key) {
-  const int unit = (key >> 3) ^ ((d >> 4) & 7);
-  return d * (kVst * 2) + unit * 16 + (key & 7) * 2;
-}
-
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kBc * kKst];
-  __shared__ __attribute__((aligned(16))) char vt_lds[kD * kVst * 2];
+// x combined with the value of lane ^ 32 (both halves get the result).
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each group of 16
+// lanes, lane i receives element (i & 3) of the 8-byte chunks addressed by
+// lanes 4j + (i >> 2), j = 0..3.
+__device__ __forceinline__ uint2 lds_read_tr16(const char* p) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
+  constexpr int NT = 64 * NW;                 // threads
+  constexpr int BR = 32 * NW;                 // query rows per workgroup
+  constexpr int KBUF = kBc * kRow;            // bytes per K buffer
+  constexpr int VBUF = kBc * kRow;            // bytes per V buffer
+  constexpr int QBUF = BR * kQst * 2;         // bytes of the Q tile
+  constexpr int BLK = (kBc * kRow / 1024) / NW;  // 1 KB direct-load blocks per wave per tile
+  __shared__ __attribute__((aligned(16))) char k_lds[2 * KBUF];
+  __shared__ __attribute__((aligned(16))) char v_lds[2 * VBUF];
+  __shared__ __attribute__((aligned(16))) char q_lds[QBUF];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -93,29 +122,30 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a, int n_
     g = bg % a.Hkv;
     h = g * G + j;
   }
-  const int q0 = qt * kBr;
+  const int q0 = qt * BR;
   const int off = a.Sk - a.Sq;  // causal: key j visible to query i iff j <= i + off
   int kend = a.Sk;
-  if (a.causal) kend = min(a.Sk, q0 + kBr + off);
+  if (a.causal) kend = min(a.Sk, q0 + BR + off);
   const int n_kt = kend > 0 ? (kend + kBc - 1) / kBc : 0;
 
   const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + h) * (size_t)a.Sq * kD;
   const uint16_t* K = reinterpret_cast<const uint16_t*>(a.k) + ((size_t)b * a.Hkv + g) * (size_t)a.Sk * kD;
   const uint16_t* V = reinterpret_cast<const uint16_t*>(a.v) + ((size_t)b * a.Hkv + g) * (size_t)a.Sk * kD;
 
-  // ---- Q^T as the B operand of S^T = K Q^T: lane holds query (q0+32w+col),
-  // dims 16*kk + 8*hi + 0..7 for kk = 0..7.
+  // ---- The Q tile goes to LDS once (row-major, 272-byte rows); the B
+  // operand of S^T = K Q^T for lane (col, hi) is query q0+32w+col, dims
+  // 16*kk + 8*hi + 0..7, read from there at each use. Keeping it out of
+  // registers leaves room for two score tiles in flight without spilling.
   const int qrow = q0 + wave * 32 + col;
-  bf16x8_t qf[8];
-  {
-    const bool live = qrow < a.Sq;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (live) v = *reinterpret_cast<const uint4*>(Q + (size_t)qrow * kD + 16 * kk + 8 * hi);
-      qf[kk] = __builtin_bit_cast(bf16x8_t, v);
-    }
+  for (int it = 0; it < BR * 16 / NT; ++it) {
+    const int chunk = it * NT + tid;
+    const int r = chunk >> 4;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (q0 + r < a.Sq) v = *reinterpret_cast<const uint4*>(Q + (size_t)(q0 + r) * kD + 8 * (chunk & 15));
+    *reinterpret_cast<uint4*>(q_lds + (r * kQst + 8 * (chunk & 15)) * 2) = v;
   }
+  const char* q_lane = q_lds + ((wave * 32 + col) * kQst + 8 * hi) * 2;
 
   f32x16_t o[4];
 #pragma unroll
@@ -127,62 +157,64 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a, int n_
   float le = 0.f;     // this lane's share of sum(p) in fp32: gives the LSE
   const float c = a.scale * kLog2e;
 
-  // ---- global -> register staging of one K/V tile.
-  // K: 4 rounds of 16-byte chunks, chunk (it*256 + tid) = key (chunk>>4), dims 8*(chunk&15).
-  // V: thread owns keys 4*(tid>>4)+0..3, dims 8*(tid&15)+0..7.
-  uint4 kreg[4], vreg[4];
-  const int vkq = tid >> 4, vdc = tid & 15;
-  auto fetch = [&](int k0) {
+  // ---- K/V tiles go from HBM straight into LDS (buffer_load ... lds: no
+  // registers, no LDS store instructions). One such load moves 1 KB: lane l
+  // fills LDS unit (l & 15) of row 4j + (l >> 4). Rows are stored unpadded
+  // with their 16-byte units XOR-swizzled -- K: unit c of row r sits at
+  // c ^ (r & 15); V: at c ^ 4*(r & 3) -- so each lane fetches the global unit
+  // that belongs in the LDS slot it fills. A buffer resource bounded by Sk
+  // rows makes loads past the last key return zeros.
+  const __amdgpu_buffer_rsrc_t k_rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(K), (short)0, a.Sk * kRow, 0x00020000);
+  const __amdgpu_buffer_rsrc_t v_rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(V), (short)0, a.Sk * kRow, 0x00020000);
+  const int dl_row = lane >> 4, dl_pos = lane & 15;
+  auto load_tile = [&](const __amdgpu_buffer_rsrc_t& rs, int k0, char* buf, bool is_v) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int chunk = it * 256 + tid;
-      const int key = k0 + (chunk >> 4);
-      kreg[it] = key < a.Sk ? *reinterpret_cast<const uint4*>(K + (size_t)key * kD + 8 * (chunk & 15))
-                            : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = k0 + 4 * vkq + j;
-      vreg[j] = key < a.Sk ? *reinterpret_cast<const uint4*>(V + (size_t)key * kD + 8 * vdc)
-                           : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto stage = [&]() {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int chunk = it * 256 + tid;
-      *reinterpret_cast<uint4*>(&k_lds[(chunk >> 4) * kKst + 8 * (chunk & 15)]) = kreg[it];
-    }
-    const uint32_t v0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-    const uint32_t v1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
-    const uint32_t v2[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
-    const uint32_t v3[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int d0 = 8 * vdc + 2 * w;
-      // keys 4*vkq .. +3 of dims d0 (low halves) and d0+1 (high halves)
-      const uint2 lo = make_uint2(perm_b32(v1[w], v0[w], 0x05040100u), perm_b32(v3[w], v2[w], 0x05040100u));
-      const uint2 hv = make_uint2(perm_b32(v1[w], v0[w], 0x07060302u), perm_b32(v3[w], v2[w], 0x07060302u));
-      *reinterpret_cast<uint2*>(vt_lds + vt_off(d0, 4 * vkq)) = lo;
-      *reinterpret_cast<uint2*>(vt_lds + vt_off(d0 + 1, 4 * vkq)) = hv;
+    for (int i = 0; i < BLK; ++i) {
+      const int j = wave * BLK + i;
+      const int r = 4 * j + dl_row;
+      const int unit = is_v ? (dl_pos ^ (4 * (r & 3))) : (dl_pos ^ (r & 15));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(buf + j * 1024), 16, (k0 + r) * kRow + unit * 16, 0, 0, 0);
     }
   };
+  auto load_k = [&](int t) { load_tile(k_rs, t * kBc, k_lds + (t & 1) * KBUF, false); };
+  auto load_v = [&](int t) { load_tile(v_rs, t * kBc, v_lds + (t & 1) * VBUF, true); };
+  // This wavefront's direct loads have landed in LDS (the compiler does not
+  // track them, so the wait is explicit; the following barrier publishes them).
+  auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
-  const int krow0 = kperm(col);  // K row this lane feeds for MFMA row `col`
-  if (n_kt > 0) fetch(0);
-  for (int t = 0; t < n_kt; ++t) {
-    const int k0 = t * kBc;
-    __syncthreads();  // previous tile's LDS reads are done
-    stage();
-    __syncthreads();
-    if (t + 1 < n_kt) fetch(k0 + kBc);
+  // Per-lane LDS read addresses.
+  // K (A operand of S^T = K Q^T): MFMA row `col` feeds key R = kperm(col),
+  //   global unit 2*kk + hi of that row, stored at unit (2*kk + hi) ^ (R & 15);
+  //   the second 32-key half is 32 rows further.
+  int k_off[8];
+  {
+    const int R = kperm(col);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) k_off[kk] = R * kRow + 16 * ((2 * kk + hi) ^ (R & 15));
+  }
+  // V (A operand of O^T = V^T P^T, rows d = 32*db + col, k-slots = keys
+  // 16*ks + 8*hi + 0..7): two transposing reads per operand; lane L of each
+  // 16-lane group g addresses key 16*ks + 8*(g>>1) + 4*r + (L>>2) and dims
+  // 32*db + 16*(g&1) + 4*(L&3) .. +3, so lane i of the group receives keys
+  // +4r .. +4r+3 of dim 32*db + 16*(g&1) + i. With (L>>2) = key & 3 the
+  // swizzle moves the 64-byte block db to db ^ (L>>2).
+  int v_off[4];
+  {
+    const int vg = lane >> 4, vL = lane & 15, q4 = vL >> 2;
+    const int v_lane = (8 * (vg >> 1) + q4) * kRow + 16 * (2 * (vg & 1) + ((vL & 3) >> 1)) + 8 * (vL & 1);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) v_off[db] = v_lane + 64 * (db ^ q4);
+  }
 
-    // Wavefront-uniform skip of tiles entirely above this wavefront's diagonal.
-    const int wq0 = q0 + wave * 32;
-    if (a.causal && k0 > wq0 + 31 + off) continue;
+  const int wq0 = q0 + wave * 32;
+  // Tile t holds work for this wavefront unless it lies wholly above its diagonal.
+  auto active = [&](int t) { return !(a.causal && t * kBc > wq0 + 31 + off); };
 
-    // ---- S^T = K Q^T for the two 32-key halves of the tile.
-    f32x16_t s0, s1;
+  auto qk = [&](int kbuf, f32x16_t& s0, f32x16_t& s1) {
+    const char* kl = k_lds + kbuf * KBUF;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       s0[i] = 0.f;
@@ -190,29 +222,33 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a, int n_
     }
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(&k_lds[krow0 * kKst + 16 * kk + 8 * hi]);
-      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(&k_lds[(32 + krow0) * kKst + 16 * kk + 8 * hi]);
-      s0 = mfma32(a0, qf[kk], s0);
-      s1 = mfma32(a1, qf[kk], s1);
+      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(kl + k_off[kk]);
+      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(kl + k_off[kk] + 32 * kRow);
+      const bf16x8_t qf = *reinterpret_cast<const bf16x8_t*>(q_lane + 32 * kk);
+      s0 = mfma32(a0, qf, s0);
+      s1 = mfma32(a1, qf, s1);
     }
+  };
 
-    // ---- mask (ragged key tail, causal diagonal)
-    const bool need_mask = (k0 + kBc > a.Sk) || (a.causal && k0 + kBc - 1 > wq0 + off);
-    if (need_mask) {
-      const int lim = a.causal ? min(a.Sk - 1, qrow + off) : a.Sk - 1;
+  // Causal / ragged-tail mask of tile t's scores (keys beyond this row's
+  // diagonal or beyond Sk become -inf).
+  auto mask = [&](int t, f32x16_t& s0, f32x16_t& s1) {
+    const int k0 = t * kBc;
+    const int lim = a.causal ? min(a.Sk - 1, qrow + off) : a.Sk - 1;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = k0 + 16 * (i >> 3) + 8 * hi + (i & 7);
-        if (key > lim) s0[i] = kNegInf;
-        if (key + 32 > lim) s1[i] = kNegInf;
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int key = k0 + 16 * (i >> 3) + 8 * hi + (i & 7);
+      if (key > lim) s0[i] = kNegInf;
+      if (key + 32 > lim) s1[i] = kNegInf;
     }
+  };
 
-    // ---- online softmax (lazy max)
-    float mx = kNegInf;
+  // Row max of the tile and the lazy move of the running max.
+  auto update_max = [&](const f32x16_t& s0, const f32x16_t& s1) {
+    float mx = fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s1[0], s1[1]));
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-    mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+    for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(fmaxf(s0[i], s0[i + 1]), fmaxf(s1[i], s1[i + 1])));
+    mx = xor32_max(mx);
     const float mxs = mx * c;
     const bool need = mxs > m + kTau;
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
@@ -226,10 +262,24 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a, int n_
         for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
       m = mn;
     }
-    const float mu = (m == kNegInf) ? 0.f : m;
+  };
 
-    // P^T in bf16 as B operands of O^T = V^T P^T: pf[ks] covers keys 16ks..16ks+15.
-    bf16x8_t pf[4];
+  // P = exp2(s*c - m) in bf16, the two normalisers, and O^T += V^T P^T from
+  // V^T buffer vbuf. With kb >= 0 the scores of the next tile are computed
+  // from K buffer kb in the same straight-line block, so the scheduler can
+  // interleave those MFMAs with this tile's exponentials.
+  auto exp_pv_qk = [&](int vbuf, const f32x16_t& s0, const f32x16_t& s1, int kb, f32x16_t& n0,
+                       f32x16_t& n1) {
+    const float mu = (m == kNegInf) ? 0.f : m;
+    const char* vl = v_lds + vbuf * VBUF;
+    const char* kl = k_lds + (kb < 0 ? 0 : kb) * KBUF;
+    if (kb >= 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        n0[i] = 0.f;
+        n1[i] = 0.f;
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const f32x16_t& sv = (ks < 2) ? s0 : s1;
@@ -243,22 +293,88 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a, int n_
         lr = dot2_bf16(w[j], 0x3f803f80u, lr);  // + bf16(p0) + bf16(p1)
         le += p0 + p1;
       }
-      pf[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
-    }
-
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(vt_lds + vt_off(32 * db + col, 16 * ks + 8 * hi));
-        o[db] = mfma32(va, pf[ks], o[db]);
+        const char* vp = vl + v_off[db] + 16 * ks * kRow;
+        const uint2 v0 = lds_read_tr16(vp);
+        const uint2 v1 = lds_read_tr16(vp + 4 * kRow);
+        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
+        o[db] = mfma32(va, pf, o[db]);
       }
+      if (kb >= 0) {
+#pragma unroll
+        for (int kk = 2 * ks; kk < 2 * ks + 2; ++kk) {
+          const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(kl + k_off[kk]);
+          const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(kl + k_off[kk] + 32 * kRow);
+          const bf16x8_t qf = *reinterpret_cast<const bf16x8_t*>(q_lane + 32 * kk);
+          n0 = mfma32(a0, qf, n0);
+          n1 = mfma32(a1, qf, n1);
+        }
+      }
+    }
+  };
+
+  // Start the loads of K(t+2) over K(t) and of V(t+1) over V(t-1): both
+  // buffers were last read in iteration t-1, before its closing barrier.
+  auto prefetch = [&](int t) {
+    if (t + 2 < n_kt) load_k(t + 2);
+    if (t + 1 < n_kt) load_v(t + 1);
+  };
+
+  // Tiles below the whole workgroup's diagonal and inside Sk need no mask
+  // and have work for every wavefront: they run the branch-free main loop.
+  int n_main = a.Sk / kBc;
+  if (a.causal) n_main = min(n_main, max(0, (q0 + off + 1) / kBc));
+  n_main = min(n_main, n_kt);
+
+  // ---- prologue: K(0), K(1), V(0) in LDS, then S(0).
+  f32x16_t sc0, sc1;
+  if (n_kt > 0) {
+    load_k(0);
+    load_v(0);
+    if (n_kt > 1) load_k(1);
+  }
+  wait_loads();
+  __syncthreads();  // Q, K(0), K(1), V(0) visible to every wavefront
+  if (n_kt > 0 && active(0)) qk(0, sc0, sc1);
+  __syncthreads();  // every wavefront has read K(0) before K(2) replaces it
+
+  int t = 0;
+  for (; t < n_main; ++t) {
+    f32x16_t sn0, sn1;
+    prefetch(t);
+    update_max(sc0, sc1);
+    // The next tile's scores are computed even past the last tile (from a
+    // stale buffer, then discarded) to keep this block free of branches.
+    exp_pv_qk(t & 1, sc0, sc1, (t + 1) & 1, sn0, sn1);
+    sc0 = sn0;
+    sc1 = sn1;
+    wait_loads();
+    __syncthreads();
+  }
+  for (; t < n_kt; ++t) {
+    f32x16_t sn0, sn1;
+    prefetch(t);
+    const bool next = t + 1 < n_kt && active(t + 1);
+    if (active(t)) {
+      mask(t, sc0, sc1);
+      update_max(sc0, sc1);
+      exp_pv_qk(t & 1, sc0, sc1, next ? (t + 1) & 1 : -1, sn0, sn1);
+    } else if (next) {
+      qk((t + 1) & 1, sn0, sn1);
+    }
+    if (next) {
+      sc0 = sn0;
+      sc1 = sn1;
+    }
+    wait_loads();
+    __syncthreads();
   }
 
   // ---- epilogue: O = O^T / sum(bf16 p), LSE = (m + log2 sum(p)) ln 2
-  const float lrt = lr + shfl_xor_f32(lr, 32);
-  const float let_ = le + shfl_xor_f32(le, 32);
+  const float lrt = xor32_sum(lr);
+  const float let_ = xor32_sum(le);
   if (qrow >= a.Sq) return;
   const float inv = lrt > 0.f ? 1.f / lrt : 0.f;
   uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + ((size_t)b * a.Hq + h) * (size_t)a.Sq * kD + (size_t)qrow * kD;
@@ -278,11 +394,12 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(PrefillArgs a, int n_
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
-  const int n_qtiles = (a.Sq + kBr - 1) / kBr;
+  constexpr int kNW = 8;
+  const int n_qtiles = (a.Sq + 32 * kNW - 1) / (32 * kNW);
   const int nbh = a.B * a.Hq;
   const long long blocks = (long long)n_qtiles * nbh;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(prefill_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, n_qtiles, nbh);
+  hipLaunchKernelGGL(prefill_bf16_kernel<kNW>, dim3((unsigned)blocks), dim3(64 * kNW), 0, s, a, n_qtiles, nbh);
   return hipGetLastError();
 }
 
