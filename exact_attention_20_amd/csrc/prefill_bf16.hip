@@ -8,10 +8,10 @@
 // leaves registers.
 //
 // gfx950 design.
-//  * Workgroup = NW wavefronts x 32 query rows; K/V tiles of 64 keys are
-//    staged row-major in LDS and shared by all wavefronts. V reaches the
-//    second MFMA through gfx950's transposing LDS read (ds_read_b64_tr_b16),
-//    so no thread ever transposes data in registers.
+//  * Workgroup = NW wavefronts, each owning QB blocks of 32 query rows, so
+//    BR = 32*NW*QB rows per workgroup. K/V tiles of 64 keys are shared by all
+//    wavefronts through LDS; every K or V fragment a wavefront reads from
+//    LDS feeds QB matrix instructions.
 //  * Both contractions use v_mfma_f32_32x32x16_bf16 (fp32 accumulate) in the
 //    transposed form S^T = K Q^T and O^T = V^T P^T. In the 32x32 accumulator
 //    layout a lane then owns one query column and 16 keys of it, so the row
@@ -21,24 +21,24 @@
 //    contiguous, the K rows are fed to the first MFMA in a fixed permuted
 //    order (kperm below); the order of a contraction's k index is free as
 //    long as both operands agree.
+//  * K/V tiles travel HBM -> LDS with buffer_load ... lds (no registers, no
+//    LDS store instructions); a buffer resource bounded by Sk rows returns
+//    zeros past the last key. V reaches the second MFMA through gfx950's
+//    transposing LDS read (ds_read_b64_tr_b16), so nothing is transposed in
+//    registers. Rows are stored unpadded with their 16-byte units
+//    XOR-swizzled so that the operand reads are free of bank conflicts.
 //  * Software pipeline inside each wavefront: the scores of tile t+1 are
 //    computed (MFMA) while the softmax of tile t runs on the VALU and its P*V
-//    product is issued, so the matrix cores and the vector ALUs work at the
-//    same time. K therefore runs one tile ahead of V through two pairs of LDS
-//    buffers, and the HBM loads of the following tiles are in flight in
-//    registers meanwhile; one barrier per tile.
+//    product is issued. K runs one tile ahead of V through two pairs of LDS
+//    buffers whose next contents are in flight from HBM meanwhile; one
+//    barrier per tile.
 //  * Scores are scaled into log2 units once (scale*log2e folded into the exp
 //    argument's FMA) and exponentiated with v_exp_f32. The running max is
 //    lazy: it moves only when a tile's max exceeds it by more than kTau, so
-//    the O^T rescale (64 multiplies per lane) happens only on the first tiles
-//    of a row. Two normalisers are kept: the sum of the bf16-rounded P that
-//    the second MFMA consumes (one v_dot2 with ones per pair) divides O, so
-//    the normalisation matches the weights applied; the fp32 sum of P gives
-//    the LSE.
-//  * LDS row strides (272 B for K, 320 B for V) make the 16-byte row writes,
-//    the K operand reads and the transposing V reads free of bank conflicts
-//    (measured with the LDS bank-conflict counter), and every read address is
-//    a per-lane base plus a compile-time offset.
+//    the O^T rescale happens only on the first tiles of a row. Two normalisers
+//    are kept: the sum of the bf16-rounded P that the second MFMA consumes
+//    (one v_dot2 with ones per pair) divides O, so the normalisation matches
+//    the weights applied; the fp32 sum of P gives the LSE.
 //  * Grid: one workgroup per (query tile, batch, head). With causal masking
 //    the heaviest query tiles (most keys) are issued first. Heads are ordered
 //    so that workgroups with equal id mod 8 -- which the dispatcher places on
@@ -88,10 +88,11 @@ __device__ __forceinline__ uint2 lds_read_tr16(const char* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-template <int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
+template <int NW, int QB>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   constexpr int NT = 64 * NW;                 // threads
-  constexpr int BR = 32 * NW;                 // query rows per workgroup
+  constexpr int BR = 32 * NW * QB;            // query rows per workgroup
   constexpr int KBUF = kBc * kRow;            // bytes per K buffer
   constexpr int VBUF = kBc * kRow;            // bytes per V buffer
   constexpr int QBUF = BR * kQst * 2;         // bytes of the Q tile
@@ -115,6 +116,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
     h = e % a.Hq;
     g = a.kv_map[h];
   } else {
+    // e = (b*Hkv + g) + B*Hkv*j enumerates query head h = g*G + j, so heads
+    // with equal e % 8 share KV heads when B*Hkv is a multiple of 8.
     const int G = a.Hq / a.Hkv;
     const int bg = e % (a.B * a.Hkv);
     const int j = e / (a.B * a.Hkv);
@@ -132,11 +135,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   const uint16_t* K = reinterpret_cast<const uint16_t*>(a.k) + ((size_t)b * a.Hkv + g) * (size_t)a.Sk * kD;
   const uint16_t* V = reinterpret_cast<const uint16_t*>(a.v) + ((size_t)b * a.Hkv + g) * (size_t)a.Sk * kD;
 
-  // ---- The Q tile goes to LDS once (row-major, 272-byte rows); the B
-  // operand of S^T = K Q^T for lane (col, hi) is query q0+32w+col, dims
-  // 16*kk + 8*hi + 0..7, read from there at each use. Keeping it out of
-  // registers leaves room for two score tiles in flight without spilling.
-  const int qrow = q0 + wave * 32 + col;
+  // ---- The Q tile goes to LDS once (row-major, 272-byte rows). Query block
+  // qb of this wavefront is rows 32*(QB*wave + qb) .. +31 of the tile; the B
+  // operand of S^T = K Q^T for lane (col, hi) is that block's row col, dims
+  // 16*kk + 8*hi + 0..7.
 #pragma unroll
   for (int it = 0; it < BR * 16 / NT; ++it) {
     const int chunk = it * NT + tid;
@@ -145,25 +147,37 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
     if (q0 + r < a.Sq) v = *reinterpret_cast<const uint4*>(Q + (size_t)(q0 + r) * kD + 8 * (chunk & 15));
     *reinterpret_cast<uint4*>(q_lds + (r * kQst + 8 * (chunk & 15)) * 2) = v;
   }
-  const char* q_lane = q_lds + ((wave * 32 + col) * kQst + 8 * hi) * 2;
+  const char* q_lane = q_lds + ((QB * wave * 32 + col) * kQst + 8 * hi) * 2;
+  constexpr int QBLK = 32 * kQst * 2;  // bytes between query blocks in LDS
 
-  f32x16_t o[4];
+  // Per query block: first row, this lane's row, running max (log2 units,
+  // same in lane and lane^32), shares of the two normalisers, O^T.
+  int wq0[QB], qrow[QB];
+  // The normalisers are kept as 4 partial sums each, so that their updates
+  // form 4 short dependency chains instead of one long one.
+  float m[QB], lr[QB][4], le[QB][4];
+  f32x16_t o[QB][4];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    wq0[qb] = q0 + (QB * wave + qb) * 32;
+    qrow[qb] = wq0[qb] + col;
+    m[qb] = kNegInf;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-  float m = kNegInf;  // running max of this query row, log2 units (same in lane and lane^32)
-  float lr = 0.f;     // this lane's share of sum(bf16(p)): normalises O (matches the MFMA weights)
-  float le = 0.f;     // this lane's share of sum(p) in fp32: gives the LSE
+    for (int j = 0; j < 4; ++j) {
+      lr[qb][j] = 0.f;  // sum(bf16(p)): normalises O (matches the MFMA weights)
+      le[qb][j] = 0.f;  // sum(p) in fp32: gives the LSE
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[qb][db][i] = 0.f;
+  }
   const float c = a.scale * kLog2e;
 
-  // ---- K/V tiles go from HBM straight into LDS (buffer_load ... lds: no
-  // registers, no LDS store instructions). One such load moves 1 KB: lane l
-  // fills LDS unit (l & 15) of row 4j + (l >> 4). Rows are stored unpadded
-  // with their 16-byte units XOR-swizzled -- K: unit c of row r sits at
-  // c ^ (r & 15); V: at c ^ 4*(r & 3) -- so each lane fetches the global unit
-  // that belongs in the LDS slot it fills. A buffer resource bounded by Sk
-  // rows makes loads past the last key return zeros.
+  // ---- K/V tiles: one direct load moves 1 KB, lane l filling LDS unit
+  // (l & 15) of row 4j + (l >> 4). K: unit c of row r sits at c ^ (r & 15);
+  // V: at c ^ 4*(r & 3); each lane fetches the global unit that belongs in the
+  // LDS slot it fills.
   const __amdgpu_buffer_rsrc_t k_rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(K), (short)0, a.Sk * kRow, 0x00020000);
   const __amdgpu_buffer_rsrc_t v_rs =
@@ -209,32 +223,37 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
     for (int db = 0; db < 4; ++db) v_off[db] = v_lane + 64 * (db ^ q4);
   }
 
-  const int wq0 = q0 + wave * 32;
-  // Tile t holds work for this wavefront unless it lies wholly above its diagonal.
-  auto active = [&](int t) { return !(a.causal && t * kBc > wq0 + 31 + off); };
+  // Tile t holds work for query block qb unless it lies wholly above its diagonal.
+  auto blk_active = [&](int t, int qb) { return !(a.causal && t * kBc > wq0[qb] + 31 + off); };
+  auto any_active = [&](int t) { return blk_active(t, QB - 1); };
 
-  auto qk = [&](int kbuf, f32x16_t& s0, f32x16_t& s1) {
+  // S^T for every query block from K buffer kbuf.
+  auto qk = [&](int kbuf, f32x16_t (&s)[QB][2]) {
     const char* kl = k_lds + kbuf * KBUF;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s0[i] = 0.f;
-      s1[i] = 0.f;
-    }
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[qb][0][i] = 0.f;
+        s[qb][1][i] = 0.f;
+      }
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(kl + k_off[kk]);
       const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(kl + k_off[kk] + 32 * kRow);
-      const bf16x8_t qf = *reinterpret_cast<const bf16x8_t*>(q_lane + 32 * kk);
-      s0 = mfma32(a0, qf, s0);
-      s1 = mfma32(a1, qf, s1);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const bf16x8_t qf = *reinterpret_cast<const bf16x8_t*>(q_lane + qb * QBLK + 32 * kk);
+        s[qb][0] = mfma32(a0, qf, s[qb][0]);
+        s[qb][1] = mfma32(a1, qf, s[qb][1]);
+      }
     }
   };
 
-  // Causal / ragged-tail mask of tile t's scores (keys beyond this row's
-  // diagonal or beyond Sk become -inf).
-  auto mask = [&](int t, f32x16_t& s0, f32x16_t& s1) {
+  // Causal / ragged-tail mask of tile t's scores for query block qb.
+  auto mask = [&](int t, int qb, f32x16_t& s0, f32x16_t& s1) {
     const int k0 = t * kBc;
-    const int lim = a.causal ? min(a.Sk - 1, qrow + off) : a.Sk - 1;
+    const int lim = a.causal ? min(a.Sk - 1, qrow[qb] + off) : a.Sk - 1;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = k0 + 16 * (i >> 3) + 8 * hi + (i & 7);
@@ -243,73 +262,93 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
     }
   };
 
-  // Row max of the tile and the lazy move of the running max.
-  auto update_max = [&](const f32x16_t& s0, const f32x16_t& s1) {
-    float mx = fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s1[0], s1[1]));
+  // Row max of the tile and the lazy move of block qb's running max.
+  auto update_max = [&](int qb, const f32x16_t& s0, const f32x16_t& s1) {
+    // balanced max tree over the 32 scores of this lane
+    float t8[8];
 #pragma unroll
-    for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(fmaxf(s0[i], s0[i + 1]), fmaxf(s1[i], s1[i + 1])));
+    for (int i = 0; i < 8; ++i) t8[i] = fmaxf(fmaxf(s0[2 * i], s0[2 * i + 1]), fmaxf(s1[2 * i], s1[2 * i + 1]));
+    float mx = fmaxf(fmaxf(fmaxf(t8[0], t8[1]), fmaxf(t8[2], t8[3])), fmaxf(fmaxf(t8[4], t8[5]), fmaxf(t8[6], t8[7])));
     mx = xor32_max(mx);
     const float mxs = mx * c;
-    const bool need = mxs > m + kTau;
+    const bool need = mxs > m[qb] + kTau;
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      const float mn = need ? mxs : m;
-      const float alpha = need ? fast_exp2(m - mn) : 1.f;
-      lr *= alpha;
-      le *= alpha;
+      const float mn = need ? mxs : m[qb];
+      const float alpha = need ? fast_exp2(m[qb] - mn) : 1.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lr[qb][j] *= alpha;
+        le[qb][j] *= alpha;
+      }
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-      m = mn;
+        for (int i = 0; i < 16; ++i) o[qb][db][i] *= alpha;
+      m[qb] = mn;
     }
   };
 
-  // P = exp2(s*c - m) in bf16, the two normalisers, and O^T += V^T P^T from
-  // V^T buffer vbuf. With kb >= 0 the scores of the next tile are computed
-  // from K buffer kb in the same straight-line block, so the scheduler can
-  // interleave those MFMAs with this tile's exponentials.
-  auto exp_pv_qk = [&](int vbuf, const f32x16_t& s0, const f32x16_t& s1, int kb, f32x16_t& n0,
-                       f32x16_t& n1) {
-    const float mu = (m == kNegInf) ? 0.f : m;
+  // P = exp2(s*c - m) in bf16 for the query blocks selected by `use`, both
+  // normalisers, and O^T += V^T P^T from V buffer vbuf. With kb >= 0 the
+  // scores of the next tile are computed from K buffer kb in the same
+  // straight-line block, so the scheduler can interleave those MFMAs with
+  // this tile's exponentials.
+  auto exp_pv_qk = [&](int vbuf, const f32x16_t (&s)[QB][2], const bool (&use)[QB], int kb,
+                       f32x16_t (&n)[QB][2]) {
+    float mu[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mu[qb] = (m[qb] == kNegInf) ? 0.f : m[qb];
     const char* vl = v_lds + vbuf * VBUF;
     const char* kl = k_lds + (kb < 0 ? 0 : kb) * KBUF;
     if (kb >= 0) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        n0[i] = 0.f;
-        n1[i] = 0.f;
-      }
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          n[qb][0][i] = 0.f;
+          n[qb][1][i] = 0.f;
+        }
     }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const f32x16_t& sv = (ks < 2) ? s0 : s1;
-      const int base = 8 * (ks & 1);
-      uint32_t w[4];
+      bf16x8_t pf[QB];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p0 = fast_exp2(__builtin_fmaf(sv[base + 2 * j], c, -mu));
-        const float p1 = fast_exp2(__builtin_fmaf(sv[base + 2 * j + 1], c, -mu));
-        w[j] = pack_bf16x2(p0, p1);
-        lr = dot2_bf16(w[j], 0x3f803f80u, lr);  // + bf16(p0) + bf16(p1)
-        le += p0 + p1;
+      for (int qb = 0; qb < QB; ++qb) {
+        if (!use[qb]) continue;
+        const f32x16_t& sv = s[qb][ks >> 1];
+        const int base = 8 * (ks & 1);
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p0 = fast_exp2(__builtin_fmaf(sv[base + 2 * j], c, -mu[qb]));
+          const float p1 = fast_exp2(__builtin_fmaf(sv[base + 2 * j + 1], c, -mu[qb]));
+          w[j] = pack_bf16x2(p0, p1);
+          lr[qb][j] = dot2_bf16(w[j], 0x3f803f80u, lr[qb][j]);  // + bf16(p0) + bf16(p1)
+          le[qb][j] += p0 + p1;
+        }
+        pf[qb] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
       }
-      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const char* vp = vl + v_off[db] + 16 * ks * kRow;
         const uint2 v0 = lds_read_tr16(vp);
         const uint2 v1 = lds_read_tr16(vp + 4 * kRow);
         const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
-        o[db] = mfma32(va, pf, o[db]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          if (use[qb]) o[qb][db] = mfma32(va, pf[qb], o[qb][db]);
       }
       if (kb >= 0) {
 #pragma unroll
         for (int kk = 2 * ks; kk < 2 * ks + 2; ++kk) {
           const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(kl + k_off[kk]);
           const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(kl + k_off[kk] + 32 * kRow);
-          const bf16x8_t qf = *reinterpret_cast<const bf16x8_t*>(q_lane + 32 * kk);
-          n0 = mfma32(a0, qf, n0);
-          n1 = mfma32(a1, qf, n1);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const bf16x8_t qf = *reinterpret_cast<const bf16x8_t*>(q_lane + qb * QBLK + 32 * kk);
+            n[qb][0] = mfma32(a0, qf, n[qb][0]);
+            n[qb][1] = mfma32(a1, qf, n[qb][1]);
+          }
         }
       }
     }
@@ -323,13 +362,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   };
 
   // Tiles below the whole workgroup's diagonal and inside Sk need no mask
-  // and have work for every wavefront: they run the branch-free main loop.
+  // and have work for every query block: they run the branch-free main loop.
   int n_main = a.Sk / kBc;
   if (a.causal) n_main = min(n_main, max(0, (q0 + off + 1) / kBc));
   n_main = min(n_main, n_kt);
 
   // ---- prologue: K(0), K(1), V(0) in LDS, then S(0).
-  f32x16_t sc0, sc1;
+  f32x16_t sc[QB][2];
   if (n_kt > 0) {
     load_k(0);
     load_v(0);
@@ -337,70 +376,97 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   }
   wait_loads();
   __syncthreads();  // Q, K(0), K(1), V(0) visible to every wavefront
-  if (n_kt > 0 && active(0)) qk(0, sc0, sc1);
+  if (n_kt > 0 && any_active(0)) qk(0, sc);
   __syncthreads();  // every wavefront has read K(0) before K(2) replaces it
 
+  bool all[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) all[qb] = true;
   int t = 0;
   for (; t < n_main; ++t) {
-    f32x16_t sn0, sn1;
+    f32x16_t sn[QB][2];
     prefetch(t);
-    update_max(sc0, sc1);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) update_max(qb, sc[qb][0], sc[qb][1]);
     // The next tile's scores are computed even past the last tile (from a
     // stale buffer, then discarded) to keep this block free of branches.
-    exp_pv_qk(t & 1, sc0, sc1, (t + 1) & 1, sn0, sn1);
-    sc0 = sn0;
-    sc1 = sn1;
+    exp_pv_qk(t & 1, sc, all, (t + 1) & 1, sn);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      sc[qb][0] = sn[qb][0];
+      sc[qb][1] = sn[qb][1];
+    }
     wait_loads();
     __syncthreads();
   }
   for (; t < n_kt; ++t) {
-    f32x16_t sn0, sn1;
+    f32x16_t sn[QB][2];
     prefetch(t);
-    const bool next = t + 1 < n_kt && active(t + 1);
-    if (active(t)) {
-      mask(t, sc0, sc1);
-      update_max(sc0, sc1);
-      exp_pv_qk(t & 1, sc0, sc1, next ? (t + 1) & 1 : -1, sn0, sn1);
-    } else if (next) {
-      qk((t + 1) & 1, sn0, sn1);
+    const bool next = t + 1 < n_kt && any_active(t + 1);
+    bool use[QB];
+    bool any = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      use[qb] = blk_active(t, qb);
+      any |= use[qb];
+      if (use[qb]) {
+        mask(t, qb, sc[qb][0], sc[qb][1]);
+        update_max(qb, sc[qb][0], sc[qb][1]);
+      }
     }
+    if (any)
+      exp_pv_qk(t & 1, sc, use, next ? (t + 1) & 1 : -1, sn);
+    else if (next)
+      qk((t + 1) & 1, sn);
     if (next) {
-      sc0 = sn0;
-      sc1 = sn1;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        sc[qb][0] = sn[qb][0];
+        sc[qb][1] = sn[qb][1];
+      }
     }
     wait_loads();
     __syncthreads();
   }
 
   // ---- epilogue: O = O^T / sum(bf16 p), LSE = (m + log2 sum(p)) ln 2
-  const float lrt = xor32_sum(lr);
-  const float let_ = xor32_sum(le);
-  if (qrow >= a.Sq) return;
-  const float inv = lrt > 0.f ? 1.f / lrt : 0.f;
-  uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + ((size_t)b * a.Hq + h) * (size_t)a.Sq * kD + (size_t)qrow * kD;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lrt = xor32_sum((lr[qb][0] + lr[qb][1]) + (lr[qb][2] + lr[qb][3]));
+    const float let_ = xor32_sum((le[qb][0] + le[qb][1]) + (le[qb][2] + le[qb][3]));
+    if (qrow[qb] >= a.Sq) continue;
+    const float inv = lrt > 0.f ? 1.f / lrt : 0.f;
+    uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + ((size_t)b * a.Hq + h) * (size_t)a.Sq * kD +
+                  (size_t)qrow[qb] * kD;
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const int d = 32 * db + 8 * gq + 4 * hi;
-      const uint2 w = make_uint2(pack_bf16x2(o[db][4 * gq] * inv, o[db][4 * gq + 1] * inv),
-                                 pack_bf16x2(o[db][4 * gq + 2] * inv, o[db][4 * gq + 3] * inv));
-      *reinterpret_cast<uint2*>(O + d) = w;
-    }
-  if (hi == 0)
-    a.lse[((size_t)b * a.Hq + h) * a.Sq + qrow] = let_ > 0.f ? (m + __log2f(let_)) * kLn2 : kNegInf;
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d = 32 * db + 8 * gq + 4 * hi;
+        const uint2 w = make_uint2(pack_bf16x2(o[qb][db][4 * gq] * inv, o[qb][db][4 * gq + 1] * inv),
+                                   pack_bf16x2(o[qb][db][4 * gq + 2] * inv, o[qb][db][4 * gq + 3] * inv));
+        *reinterpret_cast<uint2*>(O + d) = w;
+      }
+    if (hi == 0)
+      a.lse[((size_t)b * a.Hq + h) * a.Sq + qrow[qb]] = let_ > 0.f ? (m[qb] + __log2f(let_)) * kLn2 : kNegInf;
+  }
+}
+
+template <int NW, int QB>
+hipError_t launch_cfg(const PrefillArgs& a, hipStream_t s) {
+  constexpr int BR = 32 * NW * QB;
+  const int n_qtiles = (a.Sq + BR - 1) / BR;
+  const int nbh = a.B * a.Hq;
+  const long long blocks = (long long)n_qtiles * nbh;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((prefill_bf16_kernel<NW, QB>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a, n_qtiles, nbh);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
-  constexpr int kNW = 8;
-  const int n_qtiles = (a.Sq + 32 * kNW - 1) / (32 * kNW);
-  const int nbh = a.B * a.Hq;
-  const long long blocks = (long long)n_qtiles * nbh;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(prefill_bf16_kernel<kNW>, dim3((unsigned)blocks), dim3(64 * kNW), 0, s, a, n_qtiles, nbh);
-  return hipGetLastError();
+  return launch_cfg<8, 1>(a, s);
 }
 
 }  // namespace fa
