@@ -25,6 +25,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import statistics
 import sys
 import time
@@ -37,14 +38,21 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 
 
+def prefill_bytes(w):
+    """Algorithmic HBM bytes of one prefill launch: Q, K, V read and O written
+    once (bf16), the fp32 LSE written once."""
+    return 2 * w.B * w.S * w.D * (2 * w.Hq + 2 * w.Hkv) + 4 * w.B * w.Hq * w.S
+
+
 def prefill_flops(w):
     pairs = w.S * (w.S + 1) // 2
     return 4.0 * w.B * w.Hq * w.D * pairs
 
 
-def decode_bytes(kv, w):
+def decode_bytes(L, w):
+    """Algorithmic HBM bytes of one decode step for context lengths L."""
     import numpy as np
-    L = kv.seqlens.numpy().astype(np.int64)
+    L = np.asarray(L).astype(np.int64)
     pages = (L + 63) // 64
     eb = 1 if w.kv_dtype == "fp8" else 2
     b = int(L.sum()) * w.Hkv * w.D * 2 * eb          # K and V of the valid tokens
@@ -156,16 +164,174 @@ def cpu_baseline_decode(w, kv, budget_s=10.0):
                       f"fp64 numpy, BLAS 1 thread per worker"}
 
 
+COPY_BYTES = 1 << 30   # calibration copy: bytes read, and bytes written, per launch
+
+
+def copy_calibration(steps, warmup):
+    """A plain device copy of COPY_BYTES (every byte read once and written
+    once, y = -x on bf16): the known-size kernel that calibrates the HBM byte
+    counters of the attention kernels."""
+    import torch
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    t = time_calls(lambda: torch.neg(src, out=dst), steps, warmup, stream)
+    ms = statistics.mean(t)
+    print(json.dumps({"metric": "plain copy HBM GB/s (counter calibration)", "unit": "GB/s",
+                      "value": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1), "ms_mean": round(ms, 5),
+                      "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES, "steps": steps}), flush=True)
+
+
+# ---- Turning rocprofv3 output into the text summaries kept under profiles/.
+# Expected layout under DIR (each a rocprofv3 ``-d`` directory, ``-o pmc`` or
+# ``-o kt``), made by the commands that PROFILE_COMMANDS lists:
+#   DIR/kt                      --kernel-trace --stats of the default bench run
+#   DIR/pmc_<leg>_<COUNTER>     --pmc COUNTER of one leg, COUNTER in FETCH_SIZE, WRITE_SIZE
+PMC_LEGS = {
+    "prefill_bf16_wl2": ("--only prefill --prefill-workload 2", ["prefill_bf16_kernel"],
+                         "exact_attention_20_amd/csrc/prefill_bf16.hip"),
+    "prefill_bf16_wl3": ("--only prefill --prefill-workload 3", ["prefill_bf16_kernel"],
+                         "exact_attention_20_amd/csrc/prefill_bf16.hip"),
+    "decode_wl4": ("--only decode --decode-workload 4", ["decode_split_kernel", "lse_merge_kernel"],
+                   "exact_attention_20_amd/csrc/decode.hip"),
+    "decode_wl5": ("--only decode --decode-workload 5", ["decode_split_kernel", "lse_merge_kernel"],
+                   "exact_attention_20_amd/csrc/decode.hip"),
+    "copy": ("--only copy", ["neg"], None),
+}
+PMC_RUN = "--steps 3 --warmup 1 --no-cpu-baseline"
+
+
+def profile_commands(d):
+    cmds = [f"rocprofv3 --kernel-trace --stats -f csv -d {d}/kt -o kt -- python3 bench.py > {d}/kt_bench.json"]
+    for leg, (flags, _, _) in PMC_LEGS.items():
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            cmds.append(f"rocprofv3 --pmc {c} -f csv -d {d}/pmc_{leg}_{c} -o pmc -- python3 bench.py {flags} {PMC_RUN}")
+    return cmds
+
+
+def _pmc_means(path, names):
+    """Mean per dispatch of the counter in one rocprofv3 --pmc csv, summed over
+    the kernels whose name contains one of ``names``; (mean KiB, dispatches)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(path, "*counter_collection.csv"))
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {path}")
+    per_disp = {}
+    kname = {}
+    for r in csv.DictReader(open(files[0])):
+        key = r["Dispatch_Id"]
+        per_disp[key] = per_disp.get(key, 0.0) + float(r["Counter_Value"])
+        kname[key] = r["Kernel_Name"]
+    total, counts = 0.0, []
+    for n in names:
+        vals = [v for k, v in per_disp.items() if n in kname[k]]
+        if not vals:
+            raise ValueError(f"no dispatch of a kernel named *{n}* in {files[0]}: "
+                             f"{sorted(set(kname.values()))}")
+        total += statistics.mean(vals)
+        counts.append(len(vals))
+    return total, min(counts)
+
+
+def summarize_profiles(d):
+    """Write profiles/<leg>_traffic.txt for every counter leg found under d,
+    and profiles/kernel_trace_bench.txt from the kernel trace."""
+    import csv
+    import glob
+    import workloads
+    out_dir = os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    cmds = profile_commands(d)
+    header = ["# Commands, run from the repository root on one MI355X (TMPDIR=/tmp):"]
+    header += [f"#   {c}" for c in cmds]
+    header += [f"#   python3 bench.py --summarize-profiles {d}"]
+    written = []
+    copy_f, _ = _pmc_means(f"{d}/pmc_copy_FETCH_SIZE", PMC_LEGS["copy"][1])
+    copy_w, _ = _pmc_means(f"{d}/pmc_copy_WRITE_SIZE", PMC_LEGS["copy"][1])
+    f_scale = COPY_BYTES / (copy_f * 1024.0)
+    w_scale = COPY_BYTES / (copy_w * 1024.0)
+    for leg, (flags, names, src) in PMC_LEGS.items():
+        if src is None or not os.path.isdir(f"{d}/pmc_{leg}_FETCH_SIZE"):
+            continue
+        fk, n = _pmc_means(f"{d}/pmc_{leg}_FETCH_SIZE", names)
+        wk, _ = _pmc_means(f"{d}/pmc_{leg}_WRITE_SIZE", names)
+        wid = int(leg.rsplit("wl", 1)[1])
+        w = workloads.WORKLOADS[wid]
+        if leg.startswith("prefill"):
+            alg = prefill_bytes(w)
+        else:
+            alg = decode_bytes(workloads.context_lengths(wid, w.B, w.lengths), w)
+        fb, wb = fk * 1024.0 * f_scale, wk * 1024.0 * w_scale
+        lines = [f"# HBM traffic per launch of {' + '.join(names)} on workload {wid} ({w.name}),",
+                 "# from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch, one pass each), scaled by",
+                 f"# what the same counters read for a plain {COPY_BYTES} B copy (torch.neg on bf16).",
+                 *header,
+                 f"source: {src}",
+                 f"source_sha256_16: {source_sha(src)}",
+                 f"dispatches_per_kernel: {n}",
+                 f"fetch_kib_raw: {fk:.1f}",
+                 f"write_kib_raw: {wk:.1f}",
+                 f"copy_fetch_kib_raw: {copy_f:.1f}",
+                 f"copy_write_kib_raw: {copy_w:.1f}",
+                 f"fetch_scale: {f_scale:.4f}",
+                 f"write_scale: {w_scale:.4f}",
+                 f"fetch_bytes_per_launch: {fb:.0f}",
+                 f"write_bytes_per_launch: {wb:.0f}",
+                 f"algorithmic_bytes_per_launch: {alg}",
+                 f"traffic_over_algorithmic: {(fb + wb) / alg:.3f}"]
+        path = os.path.join(out_dir, f"{leg}_traffic.txt")
+        open(path, "w").write("\n".join(lines) + "\n")
+        written.append(path)
+    kt = glob.glob(f"{d}/kt/*kernel_stats.csv")
+    if kt:
+        rows = list(csv.DictReader(open(kt[0])))
+        lines = ["# rocprofv3 --kernel-trace --stats of the default bench run (one process, both legs).",
+                 *header[:2], f"#   python3 bench.py --summarize-profiles {d}",
+                 "# kernel | calls | average us | min us | max us | total ms | % of GPU time"]
+        for r in rows:
+            name = r["Name"]
+            m = re.search(r"::(\w+(?:<[^>]*>)?)\(", name)   # "void fa::(anon)::NAME<...>(args)"
+            short = m.group(1) if m else name[:70]
+            lines.append(f"{short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                         f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f}")
+        bj = f"{d}/kt_bench.json"
+        if os.path.exists(bj):
+            txt = [x for x in open(bj).read().splitlines() if x.startswith("{")]
+            if txt:
+                b = json.loads(txt[-1])
+                lines.append("# the same run's bench line, HIP-event means per launch:")
+                lines.append(f"bench prefill launch_ms_mean: {b['roofline'].get('launch_ms_mean')}")
+                if "decode" in b:
+                    lines.append(f"bench decode step ms_mean: {b['decode'].get('ms_mean')}")
+                lines.append(f"bench value: {b['value']} {b['unit']}")
+        path = os.path.join(out_dir, "kernel_trace_bench.txt")
+        open(path, "w").write("\n".join(lines) + "\n")
+        written.append(path)
+    for p in written:
+        print("wrote", os.path.relpath(p, ROOT))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None)
     ap.add_argument("--prefill-workload", type=int, default=2, choices=[2, 3])
     ap.add_argument("--decode-workload", type=int, default=4, choices=[4, 5])
+    ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
+                    help="write profiles/*.txt from rocprofv3 output under DIR (no GPU needed)")
+    ap.add_argument("--print-profile-commands", metavar="DIR", default=None)
     args = ap.parse_args()
+    if args.print_profile_commands:
+        print("\n".join(profile_commands(args.print_profile_commands)))
+        return
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(the way it would shard is described in DESIGN.md).", file=sys.stderr)
@@ -182,6 +348,10 @@ def main():
     fa.load()
     stream = torch.cuda.current_stream()
     log = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
+
+    if args.only == "copy":
+        copy_calibration(args.steps, args.warmup)
+        return
 
     res = {}
     wp = workloads.WORKLOADS[args.prefill_workload]
@@ -228,7 +398,7 @@ def main():
 
         t = time_calls(dec, args.steps, args.warmup, stream)
         res["decode_ms"] = t
-        res["decode_bytes"] = decode_bytes(kv, wd)
+        res["decode_bytes"] = decode_bytes(kv.seqlens.numpy(), wd)
         res["decode_plan"] = dict(plan_ms=round(plan_ms, 3), items=int(len(items)), chunk_pages=chunk,
                                   num_splits=plan.num_splits, pages=int(kv.num_pages),
                                   pool_copies_rotated=n_copies)
