@@ -33,6 +33,9 @@ namespace {
 
 constexpr int kD = 128;
 constexpr float kTau = 8.0f;  // lazy max threshold, log2 units (p <= 2^kTau)
+// Page buffers per wavefront (pages in flight + 1), by KV element type.
+constexpr int kRingBf16 = 3;
+constexpr int kRingFp8 = 2;
 
 template <bool FP8>
 struct KvSlot;
@@ -45,12 +48,18 @@ struct KvSlot<true> {  // 8 fp8 codes
   uint2 v;
 };
 
+// KV bytes are read exactly once per step, so the loads are nontemporal
+// (cache policy nt): they stream past the caches instead of evicting lines
+// that are reused. The resource covers one (page, KV head) block.
 template <bool FP8>
-__device__ __forceinline__ void load_slot(KvSlot<FP8>& s, const char* base, size_t off_elems) {
+__device__ __forceinline__ void load_slot(KvSlot<FP8>& s, __amdgpu_buffer_rsrc_t r, int byte_off) {
+  constexpr int kNT = 2;
   if constexpr (FP8) {
-    s.v = *reinterpret_cast<const uint2*>(base + off_elems);
+    const u32x2_t t = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, kNT);
+    s.v = make_uint2(t.x, t.y);
   } else {
-    s.v = *reinterpret_cast<const uint4*>(base + 2 * off_elems);
+    const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kNT);
+    s.v = make_uint4(t.x, t.y, t.z, t.w);
   }
 }
 
@@ -109,7 +118,16 @@ __device__ __forceinline__ void token_pairs(const KvSlot<FP8>& a, const KvSlot<F
   }
 }
 
-template <int G, bool FP8>
+// One page of one KV head as this lane holds it, with its page id and the
+// score / probability multipliers (the fp8 scales folded in).
+template <bool FP8>
+struct PageBuf {
+  KvSlot<FP8> k[4], v[4];
+  int pid;
+  float c, vsc;
+};
+
+template <int G, bool FP8, int NB>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   constexpr int kElem = FP8 ? 1 : 2;
   const WorkItem it = a.items[blockIdx.x];
@@ -141,104 +159,128 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
   }
 
-  const size_t page_elems = (size_t)64 * kD;            // one (page, head) block
-  const size_t head_stride = page_elems;                // between heads of a page
-  const size_t pid_stride = (size_t)a.Hkv * page_elems; // between pages
+  const int blk_bytes = 64 * kD * kElem;  // one (page, KV head) block
   const char* kpool = reinterpret_cast<const char*>(a.k_pages);
   const char* vpool = reinterpret_cast<const char*>(a.v_pages);
   const int32_t* table = a.page_table + (size_t)b * a.stride;
-  // Element offset of this lane's slot i inside a (page, head) block.
-  const int lane_off = (wave * 16 + row) * kD + dc * 8;
+  // Byte offset of this lane's slot i inside a block: token wave*16 + 4i + row,
+  // dims dc*8 .. dc*8+7.
+  int slot_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) slot_off[i] = ((wave * 16 + 4 * i + row) * kD + dc * 8) * kElem;
 
-  auto page_base = [&](int pid) -> size_t { return (size_t)pid * pid_stride + (size_t)g * head_stride; };
+  // Page ids of the item, 64 pages per window: lane i holds the id of page
+  // w0 + i (and for fp8 that page's K and V scales), read with one vector
+  // load each, so no page waits on a dependent page-table or scale load.
+  int w0 = p0;
+  int tbl = -1;
+  float kscl = 0.f, vscl = 0.f;
+  auto load_window = [&]() {
+    const int pp = w0 + lane;
+    tbl = pp < p1 ? table[pp] : -1;
+    if constexpr (FP8) {
+      const bool ok = (unsigned)tbl < (unsigned)a.num_pages;
+      kscl = ok ? a.k_scale[(size_t)tbl * a.Hkv + g] : 0.f;
+      vscl = ok ? a.v_scale[(size_t)tbl * a.Hkv + g] : 0.f;
+    }
+  };
+  load_window();
 
-  KvSlot<FP8> kc[4], vc[4];
-  int pid_c = 0;
-  {
-    int pid = table[p0];
-    pid_c = pid;
-    const size_t base = page_base(((unsigned)pid < (unsigned)a.num_pages) ? pid : 0);
+  // Ring of NB page buffers: page p lives in buf[(p - p0) % NB], and its
+  // loads are issued NB-1 pages ahead of its use, so each wavefront keeps
+  // NB-1 pages of K and V in flight while it computes on the current one.
+  // The page's block address is wave-uniform (scalar registers), so the
+  // per-page address work is scalar and the lane offsets are fixed.
+  PageBuf<FP8> buf[NB];
+  auto issue = [&](PageBuf<FP8>& d, int p) {
+    if (p - w0 == 64) {
+      w0 += 64;
+      load_window();
+    }
+    const int pid = __builtin_amdgcn_readlane(tbl, p - w0);
+    d.pid = pid;
+    if constexpr (FP8) {
+      d.c = c_base * __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, kscl), p - w0));
+      d.vsc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, vscl), p - w0));
+    } else {
+      d.c = c_base;
+      d.vsc = 1.f;
+    }
+    // The block offset is uniform; readfirstlane makes that visible to the
+    // compiler, which otherwise wraps each buffer load in a waterfall loop.
+    const size_t off_v = ((size_t)(((unsigned)pid < (unsigned)a.num_pages) ? pid : 0) * a.Hkv + g) * blk_bytes;
+    const size_t off = ((size_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(off_v >> 32)) << 32) |
+                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)off_v);
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kpool + off), (short)0, blk_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vpool + off), (short)0, blk_bytes, 0x00020000);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      load_slot<FP8>(kc[i], kpool, base + lane_off + i * 4 * kD);
-      load_slot<FP8>(vc[i], vpool, base + lane_off + i * 4 * kD);
+      load_slot<FP8>(d.k[i], rk, slot_off[i]);
+      load_slot<FP8>(d.v[i], rv, slot_off[i]);
     }
-  }
+  };
 
-  for (int p = p0; p < p1; ++p) {
-    KvSlot<FP8> kn[4], vn[4];
-    int pid_n = 0;
-    if (p + 1 < p1) {
-      pid_n = table[p + 1];
-      const size_t base = page_base(((unsigned)pid_n < (unsigned)a.num_pages) ? pid_n : 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        load_slot<FP8>(kn[i], kpool, base + lane_off + i * 4 * kD);
-        load_slot<FP8>(vn[i], vpool, base + lane_off + i * 4 * kD);
-      }
-    }
-
-    // Tokens of this page that belong to the request (all 64 except on the
-    // last page); an out-of-range page id contributes nothing.
-    int nvalid = min(64, L - p * 64);
-    if ((unsigned)pid_c >= (unsigned)a.num_pages) nvalid = 0;
-    float c = c_base;
-    float vsc = 1.f;
-    if constexpr (FP8) {
-      if (nvalid > 0) {
-        c = c_base * a.k_scale[(size_t)pid_c * a.Hkv + g];
-        vsc = a.v_scale[(size_t)pid_c * a.Hkv + g];
-      }
-    }
+  auto consume = [&](PageBuf<FP8>& cur, int p) {
+    // Tokens of this page that belong to the request: all 64 except on the
+    // request's last page; an out-of-range page id contributes nothing. Only
+    // such a partial page takes the masking path (a wave-uniform branch).
+    const int nvalid = ((unsigned)cur.pid < (unsigned)a.num_pages) ? min(64, L - p * 64) : 0;
     const bool partial = nvalid < 64;
     bool tok_ok[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tok_ok[i] = (wave * 16 + 4 * i + row) < nvalid;
-      if (partial && !tok_ok[i]) {  // tail slots may hold anything (NaN): never use them
-        zero_slot<FP8>(kc[i]);
-        zero_slot<FP8>(vc[i]);
-      }
+    for (int i = 0; i < 4; ++i) tok_ok[i] = (wave * 16 + 4 * i + row) < nvalid;
+    if (partial) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!tok_ok[i]) {  // tail slots may hold anything (NaN): never use them
+          zero_slot<FP8>(cur.k[i]);
+          zero_slot<FP8>(cur.v[i]);
+        }
     }
 
-    // Scores s[i][h] (log2 units) for this lane's 4 tokens.
+    // Raw dot products q.k for this lane's 4 tokens, summed over the 16 lanes
+    // that share a token.
     float s[4][G];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint32_t kp[4];
-      slot_pairs<FP8>(kc[i], kp);
+      slot_pairs<FP8>(cur.k[i], kp);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float d = dot2_bf16(qd[h][0], kp[0], 0.f);
         d = dot2_bf16(qd[h][1], kp[1], d);
         d = dot2_bf16(qd[h][2], kp[2], d);
         d = dot2_bf16(qd[h][3], kp[3], d);
-        s[i][h] = d;
+        s[i][h] = row16_sum(d);
       }
     }
+    if (partial) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float d = row16_sum(s[i][h]) * c;
-        s[i][h] = tok_ok[i] ? d : kNegInf;
-      }
+        for (int h = 0; h < G; ++h) s[i][h] = tok_ok[i] ? s[i][h] : kNegInf;
+    }
 
-    // Lazy running max: move it only when some score exceeds it by > kTau.
+    // Lazy running max in log2 units: the score is c*s with c >= 0, so the
+    // tile max is c * max(s). It moves only when some score exceeds it by
+    // more than kTau; after the first full page it is finite.
+    const float c = cur.c;
     bool need = false;
     float smax[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       smax[h] = fmaxf(fmaxf(s[0][h], s[1][h]), fmaxf(s[2][h], s[3][h]));
-      need |= smax[h] > m[h] + kTau;
+      need |= smax[h] * c > m[h] + kTau;
     }
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float x = fmaxf(smax[h], shfl_xor_f32(smax[h], 16));
         x = fmaxf(x, shfl_xor_f32(x, 32));
-        const float mn = fmaxf(m[h], x);
-        const float alpha = (mn == kNegInf) ? 1.f : fast_exp2(m[h] - mn);
+        const float mn = fmaxf(m[h], x * c);
+        const float alpha = fast_exp2(m[h] - mn);  // 0 when m was -inf
         l[h] *= alpha;
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[h][j] *= alpha;
@@ -246,20 +288,36 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       }
     }
 
+    // p = 2^(c*s - m); the fp8 V scale is folded into the weights that
+    // multiply V, not into the normaliser.
+    float e[4][G];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[i][h] = fast_exp2(__builtin_fmaf(s[i][h], c, -m[h]));
+    if (partial) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < G; ++h) e[i][h] = tok_ok[i] ? e[i][h] : 0.f;
+    }
     uint32_t pp01[G], pp23[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mu = (m[h] == kNegInf) ? 0.f : m[h];
-      const float e0 = fast_exp2(s[0][h] - mu), e1 = fast_exp2(s[1][h] - mu);
-      const float e2 = fast_exp2(s[2][h] - mu), e3 = fast_exp2(s[3][h] - mu);
-      l[h] += (e0 + e1) + (e2 + e3);
-      pp01[h] = pack_bf16x2(e0 * vsc, e1 * vsc);
-      pp23[h] = pack_bf16x2(e2 * vsc, e3 * vsc);
+      l[h] += (e[0][h] + e[1][h]) + (e[2][h] + e[3][h]);
+      if constexpr (FP8) {
+        const float vsc = cur.vsc;
+        pp01[h] = pack_bf16x2(e[0][h] * vsc, e[1][h] * vsc);
+        pp23[h] = pack_bf16x2(e[2][h] * vsc, e[3][h] * vsc);
+      } else {
+        pp01[h] = pack_bf16x2(e[0][h], e[1][h]);
+        pp23[h] = pack_bf16x2(e[2][h], e[3][h]);
+      }
     }
 
     uint32_t v01[8], v23[8];
-    token_pairs<FP8>(vc[0], vc[1], v01);
-    token_pairs<FP8>(vc[2], vc[3], v23);
+    token_pairs<FP8>(cur.v[0], cur.v[1], v01);
+    token_pairs<FP8>(cur.v[2], cur.v[3], v23);
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -267,14 +325,19 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         acc[h][j] = dot2_bf16(pp01[h], v01[j], acc[h][j]);
         acc[h][j] = dot2_bf16(pp23[h], v23[j], acc[h][j]);
       }
+  };
 
-    if (p + 1 < p1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        kc[i] = kn[i];
-        vc[i] = vn[i];
+  for (int j = 0; j < NB - 1; ++j)
+    if (p0 + j < p1) issue(buf[j], p0 + j);
+  // Unrolled by NB so that every buffer index is a compile-time constant.
+  for (int p = p0; p < p1; p += NB) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (p + j < p1) {
+        if (p + j + NB - 1 < p1) issue(buf[(j + NB - 1) % NB], p + j + NB - 1);
+        consume(buf[j], p + j);
       }
-      pid_c = pid_n;
     }
   }
 
@@ -327,31 +390,66 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// One wavefront per (request, query head): merge that request's splits by
-// their LSE into the bf16 output and the fp32 LSE.
+// One workgroup of 4 wavefronts per (request, query head) merges that
+// request's splits by their LSE into the bf16 output and the fp32 LSE:
+// L* = M + ln sum_s exp(lse_s - M), O = sum_s exp(lse_s - L*) O_s, where M is
+// the largest partial LSE. Each wavefront takes a contiguous quarter of the
+// splits and streams it 8 splits at a time (8 independent 512-byte loads in
+// flight); the quarters are combined through LDS. An empty split has
+// lse_s = -inf and weight 0; a request with no token gets O = 0, LSE = -inf.
 __global__ __launch_bounds__(256) void lse_merge_kernel(DecodeArgs a) {
+  const int bh = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int bh = blockIdx.x * 4 + wave;
-  if (bh >= a.B * a.Hq) return;
   const int b = bh / a.Hq;
   const int n = a.splits_per_req[b];
   const float* plse = a.part_lse + (size_t)bh * a.num_splits;
   const float* po = a.part_o + (size_t)bh * a.num_splits * kD;
+  __shared__ float s_max[4], s_tot[4];
+  __shared__ float2 s_o[4][kD / 2];
+
   float M = kNegInf;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, plse[s]);
+  for (int i = threadIdx.x; i < n; i += 256) M = fmaxf(M, plse[i]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, shfl_xor_f32(M, o));
+  if (lane == 0) s_max[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+
+  const int per = (n + 3) / 4;
+  const int s0 = min(n, wave * per), s1 = min(n, s0 + per);
   float tot = 0.f, o0 = 0.f, o1 = 0.f;
   if (M != kNegInf) {
-    for (int s = 0; s < n; ++s) {
-      const float w = fast_exp2((plse[s] - M) * kLog2e);
-      const float2 x = *reinterpret_cast<const float2*>(po + (size_t)s * kD + 2 * lane);
-      tot += w;
-      o0 += w * x.x;
-      o1 += w * x.y;
+    for (int i = s0; i < s1; i += 8) {
+      float w[8];
+      float2 x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool ok = i + j < s1;
+        const int sj = ok ? i + j : s0;  // past the range: a real split with weight 0
+        w[j] = ok ? plse[sj] : kNegInf;
+        x[j] = *reinterpret_cast<const float2*>(po + (size_t)sj * kD + 2 * lane);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float wj = fast_exp2((w[j] - M) * kLog2e);
+        tot += wj;
+        o0 += wj * x[j].x;
+        o1 += wj * x[j].y;
+      }
     }
   }
-  const float inv = tot > 0.f ? 1.f / tot : 0.f;
-  reinterpret_cast<uint32_t*>(a.out)[(size_t)bh * (kD / 2) + lane] = pack_bf16x2(o0 * inv, o1 * inv);
-  if (lane == 0) a.lse[bh] = tot > 0.f ? M + __logf(tot) : kNegInf;
+  s_o[wave][lane] = make_float2(o0, o1);
+  if (lane == 0) s_tot[wave] = tot;
+  __syncthreads();
+  if (wave == 0) {
+    const float T = (s_tot[0] + s_tot[1]) + (s_tot[2] + s_tot[3]);
+    const float2 a0 = s_o[0][lane], a1 = s_o[1][lane], a2 = s_o[2][lane], a3 = s_o[3][lane];
+    const float inv = T > 0.f ? 1.f / T : 0.f;
+    const float r0 = ((a0.x + a1.x) + (a2.x + a3.x)) * inv;
+    const float r1 = ((a0.y + a1.y) + (a2.y + a3.y)) * inv;
+    reinterpret_cast<uint32_t*>(a.out)[(size_t)bh * (kD / 2) + lane] = pack_bf16x2(r0, r1);
+    if (lane == 0) a.lse[bh] = T > 0.f ? M + __logf(T) : kNegInf;
+  }
 }
 
 // dst[t, :] = pool[page_table[b, t / 64], g, t % 64, :] for t < L.
@@ -373,9 +471,9 @@ __global__ void gather_kv_kernel(const char* pages, int elem_bytes, const int32_
 template <int G>
 hipError_t launch_split_g(const DecodeArgs& a, int fp8, hipStream_t s) {
   if (fp8)
-    hipLaunchKernelGGL((decode_split_kernel<G, true>), dim3(a.n_items), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_split_kernel<G, true, kRingFp8>), dim3(a.n_items), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_split_kernel<G, false>), dim3(a.n_items), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_split_kernel<G, false, kRingBf16>), dim3(a.n_items), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -392,8 +490,7 @@ hipError_t launch_decode_split(const DecodeArgs& a, int group, int fp8, hipStrea
 }
 
 hipError_t launch_lse_merge(const DecodeArgs& a, hipStream_t s) {
-  const int rows = a.B * a.Hq;
-  hipLaunchKernelGGL(lse_merge_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(lse_merge_kernel, dim3(a.B * a.Hq), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
