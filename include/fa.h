@@ -179,7 +179,9 @@ int fa_decode_plan_host(const int32_t* seqlens_host, int B, int max_pages_per_re
  *   k_pages    [P, Hkv, 64, D] bf16, or uint8 e4m3fn codes (per plan dtype)
  *   v_pages    same as k_pages
  *   k_scale    fp32 [P, Hkv] dequantisation scale per page and KV head
- *              (value = code * scale); required for fp8, ignored for bf16
+ *              (value = code * scale); required for fp8, ignored for bf16.
+ *              Scales must be finite and >= 0 (a quantiser's max|x|/448 is);
+ *              negative scales give undefined results.
  *   v_scale    same for V
  *   page_table int32 [B, max_pages_per_req] (device copy of the plan's table)
  *   seqlens    int32 [B] device copy of the lengths given to the plan (the
