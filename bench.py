@@ -1,6 +1,6 @@
 """Benchmark of the exact-attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--prewarm-s S] [--no-cpu-baseline]
                     [--only prefill|decode] [--prefill-workload 2|3] [--decode-workload 4|5]
 
 One step = one pass of the whole path over one synthetic batch:
@@ -9,8 +9,10 @@ One step = one pass of the whole path over one synthetic batch:
   * decode: fa_decode_run (split-KV kernel + LSE merge) on the paged bf16
     workload (default: 64 requests, 32/8 heads, lengths U[512, 16384]),
     planned once beforehand (the host plan is timed separately and reported).
-Inputs are resident in HBM before timing. Each kernel call is bracketed by
-HIP events on the stream it runs on; the step time is their sum.
+Inputs are resident in HBM before timing. Each leg first runs untimed for
+--prewarm-s seconds (default 1 s: GPU clocks and power reach steady state)
+and --warmup more times; each timed call is then bracketed by HIP events on
+the stream it runs on, and the step time is the sum of the legs' means.
 
 Prints ONE JSON line. ``value`` is the prefill throughput in TFLOP/s
 (algorithmic FLOPs 4*B*H*D*S(S+1)/2 over the measured time); the ``decode``
@@ -88,8 +90,17 @@ def read_traffic(name, src_rel):
         return None
 
 
-def time_calls(fn, steps, warmup, stream):
+def time_calls(fn, steps, warmup, stream, prewarm_s=0.0):
+    """HIP-event time (ms) of each of `steps` calls of fn on `stream`, after
+    running fn for at least `prewarm_s` seconds (GPU clocks and power reach
+    their steady state; an idle GPU runs the first ~0.1 s of work up to 15%
+    slower) and then `warmup` more untimed calls."""
     import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < prewarm_s:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -175,7 +186,7 @@ def copy_calibration(steps, warmup):
     src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
     dst = torch.empty_like(src)
     stream = torch.cuda.current_stream()
-    t = time_calls(lambda: torch.neg(src, out=dst), steps, warmup, stream)
+    t = time_calls(lambda: torch.neg(src, out=dst), steps, warmup, stream, 0.5)
     ms = statistics.mean(t)
     print(json.dumps({"metric": "plain copy HBM GB/s (counter calibration)", "unit": "GB/s",
                       "value": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1), "ms_mean": round(ms, 5),
@@ -318,6 +329,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--prewarm-s", type=float, default=1.0,
+                    help="seconds of untimed steps before the warmup steps (GPU clock ramp-up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None)
     ap.add_argument("--prefill-workload", type=int, default=2, choices=[2, 3])
@@ -364,7 +377,7 @@ def main():
         out = torch.empty_like(qd)
         lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=qd.device)
         pf = lambda: fa.fa_prefill_fwd(qd, kd, vd, out, lse, True, wp.scale, None, stream)  # noqa: E731
-        t = time_calls(pf, args.steps, args.warmup, stream)
+        t = time_calls(pf, args.steps, args.warmup, stream, args.prewarm_s)
         res["prefill_ms"] = t
         log(f"[bench] prefill median {statistics.median(t):.4f} ms min {min(t):.4f} ms")
         res["prefill_cpu"] = None if args.no_cpu_baseline else cpu_baseline_prefill(wp, q, k, v)
@@ -396,7 +409,7 @@ def main():
             fa.fa_decode_run(plan, d["q"], kk, vv, d["pt"], d["sl"], plan.num_splits, out, lse,
                              d["ks"], d["vs"], wd.scale, stream)
 
-        t = time_calls(dec, args.steps, args.warmup, stream)
+        t = time_calls(dec, args.steps, args.warmup, stream, args.prewarm_s)
         res["decode_ms"] = t
         res["decode_bytes"] = decode_bytes(kv.seqlens.numpy(), wd)
         res["decode_plan"] = dict(plan_ms=round(plan_ms, 3), items=int(len(items)), chunk_pages=chunk,
