@@ -113,8 +113,8 @@ static int check_decode_shape(int B, int Hq, int Hkv, int D) {
     return fail(FA_ERR_UNSUPPORTED, "decode: Hq and Hkv must be <= %d", fa::kMaxHeads);
   if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARGUMENT, "decode: Hq %% Hkv != 0 (%d, %d)", Hq, Hkv);
   int G = Hq / Hkv;
-  if (G != 1 && G != 2 && G != 4 && G != 8)
-    return fail(FA_ERR_UNSUPPORTED, "decode: group size Hq/Hkv=%d not in {1,2,4,8}", G);
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(FA_ERR_UNSUPPORTED, "decode: group size Hq/Hkv=%d not in {1,2,4,8,16}", G);
   if (D != 128) return fail(FA_ERR_UNSUPPORTED, "decode: D=%d not supported (128)", D);
   return FA_OK;
 }

@@ -24,6 +24,7 @@
 // O/l rescale disappears from the steady state. fp8 (OCP e4m3fn) pages are
 // converted to bf16 pairs with the gfx950 scaled convert (exact), the K scale
 // is folded into the score multiplier and the V scale into p.
+#include "decode_common.h"
 #include "fa_internal.h"
 #include "hip_common.h"
 
@@ -353,41 +354,25 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       acc[h][j] += shfl_xor_f32(acc[h][j], 32);
     }
   }
-  __shared__ float s_acc[4][G][kD];
-  __shared__ float s_m[4][G], s_l[4][G];
+  __shared__ float s_o[4 * G * kD];
+  __shared__ float s_m[64], s_l[64];
   if (row == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      *reinterpret_cast<float4*>(&s_acc[wave][h][dc * 8]) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-      *reinterpret_cast<float4*>(&s_acc[wave][h][dc * 8 + 4]) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+      *reinterpret_cast<float4*>(&s_o[(wave * G + h) * kD + dc * 8]) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      *reinterpret_cast<float4*>(&s_o[(wave * G + h) * kD + dc * 8 + 4]) =
+          make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
     }
     if (dc == 0) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        s_m[wave][h] = m[h];
-        s_l[wave][h] = l[h];
+        s_m[16 * wave + h] = m[h];
+        s_l[16 * wave + h] = l[h];
       }
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < G * kD; idx += 256) {
-    const int h = idx / kD, d = idx % kD;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][h]);
-    float Lsum = 0.f, o = 0.f;
-    if (M != kNegInf) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float f = fast_exp2(s_m[w][h] - M);
-        Lsum += s_l[w][h] * f;
-        o += s_acc[w][h][d] * f;
-      }
-    }
-    const size_t slot = ((size_t)b * a.Hq + g * G + h) * a.num_splits + split;
-    a.part_o[slot * kD + d] = Lsum > 0.f ? o / Lsum : 0.f;
-    if (d == 0) a.part_lse[slot] = Lsum > 0.f ? (M + __log2f(Lsum)) * kLn2 : kNegInf;
-  }
+  finish_work_item<G>(a, b, g, split, s_m, s_l, s_o);
 }
 
 // One workgroup of 4 wavefronts per (request, query head) merges that
@@ -397,11 +382,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 // splits and streams it 8 splits at a time (8 independent 512-byte loads in
 // flight); the quarters are combined through LDS. An empty split has
 // lse_s = -inf and weight 0; a request with no token gets O = 0, LSE = -inf.
+// A request with a single split was written by its work item.
 __global__ __launch_bounds__(256) void lse_merge_kernel(DecodeArgs a) {
   const int bh = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int b = bh / a.Hq;
   const int n = a.splits_per_req[b];
+  if (n == 1) return;  // uniform across the workgroup
   const float* plse = a.part_lse + (size_t)bh * a.num_splits;
   const float* po = a.part_o + (size_t)bh * a.num_splits * kD;
   __shared__ float s_max[4], s_tot[4];
@@ -479,12 +466,16 @@ hipError_t launch_split_g(const DecodeArgs& a, int fp8, hipStream_t s) {
 
 }  // namespace
 
+// One or two query heads per KV head make each page a matrix-vector product:
+// the vector-ALU kernel here. Larger groups are small dense contractions and
+// run on the matrix cores (decode_mfma.hip).
 hipError_t launch_decode_split(const DecodeArgs& a, int group, int fp8, hipStream_t s) {
   switch (group) {
     case 1: return launch_split_g<1>(a, fp8, s);
     case 2: return launch_split_g<2>(a, fp8, s);
-    case 4: return launch_split_g<4>(a, fp8, s);
-    case 8: return launch_split_g<8>(a, fp8, s);
+    case 4:
+    case 8:
+    case 16: return launch_decode_split_mfma(a, group, fp8, s);
     default: return hipErrorInvalidValue;
   }
 }

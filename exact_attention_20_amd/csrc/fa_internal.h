@@ -61,6 +61,8 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode_split(const DecodeArgs& a, int group, int fp8, hipStream_t s);
+// Split kernel on MFMA for groups of 4, 8 or 16 query heads per KV head.
+hipError_t launch_decode_split_mfma(const DecodeArgs& a, int group, int fp8, hipStream_t s);
 hipError_t launch_lse_merge(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_gather_kv(const void* pages, int elem_bytes, const int32_t* page_table,
                             int stride, int num_pages, int Hkv, int D, int b, int L, int g,

@@ -10,6 +10,8 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstdlib>
+#include <functional>
+#include <queue>
 #include <vector>
 
 #include "fa_internal.h"
@@ -18,20 +20,83 @@ namespace fa {
 
 namespace {
 
-// Work items per CU the auto mode aims for. Several resident workgroups per
-// CU and a few rounds of them keep the tail of near-equal items short.
-int items_per_cu() {
-  static int v = [] {
-    const char* e = std::getenv("FA_DECODE_ITEMS_PER_CU");
-    int x = e ? std::atoi(e) : 0;
-    return x > 0 ? x : 12;
-  }();
-  return v;
-}
-
 // Smallest chunk in pages: below this the per-item fixed cost (query load,
 // epilogue merge, partial write) stops being small next to the page traffic.
 constexpr int kMinChunkPages = 4;
+
+// Split-kernel workgroups resident on one CU at a time (the register and LDS
+// use of the split kernels allows two), i.e. work items processed in parallel
+// per CU.
+constexpr int kResidentPerCU = 2;
+
+// Fixed cost of one work item in page-equivalents (query load, first-page
+// latency, epilogue and partial write), used to compare chunk sizes.
+constexpr double kItemCost = 2.0;
+
+// Number of work items for a given chunk size.
+int64_t count_items(const std::vector<int>& pages, int Hkv, int chunk) {
+  int64_t n = 0;
+  for (int p : pages) n += (p + chunk - 1) / chunk;
+  return n * Hkv;
+}
+
+// Estimated duration, in page-equivalents, of the work list for chunk size
+// `chunk` on `slots` workgroups that take items in list order (longest
+// first) as slots free up -- how the dispatcher runs the grid.
+double makespan(const std::vector<int>& pages, int Hkv, int chunk, int slots) {
+  std::vector<int> lens;
+  for (int p : pages) {
+    const int ns = (p + chunk - 1) / chunk;
+    for (int s = 0; s < ns; ++s) {
+      const int len = (int)((int64_t)p * (s + 1) / ns - (int64_t)p * s / ns);
+      for (int g = 0; g < Hkv; ++g) lens.push_back(len);
+    }
+  }
+  std::sort(lens.begin(), lens.end(), std::greater<int>());
+  std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+  for (int i = 0; i < slots; ++i) free_at.push(0.0);
+  double end = 0.0;
+  for (int len : lens) {
+    const double t = free_at.top() + kItemCost + len;
+    free_at.pop();
+    free_at.push(t);
+    end = std::max(end, t);
+  }
+  return end;
+}
+
+// Auto chunk size: for k = 1..10 rounds of the resident workgroups, the
+// smallest chunk whose item count fits k full rounds; the candidate with the
+// shortest estimated duration wins (ties: the larger chunk, fewer items).
+// Item counts just over a multiple of the resident slots leave a nearly empty
+// last round, which is what this avoids.
+int auto_chunk(const std::vector<int>& pages, int Hkv, int num_cus) {
+  int max_pages = kMinChunkPages;
+  for (int p : pages) max_pages = std::max(max_pages, p);
+  const int slots = std::max(1, num_cus * kResidentPerCU);
+  std::vector<int> cands;
+  for (int k = 1; k <= 10; ++k) {
+    const int64_t limit = (int64_t)k * slots;
+    if (count_items(pages, Hkv, max_pages) > limit) continue;  // even one item per request is too many
+    int lo = kMinChunkPages, hi = max_pages;                     // count_items is non-increasing in chunk
+    while (lo < hi) {
+      const int mid = lo + (hi - lo) / 2;
+      if (count_items(pages, Hkv, mid) <= limit) hi = mid; else lo = mid + 1;
+    }
+    cands.push_back(lo);
+  }
+  if (cands.empty()) return max_pages;
+  int best = cands[0];
+  double best_t = makespan(pages, Hkv, best, slots);
+  for (size_t i = 1; i < cands.size(); ++i) {
+    const double t = makespan(pages, Hkv, cands[i], slots);
+    if (t < best_t - 1e-9 || (t <= best_t + 1e-9 && cands[i] > best)) {
+      best = cands[i];
+      best_t = t;
+    }
+  }
+  return best;
+}
 
 }  // namespace
 
@@ -51,11 +116,8 @@ int plan_decode_host(const int32_t* seqlens, int B, int stride, int Hkv, int num
     total_units += (int64_t)n * Hkv;
   }
   int chunk = 0;
-  if (num_splits_request == 0) {
-    int64_t target = (int64_t)num_cus * items_per_cu();
-    int64_t c = (total_units + target - 1) / std::max<int64_t>(target, 1);
-    chunk = (int)std::max<int64_t>(kMinChunkPages, c);
-  }
+  if (num_splits_request == 0 && total_units > 0) chunk = auto_chunk(pages, Hkv, num_cus);
+  if (num_splits_request == 0 && chunk < 1) chunk = kMinChunkPages;
   // Split counts and near-equal page ranges per request.
   std::vector<WorkItem> list;
   int max_splits = 0;

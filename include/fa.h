@@ -127,7 +127,7 @@ size_t fa_decode_workspace_size(const int32_t* seqlens_host, int B, int Hq, int 
  *   max_pages_per_req  row stride of the page table; ceil(L_b/64) must fit.
  *   num_pages          P, pages in each pool.
  *   Hq, Hkv, D         heads and head size; Hq % Hkv == 0, Hq/Hkv in
- *                      {1, 2, 4, 8}, D = 128.
+ *                      {1, 2, 4, 8, 16}, D = 128.
  *   kv_dtype           FA_DTYPE_BF16 or FA_DTYPE_FP8_E4M3FN.
  *   num_splits_request 0 = let the plan choose the chunk size for the
  *                      device's CUs; k > 0 = split every request into

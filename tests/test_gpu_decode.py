@@ -47,6 +47,8 @@ CASES = [
     ([300, 2000], 4, 2, "bf16"),
     ([5000, 17, 640], 16, 2, "bf16"),
     ([5000, 17, 640], 16, 2, "fp8"),
+    ([1, 700, 2049], 32, 2, "bf16"),
+    ([1, 700, 2049], 32, 2, "fp8"),
 ]
 
 
