@@ -67,8 +67,12 @@ def decode_bytes(L, w):
 
 
 def source_sha(rel):
-    with open(os.path.join(ROOT, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of a source file, or of several joined by '+'."""
+    h = hashlib.sha256()
+    for part in rel.split("+"):
+        with open(os.path.join(ROOT, part), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(name, src_rel):
@@ -198,18 +202,18 @@ def copy_calibration(steps, warmup):
 # ``-o kt``), made by the commands that PROFILE_COMMANDS lists:
 #   DIR/kt                      --kernel-trace --stats of the default bench run
 #   DIR/pmc_<leg>_<COUNTER>     --pmc COUNTER of one leg, COUNTER in FETCH_SIZE, WRITE_SIZE
+DECODE_SRC = ("exact_attention_20_amd/csrc/decode.hip+exact_attention_20_amd/csrc/decode_mfma.hip"
+              "+exact_attention_20_amd/csrc/decode_common.h")
 PMC_LEGS = {
     "prefill_bf16_wl2": ("--only prefill --prefill-workload 2", ["prefill_bf16_kernel"],
                          "exact_attention_20_amd/csrc/prefill_bf16.hip"),
     "prefill_bf16_wl3": ("--only prefill --prefill-workload 3", ["prefill_bf16_kernel"],
                          "exact_attention_20_amd/csrc/prefill_bf16.hip"),
-    "decode_wl4": ("--only decode --decode-workload 4", ["decode_split_kernel", "lse_merge_kernel"],
-                   "exact_attention_20_amd/csrc/decode.hip"),
-    "decode_wl5": ("--only decode --decode-workload 5", ["decode_split_kernel", "lse_merge_kernel"],
-                   "exact_attention_20_amd/csrc/decode.hip"),
+    "decode_wl4": ("--only decode --decode-workload 4", ["decode_mfma_kernel", "lse_merge_kernel"], DECODE_SRC),
+    "decode_wl5": ("--only decode --decode-workload 5", ["decode_mfma_kernel", "lse_merge_kernel"], DECODE_SRC),
     "copy": ("--only copy", ["neg"], None),
 }
-PMC_RUN = "--steps 3 --warmup 1 --no-cpu-baseline"
+PMC_RUN = "--steps 3 --warmup 1 --prewarm-s 0 --no-cpu-baseline"
 
 
 def profile_commands(d):
@@ -445,9 +449,8 @@ def main():
                "unit": "GB/s", "ms_mean": round(t_dc, 5), "ms_median": round(statistics.median(res["decode_ms"]), 5),
                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(gbs / PEAK_HBM_GBS, 4),
-                            "traffic": read_traffic(f"decode_wl{wd.wid}_traffic.txt",
-                                                    "exact_attention_20_amd/csrc/decode.hip"),
-                            "kernel": "decode_split_kernel + lse_merge_kernel",
+                            "traffic": read_traffic(f"decode_wl{wd.wid}_traffic.txt", DECODE_SRC),
+                            "kernel": "decode_mfma_kernel + lse_merge_kernel",
                             "bytes_per_launch": res["decode_bytes"]},
                "plan": res["decode_plan"], "cpu_baseline": res["decode_cpu"]}
         line["decode"] = dec

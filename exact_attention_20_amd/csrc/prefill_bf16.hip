@@ -9,9 +9,10 @@
 //
 // gfx950 design.
 //  * Workgroup = NW wavefronts, each owning QB blocks of 32 query rows, so
-//    BR = 32*NW*QB rows per workgroup. K/V tiles of 64 keys are shared by all
-//    wavefronts through LDS; every K or V fragment a wavefront reads from
-//    LDS feeds QB matrix instructions.
+//    BR = 32*NW*QB rows per workgroup. Each wavefront keeps its Q rows in
+//    registers for the whole row block; K/V tiles of 64 keys are shared by
+//    all wavefronts through LDS (64 KB: two K and two V buffers); every K or
+//    V fragment a wavefront reads from LDS feeds QB matrix instructions.
 //  * Both contractions use v_mfma_f32_32x32x16_bf16 (fp32 accumulate) in the
 //    transposed form S^T = K Q^T and O^T = V^T P^T. In the 32x32 accumulator
 //    layout a lane then owns one query column and 16 keys of it, so the row
@@ -52,7 +53,6 @@ namespace {
 
 constexpr int kD = 128;        // head dim
 constexpr int kBc = 64;        // keys per tile
-constexpr int kQst = kD + 8;   // Q row stride in LDS (bf16 elements) = 272 B
 constexpr int kRow = kD * 2;   // K/V row in LDS: 256 B, unpadded, 16-byte units XOR-swizzled
 constexpr float kTau = 8.0f;   // lazy max threshold (log2 units)
 
@@ -95,11 +95,9 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   constexpr int BR = 32 * NW * QB;            // query rows per workgroup
   constexpr int KBUF = kBc * kRow;            // bytes per K buffer
   constexpr int VBUF = kBc * kRow;            // bytes per V buffer
-  constexpr int QBUF = BR * kQst * 2;         // bytes of the Q tile
   constexpr int BLK = (kBc * kRow / 1024) / NW;  // 1 KB direct-load blocks per wave per tile
   __shared__ __attribute__((aligned(16))) char k_lds[2 * KBUF];
   __shared__ __attribute__((aligned(16))) char v_lds[2 * VBUF];
-  __shared__ __attribute__((aligned(16))) char q_lds[QBUF];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -135,20 +133,21 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   const uint16_t* K = reinterpret_cast<const uint16_t*>(a.k) + ((size_t)b * a.Hkv + g) * (size_t)a.Sk * kD;
   const uint16_t* V = reinterpret_cast<const uint16_t*>(a.v) + ((size_t)b * a.Hkv + g) * (size_t)a.Sk * kD;
 
-  // ---- The Q tile goes to LDS once (row-major, 272-byte rows). Query block
-  // qb of this wavefront is rows 32*(QB*wave + qb) .. +31 of the tile; the B
-  // operand of S^T = K Q^T for lane (col, hi) is that block's row col, dims
-  // 16*kk + 8*hi + 0..7.
+  // ---- Q: the B operand of S^T = K Q^T for lane (col, hi) in query block
+  // qb is row 32*(QB*wave + qb) + col of the tile, dims 16*kk + 8*hi + 0..7.
+  // It is the same for every key tile, so it is read once from HBM straight
+  // into registers (no LDS space, no LDS reads in the loop).
+  bf16x8_t qreg[QB][8];
 #pragma unroll
-  for (int it = 0; it < BR * 16 / NT; ++it) {
-    const int chunk = it * NT + tid;
-    const int r = chunk >> 4;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (q0 + r < a.Sq) v = *reinterpret_cast<const uint4*>(Q + (size_t)(q0 + r) * kD + 8 * (chunk & 15));
-    *reinterpret_cast<uint4*>(q_lds + (r * kQst + 8 * (chunk & 15)) * 2) = v;
+  for (int qb = 0; qb < QB; ++qb) {
+    const int r = q0 + 32 * (QB * wave + qb) + col;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (r < a.Sq) v = *reinterpret_cast<const uint4*>(Q + (size_t)r * kD + 16 * kk + 8 * hi);
+      qreg[qb][kk] = __builtin_bit_cast(bf16x8_t, v);
+    }
   }
-  const char* q_lane = q_lds + ((QB * wave * 32 + col) * kQst + 8 * hi) * 2;
-  constexpr int QBLK = 32 * kQst * 2;  // bytes between query blocks in LDS
 
   // Per query block: first row, this lane's row, running max (log2 units,
   // same in lane and lane^32), shares of the two normalisers, O^T.
@@ -243,7 +242,7 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
       const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(kl + k_off[kk] + 32 * kRow);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const bf16x8_t qf = *reinterpret_cast<const bf16x8_t*>(q_lane + qb * QBLK + 32 * kk);
+        const bf16x8_t qf = qreg[qb][kk];
         s[qb][0] = mfma32(a0, qf, s[qb][0]);
         s[qb][1] = mfma32(a1, qf, s[qb][1]);
       }
@@ -345,7 +344,7 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
           const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(kl + k_off[kk] + 32 * kRow);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
-            const bf16x8_t qf = *reinterpret_cast<const bf16x8_t*>(q_lane + qb * QBLK + 32 * kk);
+            const bf16x8_t qf = qreg[qb][kk];
             n[qb][0] = mfma32(a0, qf, n[qb][0]);
             n[qb][1] = mfma32(a1, qf, n[qb][1]);
           }
@@ -375,7 +374,7 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
     if (n_kt > 1) load_k(1);
   }
   wait_loads();
-  __syncthreads();  // Q, K(0), K(1), V(0) visible to every wavefront
+  __syncthreads();  // K(0), K(1), V(0) visible to every wavefront
   if (n_kt > 0 && any_active(0)) qk(0, sc);
   __syncthreads();  // every wavefront has read K(0) before K(2) replaces it
 
