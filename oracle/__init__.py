@@ -17,9 +17,12 @@ from .attention import (  # noqa: F401
     causal_allowed,
     e4m3fn_to_float,
     gather_pages,
+    kv_append,
     kv_head_of,
     lse_merge,
     paged_decode,
+    paged_prefill,
+    paged_prefill_request,
     prefill,
     scores,
     softmax_rows,

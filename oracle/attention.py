@@ -19,6 +19,9 @@ Sources (titles of the pages, with the part used):
         [1,H,seq,d], scores / sqrt(head_dim), softmax, weights @ V).
   [ARC] "FlashAttention breakthrough architecture" article, "paged storage
         system" (64-token blocks behind a page table).
+  [FPF] "Flash Attention & Paged Attention" blog, "FA and the prefill phase"
+        (prefill attends over the whole prompt and stores the computed K and V
+        in device memory as the initial KV cache).
 
 Readings where the pages leave a step open (each is stated where used):
   * LSE is the natural log of the sum of exp over the scaled, unmasked scores
@@ -27,6 +30,10 @@ Readings where the pages leave a step open (each is stated where used):
     j <= i + (Sk - Sq). A row with no visible key has O = 0, LSE = -inf.
   * GQA: query head h reads KV head h // (Hq / Hkv) unless a map is given.
   * fp8 KV values are OCP e4m3fn codes times a per-(page, KV head) scale.
+  * A ragged prefill chunk of n new tokens for a request whose cache ends up
+    L tokens long occupies logical positions L - n .. L - 1 (the new tokens
+    follow the cached prefix); causal masking over its L keys is then the
+    bottom-right rule above with Sq = n, Sk = L.
 """
 from __future__ import annotations
 
@@ -230,3 +237,76 @@ def lse_merge(partial_o, partial_lse):
     lse = mx + np.log(tot)
     o = (w / tot) @ o_s
     return o, lse
+
+
+# --------------------------------------------------------------------------
+# Ragged prefill over paged KV caches, and the KV append that precedes it.
+# --------------------------------------------------------------------------
+
+def kv_append(k_pages, v_pages, page_table, seqlens, cu_seqlens_q, k_new, v_new):
+    """Store each request's new tokens' K/V in its pages ([FPF]; [FPA] "2. PagedAttention").
+
+    Request b owns the packed new tokens cu[b] .. cu[b+1]-1; with n_b of them
+    and a final length L_b, new token i sits at logical position
+    t = L_b - n_b + i, i.e. slot t mod 64 of physical page table[b, t // 64].
+    ``k_new`` / ``v_new`` [T, Hkv, D]. Returns copies of the pools with those
+    slots overwritten and every other element unchanged. Pure data movement:
+    any element type works (pass raw bit patterns for a bitwise check).
+    """
+    kp, vp = np.array(k_pages, copy=True), np.array(v_pages, copy=True)
+    k_new, v_new = np.asarray(k_new), np.asarray(v_new)
+    cu = np.asarray(cu_seqlens_q)
+    for b in range(len(seqlens)):
+        L, n = int(seqlens[b]), int(cu[b + 1] - cu[b])
+        for i in range(n):
+            t = L - n + i
+            pid = int(page_table[b][t // PAGE])
+            kp[pid, :, t % PAGE, :] = k_new[cu[b] + i]
+            vp[pid, :, t % PAGE, :] = v_new[cu[b] + i]
+    return kp, vp
+
+
+def paged_prefill_request(q_b, k_pages, v_pages, table_row, L: int, scale, rows=None):
+    """Causal attention of one request's new tokens over its whole paged cache.
+
+    ``q_b`` [n, Hq, D]: the request's new tokens, the last n of its L
+    positions. Each KV head's L tokens are gathered in logical order, then
+    every query head runs the definition with the bottom-right causal mask
+    (Sq = n, Sk = L), so new token i sees keys 0 .. L - n + i. Returns
+    O [R, Hq, D] and LSE [R, Hq] for ``rows`` (default all n).
+    """
+    q_b = np.asarray(q_b, dtype=np.float64)
+    n, Hq, _ = q_b.shape
+    Hkv = k_pages.shape[1]
+    rows = np.arange(n) if rows is None else np.asarray(rows)
+    O = np.zeros((len(rows), Hq, v_pages.shape[3]))
+    LSE = np.zeros((len(rows), Hq))
+    if len(rows) == 0:
+        return O, LSE
+    for g in range(Hkv):
+        kb = gather_pages(k_pages, table_row, L, g)
+        vb = gather_pages(v_pages, table_row, L, g)
+        for h in range(Hq):
+            if kv_head_of(h, Hq, Hkv) != g:
+                continue
+            O[:, h], LSE[:, h] = attention_head(q_b[:, h], kb, vb, scale, True, rows)
+    return O, LSE
+
+
+def paged_prefill(q, k_pages, v_pages, page_table, seqlens, cu_seqlens_q, scale):
+    """Ragged causal prefill of a packed batch against paged caches.
+
+    q [T, Hq, D] packed by request (cu_seqlens_q [B+1]); pools [P, Hkv, 64, D]
+    already holding every request's L_b tokens, new ones included. Returns
+    O [T, Hq, D], LSE [T, Hq] ([FPF]: prefill over the whole sequence; [FIA]
+    section 2: variable-length batches over paged KV).
+    """
+    q = np.asarray(q)
+    cu = np.asarray(cu_seqlens_q)
+    O = np.zeros((q.shape[0], q.shape[1], v_pages.shape[3]))
+    LSE = np.zeros((q.shape[0], q.shape[1]))
+    for b in range(len(seqlens)):
+        s, e = int(cu[b]), int(cu[b + 1])
+        O[s:e], LSE[s:e] = paged_prefill_request(q[s:e], k_pages, v_pages, page_table[b],
+                                                 int(seqlens[b]), scale)
+    return O, LSE

@@ -368,4 +368,138 @@ def pin_fp8_paged_dequant():
         _close(got, ref.numpy(), 0.0, f"fp8 gather head {gg}")
 
 
+# --------------------------------------------------------------------------
+# Ragged prefill over pages, and the KV append
+# --------------------------------------------------------------------------
+
+def _ragged_case(seed, Hq, Hkv, D, nq, pre, stride=None, fill=np.nan):
+    """Tiny ragged batch: pools hold random prefixes, new-token slots ``fill``."""
+    g = _rng(seed)
+    nq, pre = np.asarray(nq), np.asarray(pre)
+    L = pre + nq
+    n_pages = (L + 63) // 64
+    P = int(n_pages.sum()) + 2  # two pages nobody references
+    perm = g.permutation(P)
+    table = np.full((len(L), stride or max(int(n_pages.max()), 1)), -1)
+    kp = g.standard_normal((P, Hkv, 64, D))
+    vp = g.standard_normal((P, Hkv, 64, D))
+    off = 0
+    for b in range(len(L)):
+        table[b, :n_pages[b]] = perm[off:off + n_pages[b]]
+        off += n_pages[b]
+        for t in range(pre[b], n_pages[b] * 64):  # new slots and the tail
+            kp[table[b, t // 64], :, t % 64] = fill
+            vp[table[b, t // 64], :, t % 64] = fill
+    cu = np.concatenate([[0], np.cumsum(nq)])
+    T = int(cu[-1])
+    q = g.standard_normal((T, Hq, D))
+    kn = g.standard_normal((T, Hkv, D))
+    vn = g.standard_normal((T, Hkv, D))
+    return q, kn, vn, kp, vp, table, L, cu
+
+
+def pin_kv_append_layout():
+    """Append writes new token i of request b at position prefix_b + i, bit for bit.
+
+    The expected pool is built the other way round: each request's full
+    logical sequence (prefix read from the pool by hand, then its new rows)
+    is laid out page by page through the table; slots no request covers,
+    and the tails of last pages, must keep their old bits.
+    """
+    Hkv, D = 2, 3
+    nq, pre = [5, 0, 70, 64, 1], [0, 9, 60, 128, 63]
+    q, kn, vn, kp, vp, table, L, cu = _ragged_case(20, 2, Hkv, D, nq, pre, fill=-7.0)
+    # integer-valued, distinct contents so any misplaced copy shows
+    kn = np.arange(kn.size, dtype=np.float64).reshape(kn.shape) + 1000.0
+    vn = -kn
+    got_k, got_v = A.kv_append(kp, vp, table, L, cu, kn, vn)
+    exp_k, exp_v = kp.copy(), vp.copy()
+    for b in range(len(L)):
+        seq_k = [kp[table[b, t // 64], :, t % 64] for t in range(pre[b])] + list(kn[cu[b]:cu[b + 1]])
+        seq_v = [vp[table[b, t // 64], :, t % 64] for t in range(pre[b])] + list(vn[cu[b]:cu[b + 1]])
+        assert len(seq_k) == L[b]
+        for t in range(L[b]):
+            exp_k[table[b, t // 64], :, t % 64] = seq_k[t]
+            exp_v[table[b, t // 64], :, t % 64] = seq_v[t]
+    assert np.array_equal(got_k, exp_k) and np.array_equal(got_v, exp_v), "kv_append layout"
+    assert not np.shares_memory(got_k, kp), "kv_append must not modify its input"
+
+
+def _brute_ragged(q, kp, vp, table, L, cu, scale, Hkv):
+    """Pure-Python loops: each new token against its request's keys 0 .. its own position."""
+    T, Hq, D = q.shape
+    O, LSE = np.zeros((T, Hq, vp.shape[3])), np.zeros((T, Hq))
+    for b in range(len(L)):
+        n = int(cu[b + 1] - cu[b])
+        for i in range(n):
+            pos = int(L[b]) - n + i
+            for h in range(Hq):
+                g = h * Hkv // Hq
+                ks = [kp[table[b][j // 64], g, j % 64].tolist() for j in range(pos + 1)]
+                vs = [vp[table[b][j // 64], g, j % 64].tolist() for j in range(pos + 1)]
+                qi = q[cu[b] + i, h].tolist()
+                s = [scale * math.fsum(a * c for a, c in zip(qi, kj)) for kj in ks]
+                mx = max(s)
+                w = [math.exp(x - mx) for x in s]
+                tot = math.fsum(w)
+                O[cu[b] + i, h] = [math.fsum(w[j] * vs[j][d] for j in range(len(w))) / tot
+                                   for d in range(len(vs[0]))]
+                LSE[cu[b] + i, h] = mx + math.log(tot)
+    return O, LSE
+
+
+def pin_paged_prefill_brute_force():
+    """Ragged paged prefill equals hand-indexed brute force on a tiny batch."""
+    Hq, Hkv, D = 4, 2, 3
+    nq, pre = [3, 0, 2, 66, 1], [0, 5, 62, 1, 64]
+    q, kn, vn, kp, vp, table, L, cu = _ragged_case(21, Hq, Hkv, D, nq, pre, stride=3)
+    kp, vp = A.kv_append(kp, vp, table, L, cu, kn, vn)
+    O, LSE = A.paged_prefill(q, kp, vp, table, L, cu, 0.7)
+    bo, bl = _brute_ragged(q, kp, vp, table, L, cu, 0.7, Hkv)
+    _close(O, bo, 1e-13, "ragged brute O")
+    _close(LSE, bl, 1e-13, "ragged brute LSE")
+
+
+def pin_paged_prefill_torch_sdpa():
+    """Each request equals torch SDPA (fp64) on its gathered cache with an explicit position mask."""
+    Hq, Hkv, D = 4, 1, 8
+    nq, pre = [40, 100, 1], [90, 0, 200]
+    q, kn, vn, kp, vp, table, L, cu = _ragged_case(22, Hq, Hkv, D, nq, pre)
+    kp, vp = A.kv_append(kp, vp, table, L, cu, kn, vn)
+    O, LSE = A.paged_prefill(q, kp, vp, table, L, cu, 0.25)
+    tk, tv = torch.from_numpy(kp), torch.from_numpy(vp)
+    for b in range(len(L)):
+        n, Lb = int(nq[b]), int(L[b])
+        ids = torch.from_numpy(table[b, :(Lb + 63) // 64].astype(np.int64))
+        kb = tk[ids].permute(1, 0, 2, 3).reshape(Hkv, -1, D)[:, :Lb]  # [Hkv, L, D]
+        vb = tv[ids].permute(1, 0, 2, 3).reshape(Hkv, -1, D)[:, :Lb]
+        qb = torch.from_numpy(q[cu[b]:cu[b + 1]]).permute(1, 0, 2)     # [Hq, n, D]
+        keep = torch.arange(Lb)[None, :] <= (Lb - n + torch.arange(n))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qb, kb.expand(Hq, -1, -1), vb.expand(Hq, -1, -1), attn_mask=keep, scale=0.25)
+        _close(O[cu[b]:cu[b + 1]], ref.permute(1, 0, 2).numpy(), 1e-12, f"ragged sdpa O b={b}")
+        s = 0.25 * qb @ kb.expand(Hq, -1, -1).transpose(1, 2)
+        lse = torch.logsumexp(s.masked_fill(~keep, float("-inf")), dim=2).T
+        _close(LSE[cu[b]:cu[b + 1]], lse.numpy(), 1e-12, f"ragged logsumexp b={b}")
+
+
+def pin_paged_prefill_reductions():
+    """Special cases: no prefix == causal prefill; the last new token == paged decode."""
+    Hq, Hkv, D = 4, 2, 8
+    nq, pre = [70, 5], [0, 130]
+    q, kn, vn, kp, vp, table, L, cu = _ragged_case(23, Hq, Hkv, D, nq, pre)
+    kp, vp = A.kv_append(kp, vp, table, L, cu, kn, vn)
+    O, LSE = A.paged_prefill(q, kp, vp, table, L, cu, 0.4)
+    # request 0 has no prefix: ordinary square causal prefill on its own tokens
+    po, pl = A.prefill(q[None, :70].transpose(0, 2, 1, 3), kn[None, :70].transpose(0, 2, 1, 3),
+                       vn[None, :70].transpose(0, 2, 1, 3), 0.4, True)
+    _close(O[:70], po[0].transpose(1, 0, 2), 1e-12, "no-prefix == prefill O")
+    _close(LSE[:70], pl[0].T, 1e-12, "no-prefix == prefill LSE")
+    # each request's last new token sees the whole cache: a decode query
+    last = cu[1:] - 1
+    do, dl = A.paged_decode(q[last], kp, vp, table, L, 0.4)
+    _close(O[last], do, 1e-12, "last token == decode O")
+    _close(LSE[last], dl, 1e-12, "last token == decode LSE")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

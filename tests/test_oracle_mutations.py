@@ -12,7 +12,8 @@ import oracle_pins
 from oracle import attention as A
 
 _orig = {n: getattr(A, n) for n in ("scores", "causal_allowed", "softmax_rows", "attention_head",
-                                    "kv_head_of", "e4m3fn_to_float", "gather_pages", "lse_merge")}
+                                    "kv_head_of", "e4m3fn_to_float", "gather_pages", "lse_merge",
+                                    "kv_append", "paged_prefill_request", "paged_prefill")}
 
 
 def _scores_no_scale(q, k, scale):
@@ -131,6 +132,73 @@ def _merge_max_lse(po, pl):
     return o, pl[np.isfinite(pl)].max()
 
 
+def _append_at(k_pages, v_pages, page_table, seqlens, cu, k_new, v_new, where):
+    kp, vp = np.array(k_pages, copy=True), np.array(v_pages, copy=True)
+    for b in range(len(seqlens)):
+        L, n = int(seqlens[b]), int(cu[b + 1] - cu[b])
+        for i in range(n):
+            t = where(L, n, i, b, cu)
+            kp[int(page_table[b][t // 64]), :, t % 64] = k_new[cu[b] + i]
+            vp[int(page_table[b][t // 64]), :, t % 64] = v_new[cu[b] + i]
+    return kp, vp
+
+
+def _append_ignores_prefix(*a):
+    return _append_at(*a, where=lambda L, n, i, b, cu: i)
+
+
+def _append_prefix_from_offsets(*a):
+    # prefix taken as L - cu[b+1] (a packed offset) instead of L - n
+    return _append_at(*a, where=lambda L, n, i, b, cu: max(L - int(cu[b + 1]), 0) + i)
+
+
+def _append_k_only(k_pages, v_pages, page_table, seqlens, cu, k_new, v_new):
+    kp, _ = _orig["kv_append"](k_pages, v_pages, page_table, seqlens, cu, k_new, v_new)
+    return kp, np.array(v_pages, copy=True)
+
+
+def _ragged_top_left(q_b, k_pages, v_pages, table_row, L, scale, rows=None):
+    # causal mask aligned top-left (key j <= new-token index i), ignoring the prefix
+    q_b = np.asarray(q_b, dtype=np.float64)
+    n, Hq, _ = q_b.shape
+    Hkv = k_pages.shape[1]
+    O, LSE = np.zeros((n, Hq, v_pages.shape[3])), np.zeros((n, Hq))
+    for h in range(Hq):
+        g = A.kv_head_of(h, Hq, Hkv)
+        kb = A.gather_pages(k_pages, table_row, L, g)
+        vb = A.gather_pages(v_pages, table_row, L, g)
+        s = A.scores(q_b[:, h], kb, scale)
+        s = np.where(np.arange(L)[None, :] <= np.arange(n)[:, None], s, -np.inf)
+        P, m, l = A.softmax_rows(s)
+        O[:, h] = P @ vb
+        LSE[:, h] = m + np.log(l)
+    return O, LSE
+
+
+def _ragged_non_causal(q_b, k_pages, v_pages, table_row, L, scale, rows=None):
+    q_b = np.asarray(q_b, dtype=np.float64)
+    n, Hq, _ = q_b.shape
+    Hkv = k_pages.shape[1]
+    O, LSE = np.zeros((n, Hq, v_pages.shape[3])), np.zeros((n, Hq))
+    for h in range(Hq):
+        g = A.kv_head_of(h, Hq, Hkv)
+        O[:, h], LSE[:, h] = A.attention_head(q_b[:, h], A.gather_pages(k_pages, table_row, L, g),
+                                              A.gather_pages(v_pages, table_row, L, g), scale, False)
+    return O, LSE
+
+
+def _ragged_prefix_keys_only(q, k_pages, v_pages, page_table, seqlens, cu, scale):
+    # keys limited to the cached prefix (length L - n): the new tokens are left out
+    cu = np.asarray(cu)
+    O = np.zeros((q.shape[0], q.shape[1], v_pages.shape[3]))
+    LSE = np.zeros((q.shape[0], q.shape[1]))
+    for b in range(len(seqlens)):
+        s, e = int(cu[b]), int(cu[b + 1])
+        O[s:e], LSE[s:e] = A.paged_prefill_request(q[s:e], k_pages, v_pages, page_table[b],
+                                                   int(seqlens[b]) - (e - s), scale)
+    return O, LSE
+
+
 MUTANTS = {
     "scores_no_scale": ("scores", _scores_no_scale),
     "scores_sqrt_scale": ("scores", _scores_sqrt_scale),
@@ -152,6 +220,12 @@ MUTANTS = {
     "gather_wrong_scale": ("gather_pages", _gather_wrong_scale_index),
     "merge_plain_mean": ("lse_merge", _merge_plain_mean),
     "merge_max_lse": ("lse_merge", _merge_max_lse),
+    "append_ignores_prefix": ("kv_append", _append_ignores_prefix),
+    "append_prefix_from_offsets": ("kv_append", _append_prefix_from_offsets),
+    "append_k_only": ("kv_append", _append_k_only),
+    "ragged_top_left_mask": ("paged_prefill_request", _ragged_top_left),
+    "ragged_non_causal": ("paged_prefill_request", _ragged_non_causal),
+    "ragged_prefix_keys_only": ("paged_prefill", _ragged_prefix_keys_only),
 }
 
 

@@ -39,6 +39,7 @@ import torch
 PAGE = 64  # tokens per KV page
 
 STREAM_LENGTHS, STREAM_PERM, STREAM_Q, STREAM_K, STREAM_V = 0, 1, 2, 3, 4
+STREAM_PREFIX, STREAM_KNEW, STREAM_VNEW = 5, 6, 7
 
 
 @dataclass(frozen=True)
@@ -74,6 +75,28 @@ class DecodeWorkload:
         return float(np.float32(1.0 / math.sqrt(self.D)))
 
 
+@dataclass(frozen=True)
+class RaggedPrefillWorkload:
+    """A ragged batch of prefill chunks appended to paged KV caches.
+
+    Request b brings ``new_b`` query tokens whose K/V are appended after a
+    cached prefix of ``prefix_b`` tokens; its causal attention covers all
+    ``prefix_b + new_b`` keys.
+    """
+    wid: int
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    new_lens: tuple     # length spec for the new tokens (see context_lengths)
+    prefix_lens: tuple  # length spec for the cached prefixes
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.D)))
+
+
 WORKLOADS = {
     1: PrefillWorkload(1, "tiny_fp32_b1_h2_s128_d64", 1, 2, 2, 128, 64, "f32", (False, True)),
     2: PrefillWorkload(2, "causal_prefill_bf16_b4_h32_s4096_d128", 4, 32, 32, 4096, 128, "bf16", (True,)),
@@ -82,6 +105,8 @@ WORKLOADS = {
                       ("uniform", 512, 16384)),
     5: DecodeWorkload(5, "paged_decode_fp8_b8_hq32_hkv8_d128_L4096-131072", 8, 32, 8, 128, "fp8",
                       ("loguniform", 4096, 131072)),
+    6: RaggedPrefillWorkload(6, "ragged_paged_prefill_bf16_b16_hq32_hkv8_d128_new256-2048_prefix0-16384",
+                             16, 32, 8, 128, ("uniform", 256, 2048), ("uniform", 0, 16384)),
 }
 
 
@@ -112,7 +137,7 @@ def workload_prefill_inputs(w: PrefillWorkload):
     return prefill_inputs(w.B, w.Hq, w.Hkv, w.S, w.S, w.D, w.dtype, w.wid)
 
 
-def context_lengths(wid: int, B: int, spec) -> np.ndarray:
+def context_lengths(wid: int, B: int, spec, stream: int = STREAM_LENGTHS) -> np.ndarray:
     """Per-request context lengths, int32 [B].
 
     ("uniform", lo, hi): integers uniform on [lo, hi] inclusive.
@@ -121,7 +146,7 @@ def context_lengths(wid: int, B: int, spec) -> np.ndarray:
     ("list", [...]): the given lengths.
     """
     kind = spec[0]
-    g = rng(wid, STREAM_LENGTHS)
+    g = rng(wid, stream)
     if kind == "uniform":
         L = g.integers(spec[1], spec[2], size=B, endpoint=True)
     elif kind == "loguniform":
@@ -155,6 +180,32 @@ class PagedKV:
         return self.q.shape[0]
 
 
+def _page_layout(L: np.ndarray, wid: int, max_pages=None, extra_pages=0):
+    """Page table for lengths ``L``: (table [B, stride], pool size, partial pages).
+
+    Request b's logical page j is physical page ``perm[offset_b + j]``;
+    ``partial`` lists (physical page, valid tokens) for every referenced page
+    that is only partly filled (at most one per request, its last page).
+    """
+    B = len(L)
+    pages_b = (L.astype(np.int64) + PAGE - 1) // PAGE
+    P = int(pages_b.sum()) + int(extra_pages)
+    P_alloc = max(P, 1)
+    stride = int(max_pages) if max_pages is not None else max(int(pages_b.max(initial=0)), 1)
+    perm = rng(wid, STREAM_PERM).permutation(P_alloc).astype(np.int32)
+    table = np.full((B, stride), -1, dtype=np.int32)
+    partial = []
+    off = 0
+    for b in range(B):
+        n = int(pages_b[b])
+        ids = perm[off:off + n]
+        table[b, :n] = ids
+        if n and int(L[b]) % PAGE:
+            partial.append((int(ids[-1]), int(L[b]) % PAGE))
+        off += n
+    return table, P_alloc, partial
+
+
 def paged_inputs(B, Hq, Hkv, D, kv_dtype, lengths, wid, nan_tails=True,
                  max_pages=None, extra_pages=0) -> PagedKV:
     """Build a paged decode batch.
@@ -168,23 +219,7 @@ def paged_inputs(B, Hq, Hkv, D, kv_dtype, lengths, wid, nan_tails=True,
         L = context_lengths(wid, B, lengths)
     else:
         L = np.asarray(lengths, dtype=np.int32)
-    pages_b = (L.astype(np.int64) + PAGE - 1) // PAGE
-    P = int(pages_b.sum()) + int(extra_pages)
-    P_alloc = max(P, 1)
-    stride = int(max_pages) if max_pages is not None else max(int(pages_b.max(initial=0)), 1)
-    perm = rng(wid, STREAM_PERM).permutation(P_alloc).astype(np.int32)
-    table = np.full((B, stride), -1, dtype=np.int32)
-    # (physical page, valid tokens) for every referenced page that is only
-    # partly filled: at most one per request, its last page.
-    partial = []
-    off = 0
-    for b in range(B):
-        n = int(pages_b[b])
-        ids = perm[off:off + n]
-        table[b, :n] = ids
-        if n and int(L[b]) % PAGE:
-            partial.append((int(ids[-1]), int(L[b]) % PAGE))
-        off += n
+    table, P_alloc, partial = _page_layout(L, wid, max_pages, extra_pages)
     shape = (P_alloc, Hkv, PAGE, D)
     q = normal(wid, STREAM_Q, (B, Hq, D), "bf16")
     k32 = rng(wid, STREAM_K).standard_normal(size=shape, dtype=np.float32)
@@ -230,3 +265,75 @@ def _quantise_e4m3fn(x: np.ndarray, partial, nan_tails: bool):
 
 def workload_paged_inputs(w: DecodeWorkload, nan_tails=True) -> PagedKV:
     return paged_inputs(w.B, w.Hq, w.Hkv, w.D, w.kv_dtype, w.lengths, w.wid, nan_tails)
+
+
+@dataclass
+class RaggedPaged:
+    """A ragged prefill batch over paged KV caches, all host (CPU) tensors.
+
+    The pools already hold every request's cached prefix; the slots where its
+    new tokens go are NaN until the new K/V are appended.
+    """
+    q: torch.Tensor             # [T, Hq, D] bf16, T = total new tokens (packed)
+    k_new: torch.Tensor         # [T, Hkv, D] bf16
+    v_new: torch.Tensor         # [T, Hkv, D] bf16
+    k_pages: torch.Tensor       # [P, Hkv, 64, D] bf16
+    v_pages: torch.Tensor
+    page_table: torch.Tensor    # [B, max_pages] int32, -1 where unused
+    seqlens: torch.Tensor       # [B] int32, prefix + new tokens
+    cu_seqlens_q: torch.Tensor  # [B + 1] int32, offsets of each request's new tokens
+    num_pages: int
+
+    @property
+    def B(self):
+        return self.seqlens.shape[0]
+
+    @property
+    def max_q(self):
+        cu = self.cu_seqlens_q
+        return int((cu[1:] - cu[:-1]).max()) if self.B else 0
+
+
+def ragged_inputs(Hq, Hkv, D, new_lens, prefix_lens, wid, max_pages=None, extra_pages=0,
+                  poison=True) -> RaggedPaged:
+    """Build a ragged prefill batch from per-request int arrays.
+
+    ``new_lens[b]`` new query tokens follow a cached prefix of
+    ``prefix_lens[b]`` tokens. Pools cover the final lengths prefix + new;
+    the prefix slots hold N(0,1) bf16 values, and when ``poison`` is set the
+    new tokens' slots and the tails of partly filled last pages hold NaN.
+    Q and the new K/V are packed along the token axis in request order.
+    """
+    nq = np.asarray(new_lens, dtype=np.int32)
+    pre = np.asarray(prefix_lens, dtype=np.int32)
+    assert nq.shape == pre.shape and (nq >= 0).all() and (pre >= 0).all()
+    B = len(nq)
+    L = (pre.astype(np.int64) + nq).astype(np.int32)
+    table, P_alloc, partial = _page_layout(L, wid, max_pages, extra_pages)
+    cu = np.zeros(B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(nq)
+    T = int(cu[-1])
+    shape = (P_alloc, Hkv, PAGE, D)
+    k = normal(wid, STREAM_K, shape, "bf16")
+    v = normal(wid, STREAM_V, shape, "bf16")
+    if poison:
+        for p, n in partial:
+            k[p, :, n:, :] = float("nan")
+            v[p, :, n:, :] = float("nan")
+        pos = [np.arange(pre[b], L[b]) for b in range(B)]
+        pid = np.concatenate([table[b, pos[b] // PAGE] for b in range(B)] + [np.zeros(0, np.int32)])
+        slot = np.concatenate([pos[b] % PAGE for b in range(B)] + [np.zeros(0, np.int64)])
+        pid, slot = torch.from_numpy(pid.astype(np.int64)), torch.from_numpy(slot.astype(np.int64))
+        k[pid, :, slot, :] = float("nan")
+        v[pid, :, slot, :] = float("nan")
+    q = normal(wid, STREAM_Q, (T, Hq, D), "bf16")
+    k_new = normal(wid, STREAM_KNEW, (T, Hkv, D), "bf16")
+    v_new = normal(wid, STREAM_VNEW, (T, Hkv, D), "bf16")
+    return RaggedPaged(q, k_new, v_new, k, v, torch.from_numpy(table), torch.from_numpy(L),
+                       torch.from_numpy(cu), P_alloc)
+
+
+def workload_ragged_inputs(w: RaggedPrefillWorkload, poison=True) -> RaggedPaged:
+    nq = context_lengths(w.wid, w.B, w.new_lens, STREAM_LENGTHS)
+    pre = context_lengths(w.wid, w.B, w.prefix_lens, STREAM_PREFIX)
+    return ragged_inputs(w.Hq, w.Hkv, w.D, nq, pre, w.wid, poison=poison)
