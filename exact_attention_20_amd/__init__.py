@@ -8,8 +8,10 @@ fallback. If ``libfa.so`` is missing the import of this module still works
 it with ``python -m exact_attention_20_amd.build``.
 
 Names mirror the C ABI in ``include/fa.h`` (``fa_prefill_fwd``,
-``fa_decode_plan``, ``fa_decode_run``, ...) plus convenience wrappers
-``prefill`` and ``decode`` that allocate the outputs.
+``fa_decode_plan``, ``fa_decode_run``, ``fa_kv_append``,
+``fa_prefill_paged_plan``, ``fa_prefill_paged_run``, ...) plus convenience
+wrappers ``prefill``, ``decode`` and ``prefill_paged`` that allocate the
+outputs.
 """
 from __future__ import annotations
 
@@ -22,6 +24,8 @@ __all__ = [
     "FAError", "lib_path", "load", "F32", "BF16", "FP8_E4M3FN",
     "fa_prefill_fwd", "prefill", "DecodePlan", "fa_decode_plan", "fa_decode_run", "decode",
     "fa_decode_plan_host", "fa_decode_workspace_size", "fa_debug_gather_kv",
+    "fa_kv_append", "PrefillPlan", "fa_prefill_paged_plan", "fa_prefill_paged_run",
+    "fa_prefill_paged_plan_host", "fa_prefill_paged_workspace_size", "prefill_paged",
 ]
 
 F32, BF16, FP8_E4M3FN = 0, 1, 2
@@ -73,6 +77,19 @@ def load():
     lib.fa_decode_run.restype = ci
     lib.fa_debug_gather_kv.argtypes = [vp, ci, vp, ci, ci, ci, ci, ci, ci, ci, vp, vp]
     lib.fa_debug_gather_kv.restype = ci
+    lib.fa_kv_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, vp]
+    lib.fa_kv_append.restype = ci
+    lib.fa_prefill_paged_plan_host.argtypes = [i32p, i32p, ci, i32p, ci]
+    lib.fa_prefill_paged_plan_host.restype = ci
+    lib.fa_prefill_paged_workspace_size.argtypes = [i32p, i32p, ci]
+    lib.fa_prefill_paged_workspace_size.restype = csz
+    lib.fa_prefill_paged_plan.argtypes = [i32p, i32p, i32p, ci, ci, ci, ci, ci, ci, vp, csz, vp,
+                                          C.POINTER(vp)]
+    lib.fa_prefill_paged_plan.restype = ci
+    lib.fa_prefill_paged_plan_destroy.argtypes = [vp]
+    lib.fa_prefill_paged_plan_destroy.restype = None
+    lib.fa_prefill_paged_run.argtypes = [vp, vp, vp, vp, vp, vp, vp, cf, vp, vp, vp, vp]
+    lib.fa_prefill_paged_run.restype = ci
     _LIB = lib
     return lib
 
@@ -269,3 +286,119 @@ def fa_debug_gather_kv(pages, kv_dtype, page_table, num_pages, b, L, kv_head, st
     _check(lib.fa_debug_gather_kv(_ptr(pages), kv_dtype, _ptr(page_table), page_table.shape[1],
                                   num_pages, Hkv, D, b, L, kv_head, _ptr(dst), _stream(stream)))
     return dst
+
+
+# ------------------------------------------------------------------ ragged paged prefill
+
+def _host_i32(x):
+    return _i32_host(x.cpu() if isinstance(x, torch.Tensor) else x)
+
+
+def fa_kv_append(k_new, v_new, k_pages, v_pages, page_table, seqlens, cu_seqlens_q, stream=None):
+    """Write the packed new tokens' K/V [T, Hkv, D] into their pages (in place)."""
+    lib = load()
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (k_pages, "k_pages"), (v_pages, "v_pages")):
+        _need(t, n, torch.bfloat16)
+    for t, n in ((page_table, "page_table"), (seqlens, "seqlens"), (cu_seqlens_q, "cu_seqlens_q")):
+        _need(t, n, torch.int32)
+    T, Hkv, D = k_new.shape
+    if v_new.shape != k_new.shape or k_pages.dim() != 4 or k_pages.shape[1:] != (Hkv, 64, D) \
+            or v_pages.shape != k_pages.shape:
+        raise FAError(1, "k_new/v_new must be [T, Hkv, D] and pools [P, Hkv, 64, D]")
+    B = seqlens.numel()
+    if cu_seqlens_q.numel() != B + 1 or page_table.dim() != 2 or page_table.shape[0] != B:
+        raise FAError(1, "cu_seqlens_q must have B + 1 entries and page_table B rows")
+    _check(lib.fa_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages), _ptr(page_table),
+                            _ptr(seqlens), _ptr(cu_seqlens_q), B, T, page_table.shape[1],
+                            k_pages.shape[0], Hkv, D, _stream(stream)))
+
+
+def fa_prefill_paged_plan_host(seqlens, cu_seqlens_q):
+    """Pure host planning: work items [n, 2] (request, query tile), heaviest first."""
+    lib = load()
+    sl, sp = _host_i32(seqlens)
+    cu, cp = _host_i32(cu_seqlens_q)
+    i32 = C.POINTER(C.c_int32)
+    B = sl.numel()
+    n = lib.fa_prefill_paged_plan_host(C.cast(sp, i32), C.cast(cp, i32), B, None, 0)
+    if n < 0:
+        _check(-n)
+    items = torch.zeros((max(n, 1), 2), dtype=torch.int32)
+    lib.fa_prefill_paged_plan_host(C.cast(sp, i32), C.cast(cp, i32), B, C.cast(items.data_ptr(), i32), n)
+    return items[:n]
+
+
+def fa_prefill_paged_workspace_size(seqlens, cu_seqlens_q):
+    sl, sp = _host_i32(seqlens)
+    cu, cp = _host_i32(cu_seqlens_q)
+    i32 = C.POINTER(C.c_int32)
+    n = load().fa_prefill_paged_workspace_size(C.cast(sp, i32), C.cast(cp, i32), sl.numel())
+    if n == 0:
+        raise FAError(1, "invalid lengths for the ragged prefill workspace")
+    return n
+
+
+class PrefillPlan:
+    """A ragged prefill plan plus the device workspace holding its work list."""
+
+    def __init__(self, handle, workspace, B, Hq, Hkv, D, n_items):
+        self.handle = handle
+        self.workspace = workspace
+        self.B, self.Hq, self.Hkv, self.D, self.n_items = B, Hq, Hkv, D, n_items
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _LIB is not None:
+            _LIB.fa_prefill_paged_plan_destroy(self.handle)
+            self.handle = None
+
+
+def fa_prefill_paged_plan(seqlens, cu_seqlens_q, page_table, num_pages, Hq, Hkv, D=128, device=None,
+                          stream=None):
+    """Plan a ragged prefill batch from host copies of its lengths (and page table, validated)."""
+    lib = load()
+    sl, sp = _host_i32(seqlens)
+    cu, cp = _host_i32(cu_seqlens_q)
+    pt, pp = _host_i32(page_table)
+    if pt.dim() != 2 or pt.shape[0] != sl.numel() or cu.numel() != sl.numel() + 1:
+        raise FAError(1, "page_table must be [B, max_pages] and cu_seqlens_q [B + 1]")
+    B, stride = pt.shape
+    i32 = C.POINTER(C.c_int32)
+    ws_bytes = lib.fa_prefill_paged_workspace_size(C.cast(sp, i32), C.cast(cp, i32), B)
+    if ws_bytes == 0:
+        raise FAError(1, "invalid ragged lengths")
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+    handle = C.c_void_p()
+    _check(lib.fa_prefill_paged_plan(C.cast(sp, i32), C.cast(cp, i32), C.cast(pp, i32), B, stride,
+                                     int(num_pages), Hq, Hkv, D, _ptr(ws), ws_bytes, _stream(stream),
+                                     C.byref(handle)))
+    n = lib.fa_prefill_paged_plan_host(C.cast(sp, i32), C.cast(cp, i32), B, None, 0)
+    return PrefillPlan(handle, ws, B, Hq, Hkv, D, n)
+
+
+def fa_prefill_paged_run(plan, q, k_pages, v_pages, page_table, seqlens, cu_seqlens_q, out, lse,
+                         scale=0.0, stream=None):
+    """Causal attention of the packed new tokens q [T, Hq, D] over their paged caches."""
+    lib = load()
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (out, "out")):
+        _need(t, n, torch.bfloat16)
+    _need(lse, "lse", torch.float32)
+    for t, n in ((page_table, "page_table"), (seqlens, "seqlens"), (cu_seqlens_q, "cu_seqlens_q")):
+        _need(t, n, torch.int32)
+    T, Hq, D = q.shape
+    if (Hq, D) != (plan.Hq, plan.D) or out.shape != q.shape or lse.shape != (T, Hq):
+        raise FAError(1, "q/out/lse shapes do not match the plan")
+    if k_pages.dim() != 4 or k_pages.shape[1:] != (plan.Hkv, 64, D) or v_pages.shape != k_pages.shape:
+        raise FAError(1, "KV pools must be [P, Hkv, 64, D]")
+    _check(lib.fa_prefill_paged_run(plan.handle, _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(page_table),
+                                    _ptr(seqlens), _ptr(cu_seqlens_q), float(scale or 0.0), _ptr(out),
+                                    _ptr(lse), _ptr(plan.workspace), _stream(stream)))
+    return out, lse
+
+
+def prefill_paged(plan, q, k_pages, v_pages, page_table, seqlens, cu_seqlens_q, scale=None,
+                  stream=None):
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    return fa_prefill_paged_run(plan, q, k_pages, v_pages, page_table, seqlens, cu_seqlens_q, out, lse,
+                                scale or 0.0, stream)

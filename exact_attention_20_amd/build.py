@@ -19,7 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["abi.cpp", "plan.cpp", "decode.hip", "decode_mfma.hip", "prefill_f32.hip", "prefill_bf16.hip"]
+SOURCES = ["abi.cpp", "plan.cpp", "decode.hip", "decode_mfma.hip", "prefill_f32.hip", "prefill_bf16.hip",
+           "kv_append.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -4,6 +4,7 @@
 // every check has passed.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -54,6 +55,11 @@ struct fa_decode_plan_s {
   std::vector<fa::WorkItem> items;
   std::vector<int32_t> splits;
   fa::WorkspaceLayout layout;
+};
+
+struct fa_prefill_plan_s {
+  int B, stride, num_pages, Hq, Hkv, D, n_items;
+  size_t bytes;  // workspace bytes the work list occupies
 };
 
 extern "C" {
@@ -287,6 +293,131 @@ int fa_decode_run(const fa_decode_plan_t* plan, const void* q, const void* k_pag
   if (e != hipSuccess) return hip_fail(e, "fa_decode_run split launch");
   e = fa::launch_lse_merge(a, s);
   if (e != hipSuccess) return hip_fail(e, "fa_decode_run merge launch");
+  return ok();
+}
+
+static int check_ragged_shape(const char* who, int B, int Hq, int Hkv, int D) {
+  if (B < 1 || Hq < 1 || Hkv < 1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: need B, Hq, Hkv >= 1", who);
+  if (Hq > fa::kMaxHeads || Hkv > fa::kMaxHeads)
+    return fail(FA_ERR_UNSUPPORTED, "%s: Hq and Hkv must be <= %d", who, fa::kMaxHeads);
+  if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARGUMENT, "%s: Hq %% Hkv != 0 (%d, %d)", who, Hq, Hkv);
+  if (D != 128) return fail(FA_ERR_UNSUPPORTED, "%s: D=%d not supported (128)", who, D);
+  return FA_OK;
+}
+
+int fa_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                 const int32_t* page_table, const int32_t* seqlens, const int32_t* cu_seqlens_q,
+                 int B, int total_q, int max_pages_per_req, int num_pages, int Hkv, int D,
+                 void* stream) {
+  if (B < 1 || Hkv < 1 || total_q < 0 || max_pages_per_req < 1 || num_pages < 1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_kv_append: need B, Hkv, max_pages_per_req, num_pages >= 1 and total_q >= 0");
+  if (D != 128) return fail(FA_ERR_UNSUPPORTED, "fa_kv_append: D=%d not supported (128)", D);
+  if (total_q == 0) return ok();
+  if (!k_new || !v_new || !k_pages || !v_pages || !page_table || !seqlens || !cu_seqlens_q)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_kv_append: null pointer");
+  fa::AppendArgs a;
+  a.k_new = k_new; a.v_new = v_new; a.k_pages = k_pages; a.v_pages = v_pages;
+  a.page_table = page_table; a.seqlens = seqlens; a.cu_q = cu_seqlens_q;
+  a.B = B; a.T = total_q; a.stride = max_pages_per_req; a.num_pages = num_pages; a.Hkv = Hkv; a.D = D;
+  hipError_t e = fa::launch_kv_append(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fa_kv_append launch");
+  return ok();
+}
+
+int fa_prefill_paged_plan_host(const int32_t* seqlens_host, const int32_t* cu_seqlens_q_host,
+                               int B, int32_t* items_out, int capacity) {
+  if (!seqlens_host || !cu_seqlens_q_host || B < 1 || capacity < 0) {
+    fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_paged_plan_host: invalid argument");
+    return -FA_ERR_INVALID_ARGUMENT;
+  }
+  int n = fa::plan_prefill_host(seqlens_host, cu_seqlens_q_host, B, items_out, capacity);
+  if (n < 0) {
+    fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_paged_plan_host: inconsistent lengths (cu[0] != 0, n_b < 0 or n_b > L_b)");
+    return -FA_ERR_INVALID_ARGUMENT;
+  }
+  ok();
+  return n;
+}
+
+size_t fa_prefill_paged_workspace_size(const int32_t* seqlens_host,
+                                       const int32_t* cu_seqlens_q_host, int B) {
+  if (!seqlens_host || !cu_seqlens_q_host || B < 1) return 0;
+  int n = fa::plan_prefill_host(seqlens_host, cu_seqlens_q_host, B, nullptr, 0);
+  if (n < 0) return 0;
+  return ((size_t)std::max(n, 1) * 2 * sizeof(int32_t) + 255) / 256 * 256;
+}
+
+int fa_prefill_paged_plan(const int32_t* seqlens_host, const int32_t* cu_seqlens_q_host,
+                          const int32_t* page_table_host, int B, int max_pages_per_req,
+                          int num_pages, int Hq, int Hkv, int D, void* workspace,
+                          size_t workspace_bytes, void* stream, fa_prefill_plan_t** plan_out) {
+  if (!plan_out) return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_paged_plan: plan_out is null");
+  *plan_out = nullptr;
+  int st = check_ragged_shape("fa_prefill_paged_plan", B, Hq, Hkv, D);
+  if (st != FA_OK) return st;
+  if (!seqlens_host || !cu_seqlens_q_host)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_paged_plan: seqlens_host and cu_seqlens_q_host are required");
+  if (max_pages_per_req < 1 || num_pages < 1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_paged_plan: need max_pages_per_req >= 1 and num_pages >= 1");
+  std::vector<int32_t> items;
+  int n = fa::plan_prefill_host(seqlens_host, cu_seqlens_q_host, B, nullptr, 0);
+  if (n < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_paged_plan: inconsistent lengths (cu[0] != 0, n_b < 0 or n_b > L_b)");
+  for (int b = 0; b < B; ++b) {
+    int64_t np = ((int64_t)seqlens_host[b] + fa::kPage - 1) / fa::kPage;
+    if (np > max_pages_per_req)
+      return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_paged_plan: request %d needs %lld pages > max_pages_per_req %d", b, (long long)np, max_pages_per_req);
+    if (page_table_host) {
+      for (int64_t j = 0; j < np; ++j) {
+        int32_t id = page_table_host[(int64_t)b * max_pages_per_req + j];
+        if (id < 0 || id >= num_pages)
+          return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_paged_plan: page_table[%d][%lld]=%d outside [0,%d)", b, (long long)j, id, num_pages);
+      }
+    }
+  }
+  const size_t need = fa_prefill_paged_workspace_size(seqlens_host, cu_seqlens_q_host, B);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "fa_prefill_paged_plan: workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  items.resize(2 * (size_t)std::max(n, 1), 0);
+  fa::plan_prefill_host(seqlens_host, cu_seqlens_q_host, B, items.data(), n);
+  fa_prefill_plan_t* p = new (std::nothrow) fa_prefill_plan_t;
+  if (!p) return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_paged_plan: out of host memory");
+  p->B = B; p->stride = max_pages_per_req; p->num_pages = num_pages;
+  p->Hq = Hq; p->Hkv = Hkv; p->D = D; p->n_items = n; p->bytes = need;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(workspace, items.data(), items.size() * sizeof(int32_t), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);  // the host list is freed on return
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "fa_prefill_paged_plan upload");
+  }
+  *plan_out = p;
+  return ok();
+}
+
+void fa_prefill_paged_plan_destroy(fa_prefill_plan_t* plan) { delete plan; }
+
+int fa_prefill_paged_run(const fa_prefill_plan_t* plan, const void* q, const void* k_pages,
+                         const void* v_pages, const int32_t* page_table, const int32_t* seqlens,
+                         const int32_t* cu_seqlens_q, float scale, void* out, float* lse,
+                         void* workspace, void* stream) {
+  if (!plan) return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_paged_run: plan is null");
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_paged_run: scale is not finite");
+  if (plan->n_items == 0) return ok();
+  if (!q || !k_pages || !v_pages || !page_table || !seqlens || !cu_seqlens_q || !out || !lse || !workspace)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_paged_run: null pointer");
+  fa::PrefillArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = q; a.k = k_pages; a.v = v_pages; a.out = out; a.lse = lse;
+  a.B = plan->B; a.Hq = plan->Hq; a.Hkv = plan->Hkv; a.D = plan->D;
+  a.causal = 1;
+  a.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)plan->D));
+  a.items = (const int32_t*)workspace;
+  a.page_table = page_table; a.seqlens = seqlens; a.cu_q = cu_seqlens_q;
+  a.stride = plan->stride; a.num_pages = plan->num_pages;
+  hipError_t e = fa::launch_prefill_paged_bf16(a, plan->n_items, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fa_prefill_paged_run launch");
   return ok();
 }
 

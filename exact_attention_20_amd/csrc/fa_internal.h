@@ -14,7 +14,7 @@ constexpr int kMaxHeads = 256;    // limit on Hq and Hkv (head map travels in ke
 // ---------------------------------------------------------------- prefill
 struct PrefillArgs {
   const void* q;
-  const void* k;
+  const void* k;      // contiguous [B, Hkv, Sk, D], or the K page pool (ragged)
   const void* v;
   void* out;
   float* lse;
@@ -22,11 +22,34 @@ struct PrefillArgs {
   int causal;
   float scale;        // score multiplier (already defaulted)
   int has_map;        // 0: contiguous groups h / (Hq/Hkv)
+  // Ragged paged prefill only (the per-request Sq, Sk come from cu_q, seqlens):
+  const int32_t* items;       // [n_items][2] (request, query tile), heaviest first
+  const int32_t* page_table;  // [B, stride]
+  const int32_t* seqlens;     // [B]
+  const int32_t* cu_q;        // [B + 1]
+  int stride;
+  int num_pages;
   uint8_t kv_map[kMaxHeads];
 };
 
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+
+// Query rows per work item of the bf16 prefill kernel (ragged plan unit).
+constexpr int kPrefillRows = 256;
+hipError_t launch_prefill_paged_bf16(const PrefillArgs& a, int n_items, hipStream_t s);
+
+struct AppendArgs {
+  const void* k_new;          // [T, Hkv, D] bf16
+  const void* v_new;
+  void* k_pages;              // [P, Hkv, 64, D] bf16
+  void* v_pages;
+  const int32_t* page_table;  // [B, stride]
+  const int32_t* seqlens;     // [B]
+  const int32_t* cu_q;        // [B + 1]
+  int B, T, stride, num_pages, Hkv, D;
+};
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- decode
 // One work item of the split-KV decode: pages [page_begin, page_end) of
@@ -80,6 +103,12 @@ struct PlanResult {
 int plan_decode_host(const int32_t* seqlens, int B, int stride, int Hkv, int num_splits_request,
                      int num_cus, WorkItem* items, int capacity, int32_t* splits,
                      PlanResult* res);
+
+// Ragged prefill work list: (request, query tile) pairs of kPrefillRows new
+// tokens, sorted by decreasing key count. Returns the item count, or a
+// negative fa_status for inconsistent lengths. `items` may be null.
+int plan_prefill_host(const int32_t* seqlens, const int32_t* cu_q, int B, int32_t* items,
+                      int capacity);
 
 // Workspace layout for a plan: work items, per-request split counts, partials.
 struct WorkspaceLayout {

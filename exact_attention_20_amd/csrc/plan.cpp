@@ -1,4 +1,4 @@
-// Decode plan: split each request's pages into chunks and order the work.
+// Host plans: decode split chunks, and the ragged prefill work order.
 //
 // "FIA / FlashAttention" Q&A, section 2: a plan stage preprocesses the ragged
 // lengths and balances load so that requests of different lengths do not
@@ -146,6 +146,43 @@ int plan_decode_host(const int32_t* seqlens, int B, int stride, int Hkv, int num
     std::copy(list.begin(), list.begin() + n, items);
   }
   return 0;
+}
+
+// Ragged prefill: one item per (request, tile of kPrefillRows new tokens).
+// Every item runs on one workgroup per query head, all of equal cost, so the
+// longest-first order over items is the longest-processing-time order over
+// workgroups. An item's cost is its number of 64-key tiles: the last query
+// row of tile qt is new token min(n, 256 (qt+1)) - 1 at position
+// L - n + that index, and it sees every key up to its own position.
+int plan_prefill_host(const int32_t* seqlens, const int32_t* cu_q, int B, int32_t* items,
+                      int capacity) {
+  if (!seqlens || !cu_q || B < 1 || cu_q[0] != 0) return -1;
+  struct Item {
+    int64_t cost;
+    int32_t b, qt;
+  };
+  std::vector<Item> list;
+  for (int b = 0; b < B; ++b) {
+    const int64_t n = (int64_t)cu_q[b + 1] - cu_q[b];
+    const int64_t L = seqlens[b];
+    if (n < 0 || L < n) return -1;
+    const int64_t ntiles = (n + kPrefillRows - 1) / kPrefillRows;
+    if ((int64_t)list.size() + ntiles > (1 << 26)) return -1;
+    for (int64_t qt = 0; qt < ntiles; ++qt) {
+      const int64_t last = std::min(n, kPrefillRows * (qt + 1)) - 1;
+      const int64_t keys = L - n + last + 1;
+      list.push_back({(keys + kPage - 1) / kPage, b, (int32_t)qt});
+    }
+  }
+  std::stable_sort(list.begin(), list.end(), [](const Item& x, const Item& y) { return x.cost > y.cost; });
+  if (items) {
+    const int n = std::min<int>(capacity, (int)list.size());
+    for (int i = 0; i < n; ++i) {
+      items[2 * i] = list[i].b;
+      items[2 * i + 1] = list[i].qt;
+    }
+  }
+  return (int)list.size();
 }
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

@@ -78,6 +78,7 @@ __device__ __forceinline__ float xor32_sum(float x) {
 }
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(4))) const int32_t const_i32;
 
 // Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each group of 16
 // lanes, lane i receives element (i & 3) of the 8-byte chunks addressed by
@@ -88,7 +89,10 @@ __device__ __forceinline__ uint2 lds_read_tr16(const char* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-template <int NW, int QB>
+// PAGED: ragged paged prefill. Work unit (request, query tile) from the
+// plan's list; the request's new tokens are packed rows [T, Hq, D] of q and
+// out; key tile t is page t of the request's page-table row.
+template <int NW, int QB, bool PAGED>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   constexpr int NT = 64 * NW;                 // threads
@@ -106,32 +110,53 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
 
   // ---- work unit
   const int L = blockIdx.x;
-  const int qt = a.causal ? (n_qtiles - 1 - L / nbh) : (L / nbh);
-  const int e = L % nbh;
-  int b, h, g;
-  if (a.has_map) {
-    b = e / a.Hq;
-    h = e % a.Hq;
-    g = a.kv_map[h];
+  int b, h, g, qt, Sq, Sk, causal;
+  size_t tok0 = 0;  // ragged: packed row of the request's first new token
+  if constexpr (PAGED) {
+    // Items are ordered heaviest first; within one, e enumerates query head
+    // h = g*G + e/Hkv with g = e % Hkv, so workgroups with equal id mod 8
+    // (one XCD) share a KV head when Hq is a multiple of 8.
+    const int item = L / a.Hq, e = L % a.Hq;
+    b = a.items[2 * item];
+    qt = a.items[2 * item + 1];
+    g = e % a.Hkv;
+    h = g * (a.Hq / a.Hkv) + e / a.Hkv;
+    const int c0 = a.cu_q[b];
+    tok0 = (size_t)c0;
+    Sq = a.cu_q[b + 1] - c0;
+    Sk = a.seqlens[b];
+    causal = 1;
   } else {
-    // e = (b*Hkv + g) + B*Hkv*j enumerates query head h = g*G + j, so heads
-    // with equal e % 8 share KV heads when B*Hkv is a multiple of 8.
-    const int G = a.Hq / a.Hkv;
-    const int bg = e % (a.B * a.Hkv);
-    const int j = e / (a.B * a.Hkv);
-    b = bg / a.Hkv;
-    g = bg % a.Hkv;
-    h = g * G + j;
+    qt = a.causal ? (n_qtiles - 1 - L / nbh) : (L / nbh);
+    const int e = L % nbh;
+    if (a.has_map) {
+      b = e / a.Hq;
+      h = e % a.Hq;
+      g = a.kv_map[h];
+    } else {
+      // e = (b*Hkv + g) + B*Hkv*j enumerates query head h = g*G + j, so heads
+      // with equal e % 8 share KV heads when B*Hkv is a multiple of 8.
+      const int G = a.Hq / a.Hkv;
+      const int bg = e % (a.B * a.Hkv);
+      const int j = e / (a.B * a.Hkv);
+      b = bg / a.Hkv;
+      g = bg % a.Hkv;
+      h = g * G + j;
+    }
+    Sq = a.Sq;
+    Sk = a.Sk;
+    causal = a.causal;
   }
   const int q0 = qt * BR;
-  const int off = a.Sk - a.Sq;  // causal: key j visible to query i iff j <= i + off
-  int kend = a.Sk;
-  if (a.causal) kend = min(a.Sk, q0 + BR + off);
+  const int off = Sk - Sq;  // causal: key j visible to query i iff j <= i + off
+  int kend = Sk;
+  if (causal) kend = min(Sk, q0 + BR + off);
   const int n_kt = kend > 0 ? (kend + kBc - 1) / kBc : 0;
 
-  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + h) * (size_t)a.Sq * kD;
-  const uint16_t* K = reinterpret_cast<const uint16_t*>(a.k) + ((size_t)b * a.Hkv + g) * (size_t)a.Sk * kD;
-  const uint16_t* V = reinterpret_cast<const uint16_t*>(a.v) + ((size_t)b * a.Hkv + g) * (size_t)a.Sk * kD;
+  // Query/output rows: contiguous [Sq, D] per head, or packed [T, Hq, D].
+  const size_t row_stride = PAGED ? (size_t)a.Hq * kD : (size_t)kD;
+  const size_t qo_base = PAGED ? (tok0 * a.Hq + h) * kD : ((size_t)b * a.Hq + h) * (size_t)Sq * kD;
+  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + qo_base;
 
   // ---- Q: the B operand of S^T = K Q^T for lane (col, hi) in query block
   // qb is row 32*(QB*wave + qb) + col of the tile, dims 16*kk + 8*hi + 0..7.
@@ -144,7 +169,7 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (r < a.Sq) v = *reinterpret_cast<const uint4*>(Q + (size_t)r * kD + 16 * kk + 8 * hi);
+      if (r < Sq) v = *reinterpret_cast<const uint4*>(Q + (size_t)r * row_stride + 16 * kk + 8 * hi);
       qreg[qb][kk] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
@@ -177,10 +202,31 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   // (l & 15) of row 4j + (l >> 4). K: unit c of row r sits at c ^ (r & 15);
   // V: at c ^ 4*(r & 3); each lane fetches the global unit that belongs in the
   // LDS slot it fills.
-  const __amdgpu_buffer_rsrc_t k_rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(K), (short)0, a.Sk * kRow, 0x00020000);
-  const __amdgpu_buffer_rsrc_t v_rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(V), (short)0, a.Sk * kRow, 0x00020000);
+  //
+  // Contiguous K/V: one buffer resource over the head's Sk rows; loads past
+  // the last key return zeros. Paged: one resource per tile over its page,
+  // bounded by the page's valid rows (zeros past the request's last key, so
+  // stale or NaN tail slots are never read); a page id outside the pool
+  // gives an empty resource (all zeros) instead of a stray access.
+  const size_t kv_base = ((size_t)b * a.Hkv + g) * (size_t)Sk * kD;
+  const __amdgpu_buffer_rsrc_t k_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(a.k) + (PAGED ? 0 : kv_base)), (short)0,
+      PAGED ? 0 : Sk * kRow, 0x00020000);
+  const __amdgpu_buffer_rsrc_t v_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(a.v) + (PAGED ? 0 : kv_base)), (short)0,
+      PAGED ? 0 : Sk * kRow, 0x00020000);
+  // The page table is read-only for the whole kernel, so it is read through
+  // the constant address space: uniform indices then give scalar loads,
+  // which do not wait behind the tile loads in flight.
+  const_i32* ptab = (const_i32*)(a.page_table) + (size_t)b * a.stride;
+  auto page_rsrc = [&](const void* pool, int t) {
+    const int pid = t < a.stride ? ptab[t] : -1;
+    const bool valid = (unsigned)pid < (unsigned)a.num_pages;
+    const char* base = reinterpret_cast<const char*>(pool) +
+                       ((size_t)(valid ? pid : 0) * a.Hkv + g) * (size_t)(kBc * kRow);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0,
+                                             valid ? min(kBc, Sk - t * kBc) * kRow : 0, 0x00020000);
+  };
   const int dl_row = lane >> 4, dl_pos = lane & 15;
   auto load_tile = [&](const __amdgpu_buffer_rsrc_t& rs, int k0, char* buf, bool is_v) {
 #pragma unroll
@@ -192,8 +238,18 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
           rs, (__attribute__((address_space(3))) void*)(buf + j * 1024), 16, (k0 + r) * kRow + unit * 16, 0, 0, 0);
     }
   };
-  auto load_k = [&](int t) { load_tile(k_rs, t * kBc, k_lds + (t & 1) * KBUF, false); };
-  auto load_v = [&](int t) { load_tile(v_rs, t * kBc, v_lds + (t & 1) * VBUF, true); };
+  auto load_k = [&](int t) {
+    if constexpr (PAGED)
+      load_tile(page_rsrc(a.k, t), 0, k_lds + (t & 1) * KBUF, false);
+    else
+      load_tile(k_rs, t * kBc, k_lds + (t & 1) * KBUF, false);
+  };
+  auto load_v = [&](int t) {
+    if constexpr (PAGED)
+      load_tile(page_rsrc(a.v, t), 0, v_lds + (t & 1) * VBUF, true);
+    else
+      load_tile(v_rs, t * kBc, v_lds + (t & 1) * VBUF, true);
+  };
   // This wavefront's direct loads have landed in LDS (the compiler does not
   // track them, so the wait is explicit; the following barrier publishes them).
   auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
@@ -223,7 +279,7 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   }
 
   // Tile t holds work for query block qb unless it lies wholly above its diagonal.
-  auto blk_active = [&](int t, int qb) { return !(a.causal && t * kBc > wq0[qb] + 31 + off); };
+  auto blk_active = [&](int t, int qb) { return !(causal && t * kBc > wq0[qb] + 31 + off); };
   auto any_active = [&](int t) { return blk_active(t, QB - 1); };
 
   // S^T for every query block from K buffer kbuf.
@@ -252,7 +308,7 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   // Causal / ragged-tail mask of tile t's scores for query block qb.
   auto mask = [&](int t, int qb, f32x16_t& s0, f32x16_t& s1) {
     const int k0 = t * kBc;
-    const int lim = a.causal ? min(a.Sk - 1, qrow[qb] + off) : a.Sk - 1;
+    const int lim = causal ? min(Sk - 1, qrow[qb] + off) : Sk - 1;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = k0 + 16 * (i >> 3) + 8 * hi + (i & 7);
@@ -362,8 +418,8 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
 
   // Tiles below the whole workgroup's diagonal and inside Sk need no mask
   // and have work for every query block: they run the branch-free main loop.
-  int n_main = a.Sk / kBc;
-  if (a.causal) n_main = min(n_main, max(0, (q0 + off + 1) / kBc));
+  int n_main = Sk / kBc;
+  if (causal) n_main = min(n_main, max(0, (q0 + off + 1) / kBc));
   n_main = min(n_main, n_kt);
 
   // ---- prologue: K(0), K(1), V(0) in LDS, then S(0).
@@ -433,10 +489,9 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   for (int qb = 0; qb < QB; ++qb) {
     const float lrt = xor32_sum((lr[qb][0] + lr[qb][1]) + (lr[qb][2] + lr[qb][3]));
     const float let_ = xor32_sum((le[qb][0] + le[qb][1]) + (le[qb][2] + le[qb][3]));
-    if (qrow[qb] >= a.Sq) continue;
+    if (qrow[qb] >= Sq) continue;
     const float inv = lrt > 0.f ? 1.f / lrt : 0.f;
-    uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + ((size_t)b * a.Hq + h) * (size_t)a.Sq * kD +
-                  (size_t)qrow[qb] * kD;
+    uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + qo_base + (size_t)qrow[qb] * row_stride;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -446,8 +501,8 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
                                    pack_bf16x2(o[qb][db][4 * gq + 2] * inv, o[qb][db][4 * gq + 3] * inv));
         *reinterpret_cast<uint2*>(O + d) = w;
       }
-    if (hi == 0)
-      a.lse[((size_t)b * a.Hq + h) * a.Sq + qrow[qb]] = let_ > 0.f ? (m[qb] + __log2f(let_)) * kLn2 : kNegInf;
+    const size_t lse_idx = PAGED ? (tok0 + qrow[qb]) * a.Hq + h : ((size_t)b * a.Hq + h) * Sq + qrow[qb];
+    if (hi == 0) a.lse[lse_idx] = let_ > 0.f ? (m[qb] + __log2f(let_)) * kLn2 : kNegInf;
   }
 }
 
@@ -458,7 +513,17 @@ hipError_t launch_cfg(const PrefillArgs& a, hipStream_t s) {
   const int nbh = a.B * a.Hq;
   const long long blocks = (long long)n_qtiles * nbh;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_bf16_kernel<NW, QB>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a, n_qtiles, nbh);
+  hipLaunchKernelGGL((prefill_bf16_kernel<NW, QB, false>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a, n_qtiles, nbh);
+  return hipGetLastError();
+}
+
+template <int NW, int QB>
+hipError_t launch_paged_cfg(const PrefillArgs& a, int n_items, hipStream_t s) {
+  static_assert(32 * NW * QB == kPrefillRows, "the plan's tile height must match the kernel's");
+  const long long blocks = (long long)n_items * a.Hq;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((prefill_bf16_kernel<NW, QB, true>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a, 0, 0);
   return hipGetLastError();
 }
 
@@ -466,6 +531,10 @@ hipError_t launch_cfg(const PrefillArgs& a, hipStream_t s) {
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   return launch_cfg<8, 1>(a, s);
+}
+
+hipError_t launch_prefill_paged_bf16(const PrefillArgs& a, int n_items, hipStream_t s) {
+  return launch_paged_cfg<8, 1>(a, n_items, s);
 }
 
 }  // namespace fa

@@ -1,9 +1,11 @@
 /*
  * fa.h -- C ABI of the MI355X (gfx950) exact-attention library (libfa.so).
  *
- * Exact attention O = softmax(Q K^T / sqrt(d)) V, forward only, in two forms:
+ * Exact attention O = softmax(Q K^T / sqrt(d)) V, forward only, in three forms:
  *   - prefill: every query row of a [B, Hq, Sq, D] block against its KV head,
  *     optionally causal, tiled so the score matrix never reaches HBM;
+ *   - ragged paged prefill: the new tokens of a batch of requests against
+ *     their paged KV caches (after appending their own K/V to the pages);
  *   - paged Flash-Decoding: one query token per request against a KV cache
  *     held in 64-token pages behind a page table, split along the sequence,
  *     partial results merged by their LogSumExp.
@@ -197,6 +199,105 @@ int fa_decode_run(const fa_decode_plan_t* plan, const void* q, const void* k_pag
                   const void* v_pages, const float* k_scale, const float* v_scale,
                   const int32_t* page_table, const int32_t* seqlens, int num_splits, float scale,
                   void* out, float* lse, void* workspace, void* stream);
+
+/*
+ * Ragged prefill over a paged KV cache: append, plan, run.
+ * ("Flash Attention & Paged Attention" blog, "FA and the prefill phase":
+ * prefill attends over the whole prompt and leaves the computed K and V in
+ * device memory as the KV cache that decode reuses; "2. PagedAttention":
+ * that cache lives in fixed-size pages behind a page table; "FIA /
+ * FlashAttention" Q&A, section 2: variable-length batches, a plan step that
+ * preprocesses the lengths and balances the work, then a run step.)
+ *
+ * A batch holds B requests. Request b brings n_b new tokens (n_b >= 0) and
+ * ends up with L_b >= n_b tokens in its cache; the new tokens are the last
+ * n_b of those, at positions L_b - n_b .. L_b - 1, after a cached prefix of
+ * L_b - n_b tokens. The new tokens of all requests are packed along one axis
+ * of T = sum n_b rows in request order:
+ *   cu_seqlens_q  int32 [B + 1], cu[0] = 0, cu[b+1] = cu[b] + n_b
+ *   seqlens       int32 [B], L_b (prefix plus new tokens)
+ * KV pools and page table are laid out as for decode above (pools
+ * [P, Hkv, 64, D] bf16, page_table int32 [B, max_pages_per_req]); entry j of
+ * row b is read for j < ceil(L_b / 64). D = 128 and Hq % Hkv == 0; query
+ * head h reads KV head h / (Hq / Hkv).
+ */
+
+/*
+ * fa_kv_append -- write the new tokens' K and V into their pages.
+ *   k_new, v_new  [T, Hkv, D] bf16, packed as cu_seqlens_q says
+ *   k_pages, v_pages  pools, updated in place: new token i of request b goes
+ *                 to slot t % 64 of page page_table[b][t / 64], t = L_b - n_b + i.
+ *   page_table, seqlens, cu_seqlens_q  DEVICE int32 arrays as above
+ *   B, total_q    requests and T (= cu_seqlens_q[B])
+ * A bit-exact copy; nothing else in the pools changes. Tokens whose page id
+ * lies outside [0, num_pages), whose position is negative (n_b > L_b) or
+ * whose page index reaches max_pages_per_req are skipped, so bad device
+ * metadata cannot make the kernel write outside the pools. One kernel on
+ * `stream`; total_q = 0 is a no-op. Pages shared by several requests'
+ * positions must not be written by two of them in one call.
+ */
+int fa_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                 const int32_t* page_table, const int32_t* seqlens, const int32_t* cu_seqlens_q,
+                 int B, int total_q, int max_pages_per_req, int num_pages, int Hkv, int D,
+                 void* stream);
+
+typedef struct fa_prefill_plan_s fa_prefill_plan_t;
+
+/*
+ * Pure host planning for the ragged prefill (no device, no HIP call).
+ * The work is cut into items (request b, query tile qt) of 256 new tokens
+ * each (the last tile of a request may be shorter; a request with n_b = 0
+ * has none), ordered by decreasing key count so that the longest items
+ * start first. Writes up to `capacity` pairs (b, qt) into items_out (may be
+ * NULL) and returns the number of items, or a negative fa_status when the
+ * lengths are inconsistent (cu not starting at 0 or decreasing, n_b > L_b,
+ * a negative length).
+ */
+int fa_prefill_paged_plan_host(const int32_t* seqlens_host, const int32_t* cu_seqlens_q_host,
+                               int B, int32_t* items_out, int capacity);
+
+/* Bytes of device workspace fa_prefill_paged_plan needs (0 on invalid arguments). */
+size_t fa_prefill_paged_workspace_size(const int32_t* seqlens_host,
+                                       const int32_t* cu_seqlens_q_host, int B);
+
+/*
+ * fa_prefill_paged_plan -- build and upload the work list of a ragged batch.
+ *   seqlens_host, cu_seqlens_q_host  host copies of the batch's lengths
+ *   page_table_host  host int32 [B, max_pages_per_req] or NULL; when given,
+ *                    every entry the run reads is checked to lie in
+ *                    [0, num_pages) (FA_ERR_INVALID_ARGUMENT otherwise).
+ *   Hq, Hkv, D       heads and head size (D = 128, Hq % Hkv == 0, <= 256)
+ *   workspace        device buffer of >= fa_prefill_paged_workspace_size
+ *                    bytes; the work list is uploaded there with one
+ *                    hipMemcpyAsync on `stream` followed by a wait on it.
+ *   plan_out         receives a host plan object (fa_prefill_paged_plan_destroy).
+ */
+int fa_prefill_paged_plan(const int32_t* seqlens_host, const int32_t* cu_seqlens_q_host,
+                          const int32_t* page_table_host, int B, int max_pages_per_req,
+                          int num_pages, int Hq, int Hkv, int D, void* workspace,
+                          size_t workspace_bytes, void* stream, fa_prefill_plan_t** plan_out);
+
+void fa_prefill_paged_plan_destroy(fa_prefill_plan_t* plan);
+
+/*
+ * fa_prefill_paged_run -- causal attention of every new token over its
+ * request's whole cache (prefix and new tokens), one kernel on `stream`, no
+ * allocation and no host synchronisation.
+ *   q            [T, Hq, D] bf16, packed new tokens
+ *   k_pages, v_pages  pools already holding all L_b tokens of every request
+ *                (call fa_kv_append first for the new ones)
+ *   page_table, seqlens, cu_seqlens_q  device copies of what the plan saw
+ *   scale        score multiplier; <= 0 selects 1/sqrt(D)
+ *   out          [T, Hq, D] bf16, written (rounded to nearest even)
+ *   lse          [T, Hq] fp32 natural-log LSE, written
+ * New token i of request b sees keys 0 .. L_b - n_b + i: the causal mask
+ * aligned bottom-right, as in fa_prefill_fwd with Sq = n_b, Sk = L_b.
+ * Page ids outside [0, num_pages) read as zeros (never out of bounds).
+ */
+int fa_prefill_paged_run(const fa_prefill_plan_t* plan, const void* q, const void* k_pages,
+                         const void* v_pages, const int32_t* page_table, const int32_t* seqlens,
+                         const int32_t* cu_seqlens_q, float scale, void* out, float* lse,
+                         void* workspace, void* stream);
 
 /*
  * fa_debug_gather_kv -- copy the L_b logical tokens of one request and KV

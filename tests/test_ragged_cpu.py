@@ -1,0 +1,159 @@
+"""Ragged paged prefill and KV append on the CPU: the header, the host plan,
+argument checks that reject before any device work, and the input generator.
+
+No test here launches a kernel.
+"""
+import ctypes as C
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_20_amd as fa
+import oracle
+import workloads
+
+from test_abi_cpu import declared_functions
+
+I32P = C.POINTER(C.c_int32)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.lib_path()):
+        pytest.skip("libfa.so not built")
+    return fa.load()
+
+
+def _arr(x):
+    a = (C.c_int32 * len(x))(*x)
+    return C.cast(a, I32P), a
+
+
+def test_header_declares_ragged_calls():
+    names = declared_functions()
+    for n in ("fa_kv_append", "fa_prefill_paged_plan", "fa_prefill_paged_run",
+              "fa_prefill_paged_plan_destroy", "fa_prefill_paged_plan_host",
+              "fa_prefill_paged_workspace_size"):
+        assert n in names
+
+
+def _expected_items(L, nq):
+    """(cost, b, qt) for every query tile, cost = 64-key tiles its last row reaches."""
+    out = []
+    for b, (Lb, n) in enumerate(zip(L, nq)):
+        for qt in range((n + 255) // 256):
+            last = min(n, 256 * (qt + 1)) - 1
+            keys = Lb - n + last + 1
+            out.append(((keys + 63) // 64, b, qt))
+    return out
+
+
+@pytest.mark.parametrize("nq,pre", [
+    ([1], [0]), ([256], [0]), ([257], [5]), ([0, 3, 0], [7, 0, 0]),
+    ([1053, 1220, 1, 64, 65, 300], [7393, 0, 15000, 64, 63, 1]),
+])
+def test_plan_covers_every_tile_longest_first(lib, nq, pre):
+    L = [a + b for a, b in zip(nq, pre)]
+    cu = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    items = fa.fa_prefill_paged_plan_host(L, cu).numpy()
+    exp = _expected_items(L, nq)
+    assert sorted(map(tuple, items)) == sorted((b, qt) for _, b, qt in exp)
+    cost = {(b, qt): c for c, b, qt in exp}
+    seq = [cost[(int(b), int(qt))] for b, qt in items]
+    assert seq == sorted(seq, reverse=True), "items must be ordered by decreasing key tiles"
+
+
+def test_plan_workload6(lib):
+    w = workloads.WORKLOADS[6]
+    nq = workloads.context_lengths(w.wid, w.B, w.new_lens)
+    pre = workloads.context_lengths(w.wid, w.B, w.prefix_lens, workloads.STREAM_PREFIX)
+    cu = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    items = fa.fa_prefill_paged_plan_host(pre + nq, cu)
+    assert len(items) == sum((int(n) + 255) // 256 for n in nq)
+    assert fa.fa_prefill_paged_workspace_size(pre + nq, cu) >= 8 * len(items)
+
+
+@pytest.mark.parametrize("L,cu", [
+    ([5], [1, 3]),          # cu[0] != 0
+    ([5, 5], [0, 3, 2]),    # decreasing offsets
+    ([2], [0, 3]),          # more new tokens than the cache holds
+    ([-1], [0, 0]),         # negative length
+])
+def test_plan_host_rejects_inconsistent_lengths(lib, L, cu):
+    (lp, la), (cp, ca) = _arr(L), _arr(cu)
+    assert lib.fa_prefill_paged_plan_host(lp, cp, len(L), None, 0) == -1
+    assert lib.fa_prefill_paged_workspace_size(lp, cp, len(L)) == 0
+
+
+def _plan(lib, **kw):
+    a = dict(L=[70, 3], cu=[0, 6, 9], table=[0, 1, 2, -1], B=2, stride=2, P=3, Hq=4, Hkv=2, D=128,
+             ws=C.c_void_p(256), ws_bytes=1 << 20)
+    a.update(kw)
+    (lp, la), (cp, ca), (tp, ta) = _arr(a["L"]), _arr(a["cu"]), _arr(a["table"])
+    h = C.c_void_p()
+    st = lib.fa_prefill_paged_plan(lp, cp, tp, a["B"], a["stride"], a["P"], a["Hq"], a["Hkv"], a["D"],
+                                   a["ws"], a["ws_bytes"], None, C.byref(h))
+    assert not h.value
+    return st
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), 1), (dict(Hq=3), 1), (dict(Hq=300, Hkv=300), 2), (dict(D=64), 2),
+    (dict(stride=0), 1), (dict(P=0), 1), (dict(cu=[0, 6, 5]), 1), (dict(L=[5, 3]), 1),
+    (dict(table=[0, 7, 2, -1]), 1),          # page id outside the pool
+    (dict(L=[200, 3], cu=[0, 6, 9]), 1),     # needs 4 pages > stride 2
+    (dict(ws=None), 3), (dict(ws_bytes=8), 3),
+])
+def test_paged_plan_rejects_before_device_work(lib, kw, code):
+    assert _plan(lib, **kw) == code
+    assert lib.fa_last_error().decode()
+
+
+def test_paged_run_rejects_null_plan(lib):
+    assert lib.fa_prefill_paged_run(None, *([C.c_void_p(16)] * 6), C.c_float(0.0),
+                                    *([C.c_void_p(16)] * 4)) == 1
+
+
+def _append(lib, **kw):
+    p = C.c_void_p(16)
+    a = dict(k_new=p, v_new=p, k_pages=p, v_pages=p, table=p, seqlens=p, cu=p, B=2, T=9, stride=2,
+             P=3, Hkv=2, D=128)
+    a.update(kw)
+    return lib.fa_kv_append(a["k_new"], a["v_new"], a["k_pages"], a["v_pages"], a["table"],
+                            a["seqlens"], a["cu"], a["B"], a["T"], a["stride"], a["P"], a["Hkv"],
+                            a["D"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), 1), (dict(Hkv=0), 1), (dict(T=-1), 1), (dict(stride=0), 1), (dict(P=0), 1),
+    (dict(D=64), 2), (dict(k_new=None), 1), (dict(v_pages=None), 1), (dict(cu=None), 1),
+])
+def test_append_rejects(lib, kw, code):
+    assert _append(lib, **kw) == code
+
+
+def test_append_empty_is_noop(lib):
+    assert _append(lib, T=0, k_new=None, v_new=None) == 0
+
+
+def test_generator_poisons_exactly_the_new_slots():
+    """NaN sits at every new token's slot and every tail slot, nowhere else; the
+    oracle's append fills every slot a request reads."""
+    nq, pre = np.array([0, 3, 70, 64, 1]), np.array([9, 0, 60, 128, 63])
+    r = workloads.ragged_inputs(4, 2, 8, nq, pre, wid=40)
+    L = r.seqlens.numpy()
+    table = r.page_table.numpy()
+    nan = torch.isnan(r.k_pages.float()).all(dim=3).all(dim=1).numpy()  # [P, 64]
+    expect = np.zeros_like(nan)
+    for b in range(len(L)):
+        for t in range(pre[b], (L[b] + 63) // 64 * 64):
+            expect[table[b, t // 64], t % 64] = True
+    assert np.array_equal(nan, expect)
+    kp, vp = oracle.kv_append(r.k_pages.float().numpy(), r.v_pages.float().numpy(), table, L,
+                              r.cu_seqlens_q.numpy(), r.k_new.float().numpy(), r.v_new.float().numpy())
+    for b in range(len(L)):
+        for g in range(2):
+            assert np.isfinite(oracle.gather_pages(kp, table[b], int(L[b]), g)).all()
+            assert np.isfinite(oracle.gather_pages(vp, table[b], int(L[b]), g)).all()
