@@ -1,7 +1,8 @@
 """Benchmark of the exact-attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--prewarm-s S] [--no-cpu-baseline]
-                    [--only prefill|decode] [--prefill-workload 2|3] [--decode-workload 4|5]
+                    [--only prefill|decode|ragged|copy] [--prefill-workload 2|3]
+                    [--decode-workload 4|5]
 
 One step = one pass of the whole path over one synthetic batch:
   * prefill: fa_prefill_fwd on the causal bf16 workload (default: B=4, 32 heads,
@@ -9,7 +10,11 @@ One step = one pass of the whole path over one synthetic batch:
   * decode: fa_decode_run (split-KV kernel + LSE merge) on the paged bf16
     workload (default: 64 requests, 32/8 heads, lengths U[512, 16384]),
     planned once beforehand (the host plan is timed separately and reported).
-Inputs are resident in HBM before timing. Each leg first runs untimed for
+A third leg, reported as its own ``ragged_prefill`` object and not part of
+the step, measures the ragged paged prefill: fa_kv_append of 16 requests'
+new tokens (256..2048 each) into their paged caches, then fa_prefill_paged_run
+of those tokens over prefix + new keys (prefixes 0..16384), each timed on
+its own. Inputs are resident in HBM before timing. Each leg first runs untimed for
 --prewarm-s seconds (default 1 s: GPU clocks and power reach steady state)
 and --warmup more times; each timed call is then bracketed by HIP events on
 the stream it runs on, and the step time is the sum of the legs' means.
@@ -64,6 +69,32 @@ def decode_bytes(L, w):
     b += w.B * w.Hq * 4                               # lse
     b += int(pages.sum()) * 4 + w.B * 4               # page-table entries read, seqlens
     return b
+
+
+def ragged_flops(nq, pre, w):
+    """Causal score/value FLOPs of a ragged batch: new token i of a request
+    with prefix p sees p + i + 1 keys; 4 D FLOPs per (query, key, head)."""
+    tot = 0
+    for n, p in zip(nq, pre):
+        n, p = int(n), int(p)
+        tot += n * p + n * (n + 1) // 2
+    return 4.0 * w.Hq * w.D * tot
+
+
+def ragged_bytes(nq, pre, w):
+    """Algorithmic HBM bytes of one paged prefill launch: Q read and O written
+    once (bf16), LSE written (fp32), every cached K/V row of each request read
+    once (bf16), page-table entries and lengths read."""
+    import numpy as np
+    nq, pre = np.asarray(nq, np.int64), np.asarray(pre, np.int64)
+    T, L = int(nq.sum()), nq + pre
+    return (2 * T * w.Hq * w.D * 2 + 4 * T * w.Hq + int(L.sum()) * w.Hkv * w.D * 2 * 2
+            + int(((L + 63) // 64).sum()) * 4 + 8 * len(L))
+
+
+def append_bytes(nq, w):
+    """HBM bytes of one KV append: new K and V rows read once and written once."""
+    return 4 * int(sum(int(n) for n in nq)) * w.Hkv * w.D * 2
 
 
 def source_sha(rel):
@@ -179,6 +210,42 @@ def cpu_baseline_decode(w, kv, budget_s=10.0):
                       f"fp64 numpy, BLAS 1 thread per worker"}
 
 
+def cpu_baseline_ragged(w, r, budget_s=10.0):
+    """fp64 oracle on 64-row blocks of the ragged batch's requests (all heads), threads over blocks."""
+    import concurrent.futures as cf
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    kp, vp = oracle.kv_append(r.k_pages.float().numpy(), r.v_pages.float().numpy(), r.page_table.numpy(),
+                              r.seqlens.numpy(), r.cu_seqlens_q.numpy(), r.k_new.float().numpy(),
+                              r.v_new.float().numpy())
+    q = r.q.double().numpy()
+    L, cu, pt = r.seqlens.numpy(), r.cu_seqlens_q.numpy(), r.page_table.numpy()
+    jobs = [(b, s) for b in range(w.B) for s in range(0, int(cu[b + 1] - cu[b]), 64)]
+    jobs = [jobs[i] for i in np.random.default_rng(0).permutation(len(jobs))]
+
+    def one(job):
+        b, s = job
+        n = int(cu[b + 1] - cu[b])
+        rows = np.arange(s, min(n, s + 64))
+        oracle.paged_prefill_request(q[cu[b]:cu[b + 1]], kp, vp, pt[b], int(L[b]), w.scale, rows)
+        return 4.0 * w.Hq * w.D * float(np.sum(int(L[b]) - n + rows + 1))
+
+    done, flops = 0, 0.0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1), cf.ThreadPoolExecutor(cores) as ex:
+        while done < len(jobs) and time.perf_counter() - t0 < budget_s:
+            batch = jobs[done:done + cores]
+            flops += sum(ex.map(one, batch))
+            done += len(batch)
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {len(jobs)} random 64-row blocks (all heads, all visible keys) of the "
+                      f"ragged prefill workload, {dt:.1f} s wall, fp64 numpy, BLAS 1 thread per worker"}
+
+
 COPY_BYTES = 1 << 30   # calibration copy: bytes read, and bytes written, per launch
 
 
@@ -211,6 +278,8 @@ PMC_LEGS = {
                          "exact_attention_20_amd/csrc/prefill_bf16.hip"),
     "decode_wl4": ("--only decode --decode-workload 4", ["decode_mfma_kernel", "lse_merge_kernel"], DECODE_SRC),
     "decode_wl5": ("--only decode --decode-workload 5", ["decode_mfma_kernel", "lse_merge_kernel"], DECODE_SRC),
+    "ragged_prefill_wl6": ("--only ragged", ["prefill_bf16_kernel"],
+                           "exact_attention_20_amd/csrc/prefill_bf16.hip"),
     "copy": ("--only copy", ["neg"], None),
 }
 PMC_RUN = "--steps 3 --warmup 1 --prewarm-s 0 --no-cpu-baseline"
@@ -275,6 +344,9 @@ def summarize_profiles(d):
         w = workloads.WORKLOADS[wid]
         if leg.startswith("prefill"):
             alg = prefill_bytes(w)
+        elif leg.startswith("ragged"):
+            alg = ragged_bytes(workloads.context_lengths(wid, w.B, w.new_lens),
+                               workloads.context_lengths(wid, w.B, w.prefix_lens, workloads.STREAM_PREFIX), w)
         else:
             alg = decode_bytes(workloads.context_lengths(wid, w.B, w.lengths), w)
         fb, wb = fk * 1024.0 * f_scale, wk * 1024.0 * w_scale
@@ -336,7 +408,7 @@ def main():
     ap.add_argument("--prewarm-s", type=float, default=1.0,
                     help="seconds of untimed steps before the warmup steps (GPU clock ramp-up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "ragged", "copy"], default=None)
     ap.add_argument("--prefill-workload", type=int, default=2, choices=[2, 3])
     ap.add_argument("--decode-workload", type=int, default=4, choices=[4, 5])
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
@@ -423,6 +495,33 @@ def main():
         res["decode_cpu"] = None if args.no_cpu_baseline else cpu_baseline_decode(wd, kv)
         del d, pools
 
+    if args.only in (None, "ragged"):
+        wr = workloads.WORKLOADS[6]
+        log(f"[bench] generating ragged prefill workload {wr.name}")
+        r = workloads.workload_ragged_inputs(wr)
+        d = dict(q=r.q.cuda(), kn=r.k_new.cuda(), vn=r.v_new.cuda(), k=r.k_pages.cuda(), v=r.v_pages.cuda(),
+                 pt=r.page_table.cuda(), sl=r.seqlens.cuda(), cu=r.cu_seqlens_q.cuda())
+        t0 = time.perf_counter()
+        plan = fa.fa_prefill_paged_plan(r.seqlens, r.cu_seqlens_q, r.page_table, r.num_pages, wr.Hq, wr.Hkv)
+        plan_ms = (time.perf_counter() - t0) * 1e3
+        out = torch.empty_like(d["q"])
+        lse = torch.empty(d["q"].shape[:2], dtype=torch.float32, device=d["q"].device)
+        app = lambda: fa.fa_kv_append(d["kn"], d["vn"], d["k"], d["v"], d["pt"], d["sl"], d["cu"], stream)  # noqa: E731
+        run = lambda: fa.fa_prefill_paged_run(plan, d["q"], d["k"], d["v"], d["pt"], d["sl"], d["cu"],  # noqa: E731
+                                              out, lse, wr.scale, stream)
+        t_app = time_calls(app, args.steps, args.warmup, stream, min(args.prewarm_s, 0.3))
+        t_run = time_calls(run, args.steps, args.warmup, stream, args.prewarm_s)
+        nq = (r.cu_seqlens_q[1:] - r.cu_seqlens_q[:-1]).numpy()
+        pre = r.seqlens.numpy() - nq
+        res["ragged"] = dict(app=t_app, run=t_run, flops=ragged_flops(nq, pre, wr),
+                             bytes=ragged_bytes(nq, pre, wr), app_bytes=append_bytes(nq, wr),
+                             plan=dict(plan_ms=round(plan_ms, 3), items=plan.n_items, pages=int(r.num_pages),
+                                       tokens=int(nq.sum())), w=wr)
+        log(f"[bench] ragged append median {statistics.median(t_app):.4f} ms, "
+            f"prefill median {statistics.median(t_run):.4f} ms")
+        res["ragged_cpu"] = None if args.no_cpu_baseline else cpu_baseline_ragged(wr, r)
+        del d
+
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic"}
@@ -458,9 +557,40 @@ def main():
             line.update(value=dec["value"], unit="GB/s")
             line["roofline"] = dec["roofline"]
             line["cpu_baseline"] = dec["cpu_baseline"]
+    if "ragged" in res:
+        g = res["ragged"]
+        wr = g["w"]
+        t_run, t_app = statistics.mean(g["run"]), statistics.mean(g["app"])
+        tf = g["flops"] / (t_run * 1e-3) / 1e12
+        app_gbs = g["app_bytes"] / (t_app * 1e-3) / 1e9
+        rag = {"metric": "ragged paged causal prefill TFLOP/s (KV append timed separately)",
+               "value": round(tf, 2), "unit": "TFLOP/s",
+               "ms_mean": round(t_run, 5), "ms_median": round(statistics.median(g["run"]), 5),
+               "tflops_incl_append": round(g["flops"] / ((t_run + t_app) * 1e-3) / 1e12, 2),
+               "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                            "traffic": read_traffic("ragged_prefill_wl6_traffic.txt",
+                                                    "exact_attention_20_amd/csrc/prefill_bf16.hip"),
+                            "kernel": "prefill_bf16_kernel (paged)", "flops_per_launch": g["flops"],
+                            "algorithmic_bytes_per_launch": g["bytes"]},
+               "append": {"ms_mean": round(t_app, 5), "value": round(app_gbs, 1), "unit": "GB/s",
+                          "roofline": {"bound": "hbm", "achieved": round(app_gbs, 1), "peak": PEAK_HBM_GBS,
+                                       "unit": "GB/s", "frac": round(app_gbs / PEAK_HBM_GBS, 4),
+                                       "kernel": "kv_append_kernel", "bytes_per_launch": g["app_bytes"]}},
+               "plan": g["plan"], "cpu_baseline": res["ragged_cpu"],
+               "config": {"workload": wr.name, "B": wr.B, "Hq": wr.Hq, "Hkv": wr.Hkv, "D": wr.D,
+                          "new_tokens": list(wr.new_lens), "prefix": list(wr.prefix_lens), "page": 64}}
+        line["ragged_prefill"] = rag
+        if "value" not in line:
+            line.update(value=rag["value"], unit="TFLOP/s")
+            line["roofline"] = rag["roofline"]
+            line["cpu_baseline"] = rag["cpu_baseline"]
+            ms_step = t_run + t_app
     line["ms_per_step"] = round(ms_step, 5)
     cfg = {"workload": " + ".join(
-        ([wp.name] if "prefill_ms" in res else []) + ([wd.name] if "decode_ms" in res else []))}
+        ([wp.name] if "prefill_ms" in res else []) + ([wd.name] if "decode_ms" in res else [])
+        + ([res["ragged"]["w"].name] if "ragged" in res and "prefill_ms" not in res
+           and "decode_ms" not in res else []))}
     if "prefill_ms" in res:
         cfg["prefill"] = dict(B=wp.B, Hq=wp.Hq, Hkv=wp.Hkv, S=wp.S, D=wp.D, causal=True, dtype="bf16")
     if "decode_ms" in res:
