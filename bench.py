@@ -373,7 +373,7 @@ def summarize_profiles(d):
     kt = glob.glob(f"{d}/kt/*kernel_stats.csv")
     if kt:
         rows = list(csv.DictReader(open(kt[0])))
-        lines = ["# rocprofv3 --kernel-trace --stats of the default bench run (one process, both legs).",
+        lines = ["# rocprofv3 --kernel-trace --stats of the default bench run (one process, all legs).",
                  *header[:2], f"#   python3 bench.py --summarize-profiles {d}",
                  "# kernel | calls | average us | min us | max us | total ms | % of GPU time"]
         for r in rows:
@@ -392,6 +392,10 @@ def summarize_profiles(d):
                 lines.append(f"bench prefill launch_ms_mean: {b['roofline'].get('launch_ms_mean')}")
                 if "decode" in b:
                     lines.append(f"bench decode step ms_mean: {b['decode'].get('ms_mean')}")
+                if "ragged_prefill" in b:
+                    rg = b["ragged_prefill"]
+                    lines.append(f"bench ragged paged prefill launch ms_mean: {rg.get('ms_mean')}")
+                    lines.append(f"bench kv append launch ms_mean: {rg['append'].get('ms_mean')}")
                 lines.append(f"bench value: {b['value']} {b['unit']}")
         path = os.path.join(out_dir, "kernel_trace_bench.txt")
         open(path, "w").write("\n".join(lines) + "\n")
