@@ -44,6 +44,8 @@
 //    the heaviest query tiles (most keys) are issued first. Heads are ordered
 //    so that workgroups with equal id mod 8 -- which the dispatcher places on
 //    the same XCD -- share a KV head, keeping its K/V in that XCD's L2.
+#include <type_traits>
+
 #include "fa_internal.h"
 #include "hip_common.h"
 
@@ -65,6 +67,10 @@ __device__ __forceinline__ int kperm(int r) {
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// The same with a zero accumulator (an inline constant: nothing to clear).
+__device__ __forceinline__ f32x16_t mfma32_first(bf16x8_t a, bf16x8_t b) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, f32x16_t{}, 0, 0, 0);
 }
 
 // x combined with the value of lane ^ 32 (both halves get the result).
@@ -286,21 +292,14 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   auto qk = [&](int kbuf, f32x16_t (&s)[QB][2]) {
     const char* kl = k_lds + kbuf * KBUF;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[qb][0][i] = 0.f;
-        s[qb][1][i] = 0.f;
-      }
-#pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(kl + k_off[kk]);
       const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(kl + k_off[kk] + 32 * kRow);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const bf16x8_t qf = qreg[qb][kk];
-        s[qb][0] = mfma32(a0, qf, s[qb][0]);
-        s[qb][1] = mfma32(a1, qf, s[qb][1]);
+        s[qb][0] = kk == 0 ? mfma32_first(a0, qf) : mfma32(a0, qf, s[qb][0]);
+        s[qb][1] = kk == 0 ? mfma32_first(a1, qf) : mfma32(a1, qf, s[qb][1]);
       }
     }
   };
@@ -327,7 +326,11 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
     mx = xor32_max(mx);
     const float mxs = mx * c;
     const bool need = mxs > m[qb] + kTau;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+      // Rarely taken once the max has settled: kept as a branch (the empty
+      // volatile asm stops the compiler from turning it into unconditional
+      // multiplies by alpha = 1).
+      asm volatile("");
       const float mn = need ? mxs : m[qb];
       const float alpha = need ? fast_exp2(m[qb] - mn) : 1.f;
 #pragma unroll
@@ -355,15 +358,6 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
     for (int qb = 0; qb < QB; ++qb) mu[qb] = (m[qb] == kNegInf) ? 0.f : m[qb];
     const char* vl = v_lds + vbuf * VBUF;
     const char* kl = k_lds + (kb < 0 ? 0 : kb) * KBUF;
-    if (kb >= 0) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          n[qb][0][i] = 0.f;
-          n[qb][1][i] = 0.f;
-        }
-    }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       bf16x8_t pf[QB];
@@ -401,8 +395,8 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
             const bf16x8_t qf = qreg[qb][kk];
-            n[qb][0] = mfma32(a0, qf, n[qb][0]);
-            n[qb][1] = mfma32(a1, qf, n[qb][1]);
+            n[qb][0] = kk == 0 ? mfma32_first(a0, qf) : mfma32(a0, qf, n[qb][0]);
+            n[qb][1] = kk == 0 ? mfma32_first(a1, qf) : mfma32(a1, qf, n[qb][1]);
           }
         }
       }
@@ -437,22 +431,38 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   bool all[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) all[qb] = true;
-  int t = 0;
-  for (; t < n_main; ++t) {
-    f32x16_t sn[QB][2];
+  // One tile of the main loop with buffer parity PAR known at compile time
+  // (LDS offsets become immediates); the scores of tile t arrive in `cur`
+  // and those of tile t+1 leave in `nxt`. The next tile's scores are
+  // computed even past the last tile (from a stale buffer, then discarded)
+  // to keep this block free of branches.
+  auto main_step = [&](auto par, int t, f32x16_t (&cur)[QB][2], f32x16_t (&nxt)[QB][2]) {
+    constexpr int PAR = decltype(par)::value;
     prefetch(t);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) update_max(qb, sc[qb][0], sc[qb][1]);
-    // The next tile's scores are computed even past the last tile (from a
-    // stale buffer, then discarded) to keep this block free of branches.
-    exp_pv_qk(t & 1, sc, all, (t + 1) & 1, sn);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      sc[qb][0] = sn[qb][0];
-      sc[qb][1] = sn[qb][1];
-    }
+    for (int qb = 0; qb < QB; ++qb) update_max(qb, cur[qb][0], cur[qb][1]);
+    exp_pv_qk(PAR, cur, all, 1 - PAR, nxt);
     wait_loads();
     __syncthreads();
+  };
+  // Unrolled by two so the two score arrays swap roles instead of being
+  // copied, and t starts at 0, so tile t uses buffer t & 1 = its position.
+  int t = 0;
+  {
+    f32x16_t sn[QB][2];
+    for (; t + 1 < n_main; t += 2) {
+      main_step(std::integral_constant<int, 0>{}, t, sc, sn);
+      main_step(std::integral_constant<int, 1>{}, t + 1, sn, sc);
+    }
+    if (t < n_main) {
+      main_step(std::integral_constant<int, 0>{}, t, sc, sn);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        sc[qb][0] = sn[qb][0];
+        sc[qb][1] = sn[qb][1];
+      }
+      ++t;
+    }
   }
   for (; t < n_kt; ++t) {
     f32x16_t sn[QB][2];
