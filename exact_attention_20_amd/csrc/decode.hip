@@ -394,48 +394,61 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(DecodeArgs a) {
   __shared__ float s_max[4], s_tot[4];
   __shared__ float2 s_o[4][kD / 2];
 
-  float M = kNegInf;
-  for (int i = threadIdx.x; i < n; i += 256) M = fmaxf(M, plse[i]);
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, shfl_xor_f32(M, o));
-  if (lane == 0) s_max[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
-
+  // Each wavefront merges a contiguous quarter of the splits on its own,
+  // loading the LSEs and partial outputs of up to 8 splits together (one
+  // memory round trip per 8 splits) and keeping a running max M, weight
+  // sum and weighted output; the four states are then merged the same way.
   const int per = (n + 3) / 4;
   const int s0 = min(n, wave * per), s1 = min(n, s0 + per);
-  float tot = 0.f, o0 = 0.f, o1 = 0.f;
-  if (M != kNegInf) {
-    for (int i = s0; i < s1; i += 8) {
-      float w[8];
-      float2 x[8];
+  float M = kNegInf, tot = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int i = s0; i < s1; i += 8) {
+    float w[8];
+    float2 x[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool ok = i + j < s1;
-        const int sj = ok ? i + j : s0;  // past the range: a real split with weight 0
-        w[j] = ok ? plse[sj] : kNegInf;
-        x[j] = *reinterpret_cast<const float2*>(po + (size_t)sj * kD + 2 * lane);
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float wj = fast_exp2((w[j] - M) * kLog2e);
-        tot += wj;
-        o0 += wj * x[j].x;
-        o1 += wj * x[j].y;
-      }
+    for (int j = 0; j < 8; ++j) {
+      const bool ok = i + j < s1;
+      const int sj = ok ? i + j : s0;  // past the range: a real split with weight 0
+      w[j] = ok ? plse[sj] : kNegInf;
+      x[j] = *reinterpret_cast<const float2*>(po + (size_t)sj * kD + 2 * lane);
     }
+    float mc = M;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mc = fmaxf(mc, w[j]);
+    if (mc == kNegInf) continue;  // only empty splits so far (uniform)
+    const float r = fast_exp2((M - mc) * kLog2e);  // 0 when M = -inf
+    tot *= r;
+    o0 *= r;
+    o1 *= r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float wj = fast_exp2((w[j] - mc) * kLog2e);
+      tot += wj;
+      o0 += wj * x[j].x;
+      o1 += wj * x[j].y;
+    }
+    M = mc;
   }
   s_o[wave][lane] = make_float2(o0, o1);
-  if (lane == 0) s_tot[wave] = tot;
+  if (lane == 0) {
+    s_max[wave] = M;
+    s_tot[wave] = tot;
+  }
   __syncthreads();
   if (wave == 0) {
-    const float T = (s_tot[0] + s_tot[1]) + (s_tot[2] + s_tot[3]);
-    const float2 a0 = s_o[0][lane], a1 = s_o[1][lane], a2 = s_o[2][lane], a3 = s_o[3][lane];
+    const float Mx = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+    float T = 0.f, r0 = 0.f, r1 = 0.f;
+    if (Mx != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = s_max[w] == kNegInf ? 0.f : fast_exp2((s_max[w] - Mx) * kLog2e);
+        T += s_tot[w] * f;
+        r0 += s_o[w][lane].x * f;
+        r1 += s_o[w][lane].y * f;
+      }
+    }
     const float inv = T > 0.f ? 1.f / T : 0.f;
-    const float r0 = ((a0.x + a1.x) + (a2.x + a3.x)) * inv;
-    const float r1 = ((a0.y + a1.y) + (a2.y + a3.y)) * inv;
-    reinterpret_cast<uint32_t*>(a.out)[(size_t)bh * (kD / 2) + lane] = pack_bf16x2(r0, r1);
-    if (lane == 0) a.lse[bh] = T > 0.f ? M + __logf(T) : kNegInf;
+    reinterpret_cast<uint32_t*>(a.out)[(size_t)bh * (kD / 2) + lane] = pack_bf16x2(r0 * inv, r1 * inv);
+    if (lane == 0) a.lse[bh] = T > 0.f ? Mx + __logf(T) : kNegInf;
   }
 }
 
