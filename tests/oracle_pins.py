@@ -502,4 +502,47 @@ def pin_paged_prefill_reductions():
     _close(LSE[last], dl, 1e-12, "last token == decode LSE")
 
 
+def pin_shared_prefix_cascade():
+    """Cascade decomposition: for requests sharing prefix pages, attention over
+    the prefix (gathered once per group) and over each request's own suffix,
+    merged by LSE, equals decode over the whole cache; an empty suffix merges
+    as a split with LSE = -inf."""
+    g = _rng(24)
+    Hq, Hkv, D = 4, 2, 8
+    pp = [2, 1]
+    groups = [0, 0, -1, 1, 0]
+    suffix = [0, 70, 5, 64, 130]
+    P = sum(pp) + sum((x + 63) // 64 for x in suffix) + 1
+    kp = g.standard_normal((P, Hkv, 64, D))
+    vp = g.standard_normal((P, Hkv, 64, D))
+    perm = g.permutation(P)
+    pre_ids = [list(perm[:2]), list(perm[2:3])]
+    nxt = 3
+    table = np.full((5, 6), -1)
+    L = np.zeros(5, dtype=np.int64)
+    for b in range(5):
+        row = list(pre_ids[groups[b]]) if groups[b] >= 0 else []
+        n_own = (suffix[b] + 63) // 64
+        row += list(perm[nxt:nxt + n_own])
+        nxt += n_own
+        table[b, :len(row)] = row
+        L[b] = (64 * pp[groups[b]] if groups[b] >= 0 else 0) + suffix[b]
+    q = g.standard_normal((5, Hq, D))
+    O, LSE = A.paged_decode(q, kp, vp, table, L, 0.35)
+    for b in range(5):
+        P_tok = 64 * pp[groups[b]] if groups[b] >= 0 else 0
+        for h in range(Hq):
+            gg = h // (Hq // Hkv)
+            kb = A.gather_pages(kp, table[b], int(L[b]), gg)
+            vb = A.gather_pages(vp, table[b], int(L[b]), gg)
+            parts_o, parts_l = [], []
+            for lo, hi in ((0, P_tok), (P_tok, int(L[b]))):
+                o, l = A.attention_head(q[b, h][None], kb[lo:hi], vb[lo:hi], 0.35)
+                parts_o.append(o[0])
+                parts_l.append(l[0])
+            mo, ml = A.lse_merge(np.array(parts_o), np.array(parts_l))
+            _close(mo, O[b, h], 1e-12, f"cascade O b={b} h={h}")
+            _close(ml, LSE[b, h], 1e-12, f"cascade LSE b={b} h={h}")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -97,6 +97,31 @@ class RaggedPrefillWorkload:
         return float(np.float32(1.0 / math.sqrt(self.D)))
 
 
+@dataclass(frozen=True)
+class SharedPrefixWorkload:
+    """Decode requests in groups that share a prefix of whole pages.
+
+    ``group_sizes[j]`` requests share a prefix of ``prefix_pages[j]`` pages;
+    every request then has its own suffix (length spec ``suffix_lens``).
+    """
+    wid: int
+    name: str
+    Hq: int
+    Hkv: int
+    D: int
+    group_sizes: tuple
+    prefix_pages: tuple
+    suffix_lens: tuple
+
+    @property
+    def B(self):
+        return sum(self.group_sizes)
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.D)))
+
+
 WORKLOADS = {
     1: PrefillWorkload(1, "tiny_fp32_b1_h2_s128_d64", 1, 2, 2, 128, 64, "f32", (False, True)),
     2: PrefillWorkload(2, "causal_prefill_bf16_b4_h32_s4096_d128", 4, 32, 32, 4096, 128, "bf16", (True,)),
@@ -107,6 +132,8 @@ WORKLOADS = {
                       ("loguniform", 4096, 131072)),
     6: RaggedPrefillWorkload(6, "ragged_paged_prefill_bf16_b16_hq32_hkv8_d128_new256-2048_prefix0-16384",
                              16, 32, 8, 128, ("uniform", 256, 2048), ("uniform", 0, 16384)),
+    7: SharedPrefixWorkload(7, "shared_prefix_decode_bf16_b64_hq32_hkv8_d128_prefix8192_suffix256-4096",
+                            32, 8, 128, (64,), (128,), ("uniform", 256, 4096)),
 }
 
 
@@ -337,3 +364,76 @@ def workload_ragged_inputs(w: RaggedPrefillWorkload, poison=True) -> RaggedPaged
     nq = context_lengths(w.wid, w.B, w.new_lens, STREAM_LENGTHS)
     pre = context_lengths(w.wid, w.B, w.prefix_lens, STREAM_PREFIX)
     return ragged_inputs(w.Hq, w.Hkv, w.D, nq, pre, w.wid, poison=poison)
+
+
+@dataclass
+class SharedPrefixKV:
+    """A paged decode batch whose requests share prefix pages by group (host tensors).
+
+    Group j's prefix is ``prefix_pages[j]`` whole pages held once in the pool;
+    every request of the group starts its page-table row with those pages,
+    followed by pages of its own.
+    """
+    q: torch.Tensor              # [B, Hq, D] bf16
+    k_pages: torch.Tensor        # [P, Hkv, 64, D] bf16
+    v_pages: torch.Tensor
+    page_table: torch.Tensor     # [B, max_pages] int32, -1 where unused
+    seqlens: torch.Tensor        # [B] int32, prefix + suffix tokens
+    prefix_group: torch.Tensor   # [B] int32, group of each request or -1
+    prefix_pages: torch.Tensor   # [n_groups] int32
+    num_pages: int
+
+    @property
+    def B(self):
+        return self.q.shape[0]
+
+
+def shared_prefix_inputs(Hq, Hkv, D, groups, suffix_lens, prefix_pages, wid, nan_tails=True,
+                         max_pages=None) -> SharedPrefixKV:
+    """``groups[b]`` is request b's group (or -1), ``prefix_pages[j]`` group j's
+    prefix length in pages, ``suffix_lens[b]`` the tokens after the prefix.
+
+    Pool order: each group's prefix pages, then every request's own pages;
+    physical ids are a seeded permutation of that order.
+    """
+    grp = np.asarray(groups, dtype=np.int32)
+    suf = np.asarray(suffix_lens, dtype=np.int64)
+    pp = np.asarray(prefix_pages, dtype=np.int64)
+    B = len(grp)
+    pre_tok = np.array([64 * int(pp[j]) if j >= 0 else 0 for j in grp], dtype=np.int64)
+    L = (pre_tok + suf).astype(np.int32)
+    own = (suf + PAGE - 1) // PAGE
+    P = int(pp.sum() + own.sum())
+    P_alloc = max(P, 1)
+    perm = rng(wid, STREAM_PERM).permutation(P_alloc).astype(np.int32)
+    n_pages = np.array([int(pp[j]) if j >= 0 else 0 for j in grp], dtype=np.int64) + own
+    stride = int(max_pages) if max_pages is not None else max(int(n_pages.max(initial=0)), 1)
+    table = np.full((B, stride), -1, dtype=np.int32)
+    starts = np.concatenate([[0], np.cumsum(pp)]).astype(np.int64)
+    off = int(pp.sum())
+    partial = []
+    for b in range(B):
+        row = []
+        if grp[b] >= 0:
+            row += list(perm[starts[grp[b]]:starts[grp[b]] + pp[grp[b]]])
+        row += list(perm[off:off + own[b]])
+        off += int(own[b])
+        table[b, :len(row)] = row
+        if own[b] and int(suf[b]) % PAGE:
+            partial.append((int(row[-1]), int(suf[b]) % PAGE))
+    shape = (P_alloc, Hkv, PAGE, D)
+    q = normal(wid, STREAM_Q, (B, Hq, D), "bf16")
+    k = normal(wid, STREAM_K, shape, "bf16")
+    v = normal(wid, STREAM_V, shape, "bf16")
+    if nan_tails:
+        for p_, n in partial:
+            k[p_, :, n:, :] = float("nan")
+            v[p_, :, n:, :] = float("nan")
+    return SharedPrefixKV(q, k, v, torch.from_numpy(table), torch.from_numpy(L), torch.from_numpy(grp.copy()),
+                          torch.from_numpy(pp.astype(np.int32)), P_alloc)
+
+
+def workload_shared_prefix_inputs(w: SharedPrefixWorkload, nan_tails=True) -> SharedPrefixKV:
+    groups = np.concatenate([np.full(n, j, dtype=np.int32) for j, n in enumerate(w.group_sizes)])
+    suffix = context_lengths(w.wid, w.B, w.suffix_lens)
+    return shared_prefix_inputs(w.Hq, w.Hkv, w.D, groups, suffix, w.prefix_pages, w.wid, nan_tails)
