@@ -26,6 +26,7 @@ __all__ = [
     "fa_decode_plan_host", "fa_decode_workspace_size", "fa_debug_gather_kv",
     "fa_kv_append", "PrefillPlan", "fa_prefill_paged_plan", "fa_prefill_paged_run",
     "fa_prefill_paged_plan_host", "fa_prefill_paged_workspace_size", "prefill_paged",
+    "fa_decode_plan_cascade", "fa_decode_plan_cascade_host", "fa_decode_cascade_workspace_size",
 ]
 
 F32, BF16, FP8_E4M3FN = 0, 1, 2
@@ -90,6 +91,14 @@ def load():
     lib.fa_prefill_paged_plan_destroy.restype = None
     lib.fa_prefill_paged_run.argtypes = [vp, vp, vp, vp, vp, vp, vp, cf, vp, vp, vp, vp]
     lib.fa_prefill_paged_run.restype = ci
+    lib.fa_decode_cascade_workspace_size.argtypes = [i32p, ci, ci, ci, ci, ci, i32p, i32p, ci, ci]
+    lib.fa_decode_cascade_workspace_size.restype = csz
+    lib.fa_decode_plan_cascade.argtypes = [i32p, i32p, ci, ci, ci, ci, ci, ci, i32p, i32p, ci, ci, vp, csz,
+                                           vp, C.POINTER(vp), C.POINTER(ci)]
+    lib.fa_decode_plan_cascade.restype = ci
+    lib.fa_decode_plan_cascade_host.argtypes = [i32p, ci, ci, ci, ci, i32p, i32p, ci, ci, i32p, ci, i32p, ci,
+                                                i32p, C.POINTER(ci), C.POINTER(ci)]
+    lib.fa_decode_plan_cascade_host.restype = ci
     _LIB = lib
     return lib
 
@@ -402,3 +411,66 @@ def prefill_paged(plan, q, k_pages, v_pages, page_table, seqlens, cu_seqlens_q, 
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
     return fa_prefill_paged_run(plan, q, k_pages, v_pages, page_table, seqlens, cu_seqlens_q, out, lse,
                                 scale or 0.0, stream)
+
+
+# ------------------------------------------------------------------ shared-prefix (cascade) decode
+
+def _cascade_host_args(seqlens, prefix_group, prefix_pages):
+    sl, sp = _host_i32(seqlens)
+    gr, gp = _host_i32(prefix_group)
+    pg, pp = _host_i32(prefix_pages if len(prefix_pages) else [0])
+    if gr.numel() != sl.numel():
+        raise FAError(1, "prefix_group needs one entry per request")
+    i32 = C.POINTER(C.c_int32)
+    return (sl, gr, pg), C.cast(sp, i32), C.cast(gp, i32), C.cast(pp, i32), len(prefix_pages)
+
+
+def fa_decode_cascade_workspace_size(seqlens, max_pages, Hq, Hkv, prefix_group, prefix_pages, D=128,
+                                     num_cus=0):
+    keep, sp, gp, pp, ng = _cascade_host_args(seqlens, prefix_group, prefix_pages)
+    n = load().fa_decode_cascade_workspace_size(sp, keep[0].numel(), max_pages, Hq, Hkv, D, gp, pp, ng, num_cus)
+    if n == 0:
+        raise FAError(1, "invalid cascade arguments: " + load().fa_last_error().decode())
+    return n
+
+
+def fa_decode_plan_cascade_host(seqlens, max_pages, Hq, Hkv, prefix_group, prefix_pages, num_cus=256):
+    """Pure host cascade planning: (suffix items [n,4], prefix items [m,8], splits [B], num_splits)."""
+    lib = load()
+    keep, sp, gp, pp, ng = _cascade_host_args(seqlens, prefix_group, prefix_pages)
+    B = keep[0].numel()
+    npi, ns = C.c_int(0), C.c_int(0)
+    i32 = C.POINTER(C.c_int32)
+    n = lib.fa_decode_plan_cascade_host(sp, B, max_pages, Hq, Hkv, gp, pp, ng, num_cus, None, 0, None, 0, None,
+                                        C.byref(npi), C.byref(ns))
+    if n < 0:
+        _check(-n)
+    items = torch.zeros((max(n, 1), 4), dtype=torch.int32)
+    pitems = torch.zeros((max(npi.value, 1), 8), dtype=torch.int32)
+    splits = torch.zeros(B, dtype=torch.int32)
+    lib.fa_decode_plan_cascade_host(sp, B, max_pages, Hq, Hkv, gp, pp, ng, num_cus,
+                                    C.cast(items.data_ptr(), i32), n, C.cast(pitems.data_ptr(), i32), npi.value,
+                                    C.cast(splits.data_ptr(), i32), C.byref(npi), C.byref(ns))
+    return items[:n], pitems[:npi.value], splits, ns.value
+
+
+def fa_decode_plan_cascade(seqlens, page_table, num_pages, Hq, Hkv, prefix_group, prefix_pages, D=128,
+                           num_cus=0, device=None, stream=None):
+    """Plan a shared-prefix decode batch (bf16 KV); run it with fa_decode_run / decode."""
+    lib = load()
+    keep, sp, gp, pp, ng = _cascade_host_args(seqlens, prefix_group, prefix_pages)
+    pt, ptp = _host_i32(page_table)
+    if pt.dim() != 2 or pt.shape[0] != keep[0].numel():
+        raise FAError(1, "page_table must be [B, max_pages]")
+    B, stride = pt.shape
+    i32 = C.POINTER(C.c_int32)
+    ws_bytes = lib.fa_decode_cascade_workspace_size(sp, B, stride, Hq, Hkv, D, gp, pp, ng, num_cus)
+    if ws_bytes == 0:
+        raise FAError(1, "invalid cascade arguments: " + lib.fa_last_error().decode())
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+    handle = C.c_void_p()
+    ns = C.c_int(0)
+    _check(lib.fa_decode_plan_cascade(sp, C.cast(ptp, i32), B, stride, int(num_pages), Hq, Hkv, D, gp, pp, ng,
+                                      num_cus, _ptr(ws), ws_bytes, _stream(stream), C.byref(handle), C.byref(ns)))
+    return DecodePlan(handle, ws, ns.value, B, Hq, Hkv, D, BF16, keep[0])

@@ -54,6 +54,8 @@ struct fa_decode_plan_s {
   int B, stride, num_pages, Hq, Hkv, D, kv_dtype, num_splits, chunk_pages;
   std::vector<fa::WorkItem> items;
   std::vector<int32_t> splits;
+  std::vector<fa::PrefixItem> prefix_items;  // cascade plans only
+  std::vector<int32_t> group_reqs;
   fa::WorkspaceLayout layout;
 };
 
@@ -267,7 +269,7 @@ int fa_decode_run(const fa_decode_plan_t* plan, const void* q, const void* k_pag
     return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_run: num_splits %d != plan's %d", num_splits, plan->num_splits);
   if (!q || !out || !lse || !workspace || !seqlens)
     return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_run: null pointer (q/out/lse/workspace/seqlens)");
-  if (!plan->items.empty() && (!k_pages || !v_pages || !page_table))
+  if ((!plan->items.empty() || !plan->prefix_items.empty()) && (!k_pages || !v_pages || !page_table))
     return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_run: null KV pool or page table");
   bool fp8 = plan->kv_dtype == FA_DTYPE_FP8_E4M3FN;
   if (fp8 && !plan->items.empty() && (!k_scale || !v_scale))
@@ -289,10 +291,181 @@ int fa_decode_run(const fa_decode_plan_t* plan, const void* q, const void* k_pag
   a.out = out; a.lse = lse;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
+  if (!plan->prefix_items.empty()) {
+    // Cascade plan: the shared prefixes first, into their partial slots.
+    fa::PrefillArgs pa;
+    std::memset(&pa, 0, sizeof pa);
+    pa.q = q; pa.k = k_pages; pa.v = v_pages; pa.out = out; pa.lse = lse;
+    pa.B = plan->B; pa.Hq = plan->Hq; pa.Hkv = plan->Hkv; pa.D = plan->D;
+    pa.scale = a.scale;
+    pa.items = (const int32_t*)(ws + plan->layout.prefix_items_off);
+    pa.page_table = page_table; pa.seqlens = seqlens;
+    pa.stride = plan->stride; pa.num_pages = plan->num_pages;
+    pa.group_reqs = (const int32_t*)(ws + plan->layout.group_reqs_off);
+    pa.splits = a.splits_per_req;
+    pa.part_o = a.part_o; pa.part_lse = a.part_lse; pa.num_splits = plan->num_splits;
+    e = fa::launch_prefix_bf16(pa, (int)plan->prefix_items.size(), s);
+    if (e != hipSuccess) return hip_fail(e, "fa_decode_run prefix launch");
+  }
   if (a.n_items > 0) e = fa::launch_decode_split(a, plan->Hq / plan->Hkv, fp8 ? 1 : 0, s);
   if (e != hipSuccess) return hip_fail(e, "fa_decode_run split launch");
   e = fa::launch_lse_merge(a, s);
   if (e != hipSuccess) return hip_fail(e, "fa_decode_run merge launch");
+  return ok();
+}
+
+static int cascade_check(const char* who, const int32_t* seqlens_host, int B, int max_pages_per_req,
+                         int Hq, int Hkv, int D, const int32_t* prefix_group_host,
+                         const int32_t* prefix_pages_host, int n_groups, int num_cus) {
+  int st = check_decode_shape(B, Hq, Hkv, D);
+  if (st != FA_OK) return st;
+  if (!seqlens_host || !prefix_group_host || (n_groups > 0 && !prefix_pages_host))
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: seqlens, prefix_group (and prefix_pages when n_groups > 0) are required", who);
+  if (n_groups < 0 || max_pages_per_req < 1 || num_cus < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: need n_groups >= 0, max_pages_per_req >= 1, num_cus >= 0", who);
+  for (int j = 0; j < n_groups; ++j)
+    if (prefix_pages_host[j] < 0 || prefix_pages_host[j] > max_pages_per_req)
+      return fail(FA_ERR_INVALID_ARGUMENT, "%s: prefix_pages[%d]=%d outside [0, %d]", who, j, prefix_pages_host[j], max_pages_per_req);
+  for (int b = 0; b < B; ++b) {
+    const int j = prefix_group_host[b];
+    if (j < -1 || j >= n_groups)
+      return fail(FA_ERR_INVALID_ARGUMENT, "%s: prefix_group[%d]=%d outside [-1, %d)", who, b, j, n_groups);
+    if (seqlens_host[b] < 0) return fail(FA_ERR_INVALID_ARGUMENT, "%s: seqlens[%d] < 0", who, b);
+    if (j >= 0 && seqlens_host[b] < (int64_t)fa::kPage * prefix_pages_host[j])
+      return fail(FA_ERR_INVALID_ARGUMENT, "%s: request %d is shorter (%d) than its group's prefix (%d pages)", who, b, seqlens_host[b], prefix_pages_host[j]);
+    if (((int64_t)seqlens_host[b] + fa::kPage - 1) / fa::kPage > max_pages_per_req)
+      return fail(FA_ERR_INVALID_ARGUMENT, "%s: request %d needs more than max_pages_per_req pages", who, b);
+  }
+  return FA_OK;
+}
+
+size_t fa_decode_cascade_workspace_size(const int32_t* seqlens_host, int B, int max_pages_per_req, int Hq,
+                                        int Hkv, int D, const int32_t* prefix_group_host,
+                                        const int32_t* prefix_pages_host, int n_groups, int num_cus) {
+  if (cascade_check("fa_decode_cascade_workspace_size", seqlens_host, B, max_pages_per_req, Hq, Hkv, D,
+                    prefix_group_host, prefix_pages_host, n_groups, num_cus) != FA_OK)
+    return 0;
+  if (num_cus == 0 && device_cus(&num_cus) != FA_OK) return 0;
+  fa::CascadePlan cp;
+  if (fa::plan_cascade_host(seqlens_host, B, max_pages_per_req, Hq, Hkv, prefix_group_host, prefix_pages_host,
+                            n_groups, num_cus, &cp) != 0)
+    return 0;
+  return fa::workspace_layout((int)cp.items.size(), B, Hq, D, cp.num_splits, (int)cp.prefix_items.size(),
+                              (int)cp.group_reqs.size()).total;
+}
+
+int fa_decode_plan_cascade_host(const int32_t* seqlens_host, int B, int max_pages_per_req, int Hq, int Hkv,
+                                const int32_t* prefix_group_host, const int32_t* prefix_pages_host,
+                                int n_groups, int num_cus, int32_t* items_out, int capacity,
+                                int32_t* prefix_items_out, int prefix_capacity, int32_t* splits_out,
+                                int* n_prefix_items_out, int* num_splits_out) {
+  if (num_cus < 1 || capacity < 0 || prefix_capacity < 0) {
+    fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan_cascade_host: need num_cus >= 1 and capacities >= 0");
+    return -FA_ERR_INVALID_ARGUMENT;
+  }
+  int st = cascade_check("fa_decode_plan_cascade_host", seqlens_host, B, max_pages_per_req, Hq, Hkv, 128,
+                         prefix_group_host, prefix_pages_host, n_groups, num_cus);
+  if (st != FA_OK) return -st;
+  fa::CascadePlan cp;
+  if (fa::plan_cascade_host(seqlens_host, B, max_pages_per_req, Hq, Hkv, prefix_group_host, prefix_pages_host,
+                            n_groups, num_cus, &cp) != 0) {
+    fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan_cascade_host: planning failed");
+    return -FA_ERR_INVALID_ARGUMENT;
+  }
+  for (int i = 0; items_out && i < std::min<int>(capacity, (int)cp.items.size()); ++i) {
+    items_out[4 * i + 0] = cp.items[i].b;
+    items_out[4 * i + 1] = cp.items[i].g_split;
+    items_out[4 * i + 2] = cp.items[i].page_begin;
+    items_out[4 * i + 3] = cp.items[i].page_end;
+  }
+  for (int i = 0; prefix_items_out && i < std::min<int>(prefix_capacity, (int)cp.prefix_items.size()); ++i)
+    std::memcpy(prefix_items_out + 8 * i, &cp.prefix_items[i], sizeof(fa::PrefixItem));
+  if (splits_out) std::memcpy(splits_out, cp.splits.data(), sizeof(int32_t) * B);
+  if (n_prefix_items_out) *n_prefix_items_out = (int)cp.prefix_items.size();
+  if (num_splits_out) *num_splits_out = cp.num_splits;
+  ok();
+  return (int)cp.items.size();
+}
+
+int fa_decode_plan_cascade(const int32_t* seqlens_host, const int32_t* page_table_host, int B,
+                           int max_pages_per_req, int num_pages, int Hq, int Hkv, int D,
+                           const int32_t* prefix_group_host, const int32_t* prefix_pages_host,
+                           int n_groups, int num_cus, void* workspace, size_t workspace_bytes,
+                           void* stream, fa_decode_plan_t** plan_out, int* num_splits_out) {
+  if (!plan_out || !num_splits_out)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan_cascade: plan_out and num_splits_out must be non-null");
+  *plan_out = nullptr;
+  int st = cascade_check("fa_decode_plan_cascade", seqlens_host, B, max_pages_per_req, Hq, Hkv, D,
+                         prefix_group_host, prefix_pages_host, n_groups, num_cus);
+  if (st != FA_OK) return st;
+  if (!page_table_host || num_pages < 1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan_cascade: the host page table and num_pages >= 1 are required");
+  std::vector<int32_t> first(std::max(n_groups, 1), -1);
+  for (int b = 0; b < B; ++b) {
+    const int64_t n = ((int64_t)seqlens_host[b] + fa::kPage - 1) / fa::kPage;
+    const int32_t* row = page_table_host + (int64_t)b * max_pages_per_req;
+    for (int64_t j = 0; j < n; ++j)
+      if (row[j] < 0 || row[j] >= num_pages)
+        return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan_cascade: page_table[%d][%lld]=%d outside [0,%d)", b, (long long)j, row[j], num_pages);
+    const int g = prefix_group_host[b];
+    if (g < 0) continue;
+    if (first[g] < 0) {
+      first[g] = b;
+      continue;
+    }
+    const int32_t* ref = page_table_host + (int64_t)first[g] * max_pages_per_req;
+    for (int j = 0; j < prefix_pages_host[g]; ++j)
+      if (row[j] != ref[j])
+        return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan_cascade: request %d does not share page %d of group %d's prefix", b, j, g);
+  }
+  if (num_cus == 0) {
+    st = device_cus(&num_cus);
+    if (st != FA_OK) return st;
+  }
+  fa_decode_plan_t* p = new (std::nothrow) fa_decode_plan_t;
+  if (!p) return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan_cascade: out of host memory");
+  fa::CascadePlan cp;
+  if (fa::plan_cascade_host(seqlens_host, B, max_pages_per_req, Hq, Hkv, prefix_group_host, prefix_pages_host,
+                            n_groups, num_cus, &cp) != 0) {
+    delete p;
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan_cascade: planning failed");
+  }
+  p->B = B; p->stride = max_pages_per_req; p->num_pages = num_pages;
+  p->Hq = Hq; p->Hkv = Hkv; p->D = D; p->kv_dtype = FA_DTYPE_BF16;
+  p->num_splits = cp.num_splits; p->chunk_pages = cp.prefix_chunk_pages;
+  p->items = std::move(cp.items);
+  p->splits = std::move(cp.splits);
+  p->prefix_items = std::move(cp.prefix_items);
+  p->group_reqs = std::move(cp.group_reqs);
+  p->layout = fa::workspace_layout((int)p->items.size(), B, Hq, D, p->num_splits, (int)p->prefix_items.size(),
+                                   (int)p->group_reqs.size());
+  if (!workspace || workspace_bytes < p->layout.total) {
+    size_t need = p->layout.total;
+    delete p;
+    return fail(FA_ERR_WORKSPACE, "fa_decode_plan_cascade: workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  }
+  // The metadata before and after the partial-result area, staged and
+  // uploaded in two copies (the partials themselves need no initial value).
+  const fa::WorkspaceLayout& w = p->layout;
+  std::vector<char> head(w.part_o_off, 0), tail(w.total - w.prefix_items_off, 0);
+  if (!p->items.empty()) std::memcpy(head.data() + w.items_off, p->items.data(), sizeof(fa::WorkItem) * p->items.size());
+  std::memcpy(head.data() + w.splits_off, p->splits.data(), sizeof(int32_t) * B);
+  if (!p->prefix_items.empty())
+    std::memcpy(tail.data(), p->prefix_items.data(), sizeof(fa::PrefixItem) * p->prefix_items.size());
+  if (!p->group_reqs.empty())
+    std::memcpy(tail.data() + (w.group_reqs_off - w.prefix_items_off), p->group_reqs.data(),
+                sizeof(int32_t) * p->group_reqs.size());
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(workspace, head.data(), head.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && !tail.empty())
+    e = hipMemcpyAsync((char*)workspace + w.prefix_items_off, tail.data(), tail.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);  // the staging block is freed on return
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "fa_decode_plan_cascade upload");
+  }
+  *plan_out = p;
+  *num_splits_out = p->num_splits;
   return ok();
 }
 

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <vector>
+
 namespace fa {
 
 constexpr int kPage = 64;         // tokens per KV page
@@ -29,6 +31,12 @@ struct PrefillArgs {
   const int32_t* cu_q;        // [B + 1]
   int stride;
   int num_pages;
+  // Shared-prefix pass only: folded (request, head) rows, partial results.
+  const int32_t* group_reqs;  // requests of every group, concatenated
+  const int32_t* splits;      // [B] partial slots per request
+  float* part_o;              // [B, Hq, num_splits, D]
+  float* part_lse;            // [B, Hq, num_splits]
+  int num_splits;
   uint8_t kv_map[kMaxHeads];
 };
 
@@ -38,6 +46,24 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 // Query rows per work item of the bf16 prefill kernel (ragged plan unit).
 constexpr int kPrefillRows = 256;
 hipError_t launch_prefill_paged_bf16(const PrefillArgs& a, int n_items, hipStream_t s);
+
+// One workgroup of the shared-prefix pass: the decode queries of the
+// requests group_reqs[req_off + r / G] (query heads g*G + r % G), rows
+// row0 .. row0 + nrows - 1 of that folding, against prefix pages
+// [page_begin, page_end) of first_req's page-table row; the result goes to
+// partial slot `slot` of each of those (request, head) pairs.
+struct PrefixItem {
+  int32_t req_off;
+  int32_t g;
+  int32_t row0;
+  int32_t nrows;
+  int32_t page_begin;
+  int32_t page_end;
+  int32_t slot;
+  int32_t first_req;
+};
+static_assert(sizeof(PrefixItem) == 32, "PrefixItem is exported as 8 int32");
+hipError_t launch_prefix_bf16(const PrefillArgs& a, int n_items, hipStream_t s);
 
 struct AppendArgs {
   const void* k_new;          // [T, Hkv, D] bf16
@@ -110,10 +136,29 @@ int plan_decode_host(const int32_t* seqlens, int B, int stride, int Hkv, int num
 int plan_prefill_host(const int32_t* seqlens, const int32_t* cu_q, int B, int32_t* items,
                       int capacity);
 
-// Workspace layout for a plan: work items, per-request split counts, partials.
-struct WorkspaceLayout {
-  size_t items_off, splits_off, part_o_off, part_lse_off, total;
+// Shared-prefix (cascade) decode plan: prefix-pass items, the suffix
+// split-KV items (page ranges after the prefix, slots after the prefix
+// slots), per-request slot counts and the concatenated group members.
+struct CascadePlan {
+  std::vector<WorkItem> items;
+  std::vector<PrefixItem> prefix_items;
+  std::vector<int32_t> splits;      // [B]
+  std::vector<int32_t> group_reqs;  // requests of group 0, then group 1, ...
+  int num_splits = 0;
+  int prefix_chunk_pages = 0;
 };
-WorkspaceLayout workspace_layout(int n_items, int B, int Hq, int D, int num_splits);
+// Returns 0 or -1 (invalid lengths or groups). Validation of the page table
+// (shared prefix pages) is the caller's.
+int plan_cascade_host(const int32_t* seqlens, int B, int stride, int Hq, int Hkv,
+                      const int32_t* group, const int32_t* prefix_pages, int n_groups, int num_cus,
+                      CascadePlan* out);
+
+// Workspace layout for a plan: work items, per-request split counts,
+// partials, and (cascade plans) prefix items and group members.
+struct WorkspaceLayout {
+  size_t items_off, splits_off, part_o_off, part_lse_off, prefix_items_off, group_reqs_off, total;
+};
+WorkspaceLayout workspace_layout(int n_items, int B, int Hq, int D, int num_splits,
+                                 int n_prefix_items = 0, int n_group_reqs = 0);
 
 }  // namespace fa

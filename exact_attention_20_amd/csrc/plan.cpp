@@ -187,15 +187,107 @@ int plan_prefill_host(const int32_t* seqlens, const int32_t* cu_q, int B, int32_
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-WorkspaceLayout workspace_layout(int n_items, int B, int Hq, int D, int num_splits) {
+WorkspaceLayout workspace_layout(int n_items, int B, int Hq, int D, int num_splits,
+                                 int n_prefix_items, int n_group_reqs) {
   WorkspaceLayout w;
   w.items_off = 0;
   w.splits_off = align_up(w.items_off + sizeof(WorkItem) * (size_t)std::max(n_items, 1), 256);
   w.part_o_off = align_up(w.splits_off + sizeof(int32_t) * (size_t)B, 256);
   size_t rows = (size_t)B * Hq * (size_t)std::max(num_splits, 1);
   w.part_lse_off = align_up(w.part_o_off + sizeof(float) * rows * D, 256);
-  w.total = align_up(w.part_lse_off + sizeof(float) * rows, 256);
+  w.prefix_items_off = align_up(w.part_lse_off + sizeof(float) * rows, 256);
+  w.group_reqs_off = align_up(w.prefix_items_off + sizeof(PrefixItem) * (size_t)n_prefix_items, 256);
+  w.total = align_up(w.group_reqs_off + sizeof(int32_t) * (size_t)n_group_reqs, 256);
   return w;
+}
+
+// Shared-prefix (cascade) decode plan.
+//
+// The prefix of a group is attended once for all of the group's decode
+// queries: G query heads of each request fold into the rows of one dense
+// tile per KV head (up to kPrefillRows rows per workgroup), and the prefix
+// pages are cut into chunks so that there are about as many prefix
+// workgroups as CUs (at least kMinPrefixChunk pages each, which keeps the
+// per-workgroup start-up small next to its work). Each chunk is one partial
+// slot of every request of the group. The suffixes (the tokens after the
+// prefix) are planned like ordinary decode requests; their page ranges are
+// shifted past the prefix and their slots past the prefix slots, so the LSE
+// merge combines prefix and suffix partials of a request in one pass.
+constexpr int kMinPrefixChunk = 8;
+
+int plan_cascade_host(const int32_t* seqlens, int B, int stride, int Hq, int Hkv,
+                      const int32_t* group, const int32_t* prefix_pages, int n_groups, int num_cus,
+                      CascadePlan* out) {
+  if (!seqlens || !group || B < 1 || stride < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 ||
+      n_groups < 0 || (n_groups > 0 && !prefix_pages) || num_cus < 1 || !out)
+    return -1;
+  const int G = Hq / Hkv;
+  std::vector<int32_t> pre_pages(B, 0), suffix(B, 0);
+  std::vector<std::vector<int32_t>> members(n_groups);
+  for (int b = 0; b < B; ++b) {
+    const int j = group[b];
+    if (j < -1 || j >= n_groups || seqlens[b] < 0) return -1;
+    if (j >= 0) {
+      if (prefix_pages[j] < 0 || prefix_pages[j] > stride) return -1;
+      const int64_t pt = (int64_t)kPage * prefix_pages[j];
+      if (seqlens[b] < pt) return -1;  // the prefix must lie inside the cache
+      pre_pages[b] = prefix_pages[j];
+      suffix[b] = (int32_t)(seqlens[b] - pt);
+      members[j].push_back(b);
+    } else {
+      suffix[b] = seqlens[b];
+    }
+    if (((int64_t)seqlens[b] + kPage - 1) / kPage > stride) return -1;
+  }
+  // Prefix chunk size from the total prefix work (page x KV head x row block).
+  int64_t work = 0;
+  for (int j = 0; j < n_groups; ++j) {
+    const int64_t rows = (int64_t)members[j].size() * G;
+    work += (int64_t)prefix_pages[j] * Hkv * ((rows + kPrefillRows - 1) / kPrefillRows);
+  }
+  int chunk = (int)std::max<int64_t>(kMinPrefixChunk, (work + num_cus - 1) / std::max(num_cus, 1));
+  out->prefix_chunk_pages = work > 0 ? chunk : 0;
+  out->group_reqs.clear();
+  out->prefix_items.clear();
+  std::vector<int32_t> pre_slots(B, 0);
+  for (int j = 0; j < n_groups; ++j) {
+    const int req_off = (int)out->group_reqs.size();
+    out->group_reqs.insert(out->group_reqs.end(), members[j].begin(), members[j].end());
+    const int np = prefix_pages[j];
+    const int rows = (int)members[j].size() * G;
+    if (np == 0 || rows == 0) continue;
+    const int nc = (np + chunk - 1) / chunk;
+    for (int b : members[j]) pre_slots[b] = nc;
+    for (int r0 = 0; r0 < rows; r0 += kPrefillRows)
+      for (int c = 0; c < nc; ++c)
+        for (int g = 0; g < Hkv; ++g)
+          out->prefix_items.push_back(PrefixItem{req_off, g, r0, std::min(kPrefillRows, rows - r0),
+                                                 (int)((int64_t)np * c / nc), (int)((int64_t)np * (c + 1) / nc),
+                                                 c, members[j][0]});
+  }
+  std::stable_sort(out->prefix_items.begin(), out->prefix_items.end(), [](const PrefixItem& x, const PrefixItem& y) {
+    return (int64_t)(x.page_end - x.page_begin) * x.nrows > (int64_t)(y.page_end - y.page_begin) * y.nrows;
+  });
+  // Suffixes: an ordinary decode plan on the suffix lengths, then shifted.
+  PlanResult r;
+  if (plan_decode_host(suffix.data(), B, stride, Hkv, 0, num_cus, nullptr, 0, nullptr, &r) != 0) return -1;
+  out->items.assign(std::max(r.n_items, 1), WorkItem{});
+  out->splits.assign(B, 0);
+  plan_decode_host(suffix.data(), B, stride, Hkv, 0, num_cus, out->items.data(), r.n_items, out->splits.data(), &r);
+  out->items.resize(r.n_items);
+  for (WorkItem& it : out->items) {
+    const int b = it.b;
+    const int g = it.g_split & 255, s = it.g_split >> 8;
+    it.page_begin += pre_pages[b];
+    it.page_end += pre_pages[b];
+    it.g_split = g | ((s + pre_slots[b]) << 8);
+  }
+  out->num_splits = 0;
+  for (int b = 0; b < B; ++b) {
+    out->splits[b] += pre_slots[b];
+    out->num_splits = std::max(out->num_splits, (int)out->splits[b]);
+  }
+  return 0;
 }
 
 }  // namespace fa

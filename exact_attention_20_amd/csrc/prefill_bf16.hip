@@ -95,10 +95,19 @@ __device__ __forceinline__ uint2 lds_read_tr16(const char* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-// PAGED: ragged paged prefill. Work unit (request, query tile) from the
-// plan's list; the request's new tokens are packed rows [T, Hq, D] of q and
-// out; key tile t is page t of the request's page-table row.
-template <int NW, int QB, bool PAGED>
+// Modes of the kernel:
+//  kContig  contiguous [B, H, S, D] tensors, one work unit per (query tile, b, h);
+//  kRagged  ragged paged prefill: work unit (request, query tile) from the
+//           plan's list, the request's new tokens are packed rows [T, Hq, D]
+//           of q and out, key tile t is page t of the request's table row;
+//  kPrefix  shared-prefix pass of a cascade decode: one work unit per
+//           PrefixItem; its query rows are the decode queries of a group's
+//           requests, G query heads of each folded into rows (one dense tile
+//           per KV head: "head-query fusion"), its keys a chunk of the
+//           group's prefix pages, no mask; results go to partial slots.
+constexpr int kContig = 0, kRagged = 1, kPrefix = 2;
+
+template <int NW, int QB, int MODE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   constexpr int NT = 64 * NW;                 // threads
@@ -109,6 +118,7 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   __shared__ __attribute__((aligned(16))) char k_lds[2 * KBUF];
   __shared__ __attribute__((aligned(16))) char v_lds[2 * VBUF];
 
+  constexpr bool PAGED = MODE != kContig;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int hi = lane >> 5;     // which half of the wavefront
@@ -118,7 +128,22 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   const int L = blockIdx.x;
   int b, h, g, qt, Sq, Sk, causal;
   size_t tok0 = 0;  // ragged: packed row of the request's first new token
-  if constexpr (PAGED) {
+  int p_first = 0;  // paged: table entry of key tile 0
+  int slot = 0, req_off = 0, row0 = 0;  // prefix pass
+  if constexpr (MODE == kPrefix) {
+    const PrefixItem it = reinterpret_cast<const PrefixItem*>(a.items)[L];
+    b = it.first_req;  // its page-table row holds the group's prefix pages
+    g = it.g;
+    h = 0;
+    qt = 0;
+    Sq = it.nrows;
+    Sk = (it.page_end - it.page_begin) * kBc;
+    causal = 0;
+    p_first = it.page_begin;
+    slot = it.slot;
+    req_off = it.req_off;
+    row0 = it.row0;
+  } else if constexpr (MODE == kRagged) {
     // Items are ordered heaviest first; within one, e enumerates query head
     // h = g*G + e/Hkv with g = e % Hkv, so workgroups with equal id mod 8
     // (one XCD) share a KV head when Hq is a multiple of 8.
@@ -159,10 +184,23 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   if (causal) kend = min(Sk, q0 + BR + off);
   const int n_kt = kend > 0 ? (kend + kBc - 1) / kBc : 0;
 
-  // Query/output rows: contiguous [Sq, D] per head, or packed [T, Hq, D].
-  const size_t row_stride = PAGED ? (size_t)a.Hq * kD : (size_t)kD;
-  const size_t qo_base = PAGED ? (tok0 * a.Hq + h) * kD : ((size_t)b * a.Hq + h) * (size_t)Sq * kD;
+  // Query/output rows: contiguous [Sq, D] per head, packed [T, Hq, D], or
+  // (prefix pass) row r = decode query (request, head) of the group, found
+  // through the group's member list, as a row of q [B * Hq, D].
+  const size_t row_stride = MODE == kRagged ? (size_t)a.Hq * kD : (size_t)kD;
+  const size_t qo_base = MODE == kPrefix   ? 0
+                         : MODE == kRagged ? (tok0 * a.Hq + h) * kD
+                                           : ((size_t)b * a.Hq + h) * (size_t)Sq * kD;
   const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q) + qo_base;
+  auto prefix_row = [&](int r) -> size_t {
+    const int G = a.Hq / a.Hkv;
+    const int f = row0 + r;
+    const int req = a.group_reqs[req_off + f / G];
+    return (size_t)req * a.Hq + g * G + f % G;
+  };
+  auto q_row_ptr = [&](int r) {
+    return MODE == kPrefix ? reinterpret_cast<const uint16_t*>(a.q) + prefix_row(r) * kD : Q + (size_t)r * row_stride;
+  };
 
   // ---- Q: the B operand of S^T = K Q^T for lane (col, hi) in query block
   // qb is row 32*(QB*wave + qb) + col of the tile, dims 16*kk + 8*hi + 0..7.
@@ -175,7 +213,7 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (r < Sq) v = *reinterpret_cast<const uint4*>(Q + (size_t)r * row_stride + 16 * kk + 8 * hi);
+      if (r < Sq) v = *reinterpret_cast<const uint4*>(q_row_ptr(r) + 16 * kk + 8 * hi);
       qreg[qb][kk] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
@@ -226,7 +264,8 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   // which do not wait behind the tile loads in flight.
   const_i32* ptab = (const_i32*)(a.page_table) + (size_t)b * a.stride;
   auto page_rsrc = [&](const void* pool, int t) {
-    const int pid = t < a.stride ? ptab[t] : -1;
+    const int pt = p_first + t;
+    const int pid = pt < a.stride ? ptab[pt] : -1;
     const bool valid = (unsigned)pid < (unsigned)a.num_pages;
     const char* base = reinterpret_cast<const char*>(pool) +
                        ((size_t)(valid ? pid : 0) * a.Hkv + g) * (size_t)(kBc * kRow);
@@ -501,6 +540,38 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
     const float let_ = xor32_sum((le[qb][0] + le[qb][1]) + (le[qb][2] + le[qb][3]));
     if (qrow[qb] >= Sq) continue;
     const float inv = lrt > 0.f ? 1.f / lrt : 0.f;
+    const float lse_val = let_ > 0.f ? (m[qb] + __log2f(let_)) * kLn2 : kNegInf;
+    if constexpr (MODE == kPrefix) {
+      // The request's only slot: final bf16 output; else this chunk's
+      // normalised partial output and LSE for the merge.
+      const size_t pr = prefix_row(qrow[qb]);
+      const int req = (int)(pr / a.Hq);
+      if (a.splits[req] == 1) {
+        uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + pr * kD;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int d = 32 * db + 8 * gq + 4 * hi;
+            *reinterpret_cast<uint2*>(O + d) =
+                make_uint2(pack_bf16x2(o[qb][db][4 * gq] * inv, o[qb][db][4 * gq + 1] * inv),
+                           pack_bf16x2(o[qb][db][4 * gq + 2] * inv, o[qb][db][4 * gq + 3] * inv));
+          }
+        if (hi == 0) a.lse[pr] = lse_val;
+      } else {
+        float* P = a.part_o + (pr * a.num_splits + slot) * kD;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int d = 32 * db + 8 * gq + 4 * hi;
+            *reinterpret_cast<float4*>(P + d) = make_float4(o[qb][db][4 * gq] * inv, o[qb][db][4 * gq + 1] * inv,
+                                                            o[qb][db][4 * gq + 2] * inv, o[qb][db][4 * gq + 3] * inv);
+          }
+        if (hi == 0) a.part_lse[pr * a.num_splits + slot] = lse_val;
+      }
+      continue;
+    }
     uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + qo_base + (size_t)qrow[qb] * row_stride;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -512,7 +583,7 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
         *reinterpret_cast<uint2*>(O + d) = w;
       }
     const size_t lse_idx = PAGED ? (tok0 + qrow[qb]) * a.Hq + h : ((size_t)b * a.Hq + h) * Sq + qrow[qb];
-    if (hi == 0) a.lse[lse_idx] = let_ > 0.f ? (m[qb] + __log2f(let_)) * kLn2 : kNegInf;
+    if (hi == 0) a.lse[lse_idx] = lse_val;
   }
 }
 
@@ -523,7 +594,7 @@ hipError_t launch_cfg(const PrefillArgs& a, hipStream_t s) {
   const int nbh = a.B * a.Hq;
   const long long blocks = (long long)n_qtiles * nbh;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_bf16_kernel<NW, QB, false>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a, n_qtiles, nbh);
+  hipLaunchKernelGGL((prefill_bf16_kernel<NW, QB, kContig>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a, n_qtiles, nbh);
   return hipGetLastError();
 }
 
@@ -533,7 +604,15 @@ hipError_t launch_paged_cfg(const PrefillArgs& a, int n_items, hipStream_t s) {
   const long long blocks = (long long)n_items * a.Hq;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_bf16_kernel<NW, QB, true>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a, 0, 0);
+  hipLaunchKernelGGL((prefill_bf16_kernel<NW, QB, kRagged>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a, 0, 0);
+  return hipGetLastError();
+}
+
+template <int NW, int QB>
+hipError_t launch_prefix_cfg(const PrefillArgs& a, int n_items, hipStream_t s) {
+  static_assert(32 * NW * QB == kPrefillRows, "the plan's tile height must match the kernel's");
+  if (n_items == 0) return hipSuccess;
+  hipLaunchKernelGGL((prefill_bf16_kernel<NW, QB, kPrefix>), dim3((unsigned)n_items), dim3(64 * NW), 0, s, a, 0, 0);
   return hipGetLastError();
 }
 
@@ -545,6 +624,10 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
 
 hipError_t launch_prefill_paged_bf16(const PrefillArgs& a, int n_items, hipStream_t s) {
   return launch_paged_cfg<8, 1>(a, n_items, s);
+}
+
+hipError_t launch_prefix_bf16(const PrefillArgs& a, int n_items, hipStream_t s) {
+  return launch_prefix_cfg<8, 1>(a, n_items, s);
 }
 
 }  // namespace fa

@@ -300,6 +300,61 @@ int fa_prefill_paged_run(const fa_prefill_plan_t* plan, const void* q, const voi
                          void* workspace, void* stream);
 
 /*
+ * Shared-prefix (cascade) decode: requests that share a prompt prefix.
+ * ("FIA / FlashAttention" Q&A, section 3's comparison table: prefix sharing
+ * and head-query fusion as inference optimisations; "Flash Attention & Paged
+ * Attention", Flash-Decoding: partial results over parts of the KV sequence
+ * are combined exactly by their LogSumExp.)
+ *
+ * The batch is a paged decode batch as above. Requests are put in groups;
+ * every request of group j starts its page-table row with the same
+ * prefix_pages[j] physical pages (a prefix of 64 * prefix_pages[j] tokens,
+ * whole pages only, held once in the pool). The result is exactly decode
+ * attention over each request's whole cache, as fa_decode_run computes it;
+ * only the work is organised differently: a group's prefix is attended once
+ * for all its decode queries (the G query heads of every member folded into
+ * the rows of one dense matrix-core tile per KV head), each request's suffix
+ * goes through the split-KV kernel, and the LSE merge combines prefix and
+ * suffix partials. bf16 KV only; Hq, Hkv, D as for fa_decode_plan.
+ *
+ *   prefix_group_host  host int32[B]: group of each request, or -1 (no prefix)
+ *   prefix_pages_host  host int32[n_groups]: prefix length of each group in
+ *                      pages (0 allowed); every member needs L_b >= 64 * that.
+ *   n_groups           number of groups (0: an ordinary decode plan)
+ * The plan checks, on the host page table, that every member shares its
+ * group's prefix pages (FA_ERR_INVALID_ARGUMENT otherwise). The plan object
+ * is used with fa_decode_run and freed with fa_decode_plan_destroy like any
+ * decode plan; fa_decode_run then launches three kernels (prefix pass,
+ * split-KV kernel, merge).
+ */
+size_t fa_decode_cascade_workspace_size(const int32_t* seqlens_host, int B, int max_pages_per_req,
+                                        int Hq, int Hkv, int D, const int32_t* prefix_group_host,
+                                        const int32_t* prefix_pages_host, int n_groups,
+                                        int num_cus);
+
+int fa_decode_plan_cascade(const int32_t* seqlens_host, const int32_t* page_table_host, int B,
+                           int max_pages_per_req, int num_pages, int Hq, int Hkv, int D,
+                           const int32_t* prefix_group_host, const int32_t* prefix_pages_host,
+                           int n_groups, int num_cus, void* workspace, size_t workspace_bytes,
+                           void* stream, fa_decode_plan_t** plan_out, int* num_splits_out);
+
+/*
+ * Pure host cascade planning (no device, no HIP call), for inspection and
+ * tests. Writes up to `capacity` suffix work items as in
+ * fa_decode_plan_items, up to `prefix_capacity` prefix items as int32
+ * octets (member-list offset, KV head, first folded row, rows, first page,
+ * end page, partial slot, a member request), each request's slot count
+ * into splits_out[B], the prefix item count and the largest slot count.
+ * Returns the number of suffix items or a negative fa_status.
+ */
+int fa_decode_plan_cascade_host(const int32_t* seqlens_host, int B, int max_pages_per_req, int Hq,
+                                int Hkv, const int32_t* prefix_group_host,
+                                const int32_t* prefix_pages_host, int n_groups, int num_cus,
+                                int32_t* items_out, int capacity, int32_t* prefix_items_out,
+                                int prefix_capacity, int32_t* splits_out,
+                                int* n_prefix_items_out, int* num_splits_out);
+
+/*
  * fa_debug_gather_kv -- copy the L_b logical tokens of one request and KV
  * head out of a paged pool, through the same page-table indexing the decode
  * kernel uses, into dst [L_b, D] (same element type as the pool). For the
