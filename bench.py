@@ -1,7 +1,7 @@
 """Benchmark of the exact-attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--prewarm-s S] [--no-cpu-baseline]
-                    [--only prefill|decode|ragged|copy] [--prefill-workload 2|3]
+                    [--only prefill|decode|ragged|cascade|copy] [--prefill-workload 2|3]
                     [--decode-workload 4|5]
 
 One step = one pass of the whole path over one synthetic batch:
@@ -14,7 +14,10 @@ A third leg, reported as its own ``ragged_prefill`` object and not part of
 the step, measures the ragged paged prefill: fa_kv_append of 16 requests'
 new tokens (256..2048 each) into their paged caches, then fa_prefill_paged_run
 of those tokens over prefix + new keys (prefixes 0..16384), each timed on
-its own. Inputs are resident in HBM before timing. Each leg first runs untimed for
+its own. A fourth, the ``shared_prefix_decode`` object, times the cascade
+decode of 64 requests sharing an 8192-token prefix (suffixes 256..4096)
+against plain split-KV decode of the same batch. Inputs are resident in HBM
+before timing. Each leg first runs untimed for
 --prewarm-s seconds (default 1 s: GPU clocks and power reach steady state)
 and --warmup more times; each timed call is then bracketed by HIP events on
 the stream it runs on, and the step time is the sum of the legs' means.
@@ -95,6 +98,21 @@ def ragged_bytes(nq, pre, w):
 def append_bytes(nq, w):
     """HBM bytes of one KV append: new K and V rows read once and written once."""
     return 4 * int(sum(int(n) for n in nq)) * w.Hkv * w.D * 2
+
+
+def cascade_bytes(L, groups, prefix_pages, w):
+    """Algorithmic HBM bytes of a cascade decode step: every group's prefix
+    K/V read once, every request's suffix K/V once, q in, out and lse out,
+    page-table entries and lengths read."""
+    import numpy as np
+    L = np.asarray(L, np.int64)
+    pre = np.array([64 * int(prefix_pages[j]) if j >= 0 else 0 for j in groups], np.int64)
+    row = w.Hkv * w.D * 2 * 2                                # K and V bytes of one token
+    b = int(sum(int(p) for p in prefix_pages)) * 64 * row      # each prefix once
+    b += int((L - pre).sum()) * row                          # suffixes
+    b += 2 * len(L) * w.Hq * w.D * 2 + len(L) * w.Hq * 4      # q, out, lse
+    b += int(((L + 63) // 64).sum()) * 4 + len(L) * 4
+    return b
 
 
 def source_sha(rel):
@@ -246,6 +264,35 @@ def cpu_baseline_ragged(w, r, budget_s=10.0):
                       f"ragged prefill workload, {dt:.1f} s wall, fp64 numpy, BLAS 1 thread per worker"}
 
 
+def cpu_baseline_cascade(w, r, budget_s=10.0):
+    """fp64 oracle decode (the cascade's definition) on whole requests, threads over requests."""
+    import concurrent.futures as cf
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    q = r.q.double().numpy()
+    kp, vp = r.k_pages.float().numpy(), r.v_pages.float().numpy()
+    pt, sl = r.page_table.numpy(), r.seqlens.numpy()
+
+    def one(b):
+        oracle.paged_decode(q, kp, vp, pt, sl, w.scale, requests=[b])
+        return int(sl[b])
+
+    done, toks = 0, 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1), cf.ThreadPoolExecutor(cores) as ex:
+        while done < w.B and time.perf_counter() - t0 < budget_s:
+            batch = list(range(done, min(w.B, done + cores)))
+            toks += sum(ex.map(one, batch))
+            done += len(batch)
+    dt = time.perf_counter() - t0
+    return {"value": toks * w.Hkv * w.D * 4 / dt / 1e9, "unit": "GB/s (plain-decode bytes)", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{done} of {w.B} requests of the shared-prefix workload (all heads, plain decode "
+                      f"definition), {dt:.1f} s wall, fp64 numpy, BLAS 1 thread per worker"}
+
+
 COPY_BYTES = 1 << 30   # calibration copy: bytes read, and bytes written, per launch
 
 
@@ -280,6 +327,8 @@ PMC_LEGS = {
     "decode_wl5": ("--only decode --decode-workload 5", ["decode_mfma_kernel", "lse_merge_kernel"], DECODE_SRC),
     "ragged_prefill_wl6": ("--only ragged", ["prefill_bf16_kernel"],
                            "exact_attention_20_amd/csrc/prefill_bf16.hip"),
+    "cascade_wl7": ("--only cascade", ["prefill_bf16_kernel", "decode_mfma_kernel", "lse_merge_kernel"],
+                    "exact_attention_20_amd/csrc/prefill_bf16.hip+" + DECODE_SRC),
     "copy": ("--only copy", ["neg"], None),
 }
 PMC_RUN = "--steps 3 --warmup 1 --prewarm-s 0 --no-cpu-baseline"
@@ -344,6 +393,9 @@ def summarize_profiles(d):
         w = workloads.WORKLOADS[wid]
         if leg.startswith("prefill"):
             alg = prefill_bytes(w)
+        elif leg.startswith("cascade"):
+            x = workloads.workload_shared_prefix_inputs(w)
+            alg = cascade_bytes(x.seqlens.numpy(), x.prefix_group.numpy(), list(w.prefix_pages), w)
         elif leg.startswith("ragged"):
             alg = ragged_bytes(workloads.context_lengths(wid, w.B, w.new_lens),
                                workloads.context_lengths(wid, w.B, w.prefix_lens, workloads.STREAM_PREFIX), w)
@@ -392,6 +444,8 @@ def summarize_profiles(d):
                 lines.append(f"bench prefill launch_ms_mean: {b['roofline'].get('launch_ms_mean')}")
                 if "decode" in b:
                     lines.append(f"bench decode step ms_mean: {b['decode'].get('ms_mean')}")
+                if "shared_prefix_decode" in b:
+                    lines.append(f"bench shared-prefix decode step ms_mean: {b['shared_prefix_decode'].get('ms_mean')}")
                 if "ragged_prefill" in b:
                     rg = b["ragged_prefill"]
                     lines.append(f"bench ragged paged prefill launch ms_mean: {rg.get('ms_mean')}")
@@ -412,7 +466,7 @@ def main():
     ap.add_argument("--prewarm-s", type=float, default=1.0,
                     help="seconds of untimed steps before the warmup steps (GPU clock ramp-up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "ragged", "copy"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "ragged", "cascade", "copy"], default=None)
     ap.add_argument("--prefill-workload", type=int, default=2, choices=[2, 3])
     ap.add_argument("--decode-workload", type=int, default=4, choices=[4, 5])
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
@@ -526,6 +580,33 @@ def main():
         res["ragged_cpu"] = None if args.no_cpu_baseline else cpu_baseline_ragged(wr, r)
         del d
 
+    if args.only in (None, "cascade"):
+        wc = workloads.WORKLOADS[7]
+        log(f"[bench] generating shared-prefix workload {wc.name}")
+        r = workloads.workload_shared_prefix_inputs(wc)
+        d = dict(q=r.q.cuda(), k=r.k_pages.cuda(), v=r.v_pages.cuda(), pt=r.page_table.cuda(), sl=r.seqlens.cuda())
+        t0 = time.perf_counter()
+        plan_c = fa.fa_decode_plan_cascade(r.seqlens, r.page_table, r.num_pages, wc.Hq, wc.Hkv, r.prefix_group,
+                                           list(wc.prefix_pages))
+        plan_ms = (time.perf_counter() - t0) * 1e3
+        plan_p = fa.fa_decode_plan(r.seqlens, r.page_table, r.num_pages, wc.Hq, wc.Hkv, wc.D, fa.BF16, 0)
+        out = torch.empty_like(d["q"])
+        lse = torch.empty(d["q"].shape[:2], dtype=torch.float32, device=d["q"].device)
+        casc = lambda: fa.fa_decode_run(plan_c, d["q"], d["k"], d["v"], d["pt"], d["sl"], plan_c.num_splits,  # noqa: E731
+                                        out, lse, None, None, wc.scale, stream)
+        plain = lambda: fa.fa_decode_run(plan_p, d["q"], d["k"], d["v"], d["pt"], d["sl"], plan_p.num_splits,  # noqa: E731
+                                         out, lse, None, None, wc.scale, stream)
+        t_c = time_calls(casc, args.steps, args.warmup, stream, args.prewarm_s)
+        t_p = time_calls(plain, args.steps, args.warmup, stream, min(args.prewarm_s, 0.3))
+        L = r.seqlens.numpy()
+        res["cascade"] = dict(c=t_c, p=t_p, w=wc, bytes=cascade_bytes(L, r.prefix_group.numpy(), list(wc.prefix_pages), wc),
+                              plain_bytes=decode_bytes(L, workloads.DecodeWorkload(7, "", wc.B, wc.Hq, wc.Hkv, wc.D, "bf16")),
+                              plan=dict(plan_ms=round(plan_ms, 3), num_splits=plan_c.num_splits, pages=int(r.num_pages),
+                                        total_tokens=int(L.sum())))
+        log(f"[bench] cascade median {statistics.median(t_c):.4f} ms, plain decode median {statistics.median(t_p):.4f} ms")
+        res["cascade_cpu"] = None if args.no_cpu_baseline else cpu_baseline_cascade(wc, r)
+        del d
+
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic"}
@@ -590,11 +671,39 @@ def main():
             line["roofline"] = rag["roofline"]
             line["cpu_baseline"] = rag["cpu_baseline"]
             ms_step = t_run + t_app
+    if "cascade" in res:
+        g = res["cascade"]
+        wc = g["w"]
+        tc, tp = statistics.mean(g["c"]), statistics.mean(g["p"])
+        gbs = g["bytes"] / (tc * 1e-3) / 1e9
+        cas = {"metric": "shared-prefix (cascade) decode HBM GB/s of its algorithmic bytes",
+               "value": round(gbs, 1), "unit": "GB/s", "ms_mean": round(tc, 5),
+               "ms_median": round(statistics.median(g["c"]), 5),
+               "plain_decode_ms_mean": round(tp, 5), "speedup_vs_plain_decode": round(tp / tc, 3),
+               "plain_decode_bytes_per_step": g["plain_bytes"],
+               "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(gbs / PEAK_HBM_GBS, 4),
+                            "traffic": read_traffic("cascade_wl7_traffic.txt",
+                                                    "exact_attention_20_amd/csrc/prefill_bf16.hip+" + DECODE_SRC),
+                            "kernel": "prefill_bf16_kernel (prefix pass) + decode_mfma_kernel + lse_merge_kernel",
+                            "bytes_per_launch": g["bytes"]},
+               "plan": g["plan"], "cpu_baseline": res["cascade_cpu"],
+               "config": {"workload": wc.name, "B": wc.B, "Hq": wc.Hq, "Hkv": wc.Hkv, "D": wc.D,
+                          "group_sizes": list(wc.group_sizes), "prefix_pages": list(wc.prefix_pages),
+                          "suffix": list(wc.suffix_lens), "page": 64}}
+        line["shared_prefix_decode"] = cas
+        if "value" not in line:
+            line.update(value=cas["value"], unit="GB/s")
+            line["roofline"] = cas["roofline"]
+            line["cpu_baseline"] = cas["cpu_baseline"]
+            ms_step = tc
     line["ms_per_step"] = round(ms_step, 5)
     cfg = {"workload": " + ".join(
         ([wp.name] if "prefill_ms" in res else []) + ([wd.name] if "decode_ms" in res else [])
         + ([res["ragged"]["w"].name] if "ragged" in res and "prefill_ms" not in res
-           and "decode_ms" not in res else []))}
+           and "decode_ms" not in res else [])
+        + ([res["cascade"]["w"].name] if "cascade" in res and "prefill_ms" not in res
+           and "decode_ms" not in res and "ragged" not in res else []))}
     if "prefill_ms" in res:
         cfg["prefill"] = dict(B=wp.B, Hq=wp.Hq, Hkv=wp.Hkv, S=wp.S, D=wp.D, causal=True, dtype="bf16")
     if "decode_ms" in res:

@@ -213,7 +213,7 @@ WorkspaceLayout workspace_layout(int n_items, int B, int Hq, int D, int num_spli
 // prefix) are planned like ordinary decode requests; their page ranges are
 // shifted past the prefix and their slots past the prefix slots, so the LSE
 // merge combines prefix and suffix partials of a request in one pass.
-constexpr int kMinPrefixChunk = 8;
+constexpr int kMinPrefixChunk = 4;
 
 int plan_cascade_host(const int32_t* seqlens, int B, int stride, int Hq, int Hkv,
                       const int32_t* group, const int32_t* prefix_pages, int n_groups, int num_cus,
