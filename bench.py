@@ -327,7 +327,7 @@ PMC_LEGS = {
     "decode_wl5": ("--only decode --decode-workload 5", ["decode_mfma_kernel", "lse_merge_kernel"], DECODE_SRC),
     "ragged_prefill_wl6": ("--only ragged", ["prefill_bf16_kernel"],
                            "exact_attention_20_amd/csrc/prefill_bf16.hip"),
-    "cascade_wl7": ("--only cascade", ["prefill_bf16_kernel", "decode_mfma_kernel", "lse_merge_kernel"],
+    "cascade_wl7": ("--only cascade --no-plain-compare", ["prefill_bf16_kernel", "decode_mfma_kernel", "lse_merge_kernel"],
                     "exact_attention_20_amd/csrc/prefill_bf16.hip+" + DECODE_SRC),
     "copy": ("--only copy", ["neg"], None),
 }
@@ -435,6 +435,36 @@ def summarize_profiles(d):
             lines.append(f"{short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                          f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f}")
+        tr = glob.glob(f"{d}/kt/*kernel_trace.csv")
+        if tr:
+            # Per leg: the legs run one after another in a fixed order, so a
+            # dispatch belongs to the leg whose first kernel came last before
+            # it; in the shared-prefix leg a split kernel right after a prefix
+            # pass (and the merge after it) belongs to the cascade, the others
+            # to the plain-decode comparison.
+            disp = sorted(csv.DictReader(open(tr[0])), key=lambda r: int(r["Start_Timestamp"]))
+            leg, prev, per = "prefill", "", {}
+            for r in disp:
+                m = re.search(r"::(\w+(?:<[^>]*>)?)\(", r["Kernel_Name"])
+                k = m.group(1) if m else r["Kernel_Name"][:60]
+                if leg == "prefill" and k.startswith(("decode_", "lse_merge")):
+                    leg = "decode"
+                if k.startswith("kv_append"):
+                    leg = "ragged"
+                if k == "prefill_bf16_kernel<8, 1, 2>":
+                    leg = "cascade"
+                sub = leg
+                if leg in ("cascade", "cascade (plain-decode comparison)"):
+                    if k.startswith("decode_"):
+                        leg = sub = "cascade" if prev == "prefill_bf16_kernel<8, 1, 2>" else "cascade (plain-decode comparison)"
+                    elif k.startswith("lse_merge"):
+                        sub = leg
+                dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                per.setdefault((sub, k), []).append(dur)
+                prev = k
+            lines.append("# per leg (dispatches attributed by order): leg | kernel | calls | average us")
+            for (lg, k), v in per.items():
+                lines.append(f"leg {lg} | {k} | {len(v)} | {statistics.mean(v):.2f}")
         bj = f"{d}/kt_bench.json"
         if os.path.exists(bj):
             txt = [x for x in open(bj).read().splitlines() if x.startswith("{")]
@@ -466,6 +496,8 @@ def main():
     ap.add_argument("--prewarm-s", type=float, default=1.0,
                     help="seconds of untimed steps before the warmup steps (GPU clock ramp-up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-plain-compare", action="store_true",
+                    help="shared-prefix leg: skip timing plain decode of the same batch")
     ap.add_argument("--only", choices=["prefill", "decode", "ragged", "cascade", "copy"], default=None)
     ap.add_argument("--prefill-workload", type=int, default=2, choices=[2, 3])
     ap.add_argument("--decode-workload", type=int, default=4, choices=[4, 5])
@@ -597,7 +629,8 @@ def main():
         plain = lambda: fa.fa_decode_run(plan_p, d["q"], d["k"], d["v"], d["pt"], d["sl"], plan_p.num_splits,  # noqa: E731
                                          out, lse, None, None, wc.scale, stream)
         t_c = time_calls(casc, args.steps, args.warmup, stream, args.prewarm_s)
-        t_p = time_calls(plain, args.steps, args.warmup, stream, min(args.prewarm_s, 0.3))
+        t_p = [float("nan")] if args.no_plain_compare else time_calls(plain, args.steps, args.warmup, stream,
+                                                                      min(args.prewarm_s, 0.3))
         L = r.seqlens.numpy()
         res["cascade"] = dict(c=t_c, p=t_p, w=wc, bytes=cascade_bytes(L, r.prefix_group.numpy(), list(wc.prefix_pages), wc),
                               plain_bytes=decode_bytes(L, workloads.DecodeWorkload(7, "", wc.B, wc.Hq, wc.Hkv, wc.D, "bf16")),
