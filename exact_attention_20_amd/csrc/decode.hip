@@ -387,8 +387,11 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(DecodeArgs a) {
   const int bh = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int b = bh / a.Hq;
+  // The split count is loaded together with the partials (not before them):
+  // the quarters below are cut from the slot capacity num_splits, every slot
+  // position is in bounds, and slots past the count are dropped by selection
+  // once it arrives, so the merge waits for one memory round trip, not two.
   const int n = a.splits_per_req[b];
-  if (n == 1) return;  // uniform across the workgroup
   const float* plse = a.part_lse + (size_t)bh * a.num_splits;
   const float* po = a.part_o + (size_t)bh * a.num_splits * kD;
   __shared__ float s_max[4], s_tot[4];
@@ -398,18 +401,26 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(DecodeArgs a) {
   // loading the LSEs and partial outputs of up to 8 splits together (one
   // memory round trip per 8 splits) and keeping a running max M, weight
   // sum and weighted output; the four states are then merged the same way.
-  const int per = (n + 3) / 4;
-  const int s0 = min(n, wave * per), s1 = min(n, s0 + per);
+  const int cap = a.num_splits;
+  const int per = (cap + 3) / 4;
+  const int s0 = min(cap, wave * per), s1 = min(cap, s0 + per);
   float M = kNegInf, tot = 0.f, o0 = 0.f, o1 = 0.f;
   for (int i = s0; i < s1; i += 8) {
     float w[8];
     float2 x[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const bool ok = i + j < s1;
-      const int sj = ok ? i + j : s0;  // past the range: a real split with weight 0
-      w[j] = ok ? plse[sj] : kNegInf;
+      const int sj = i + j < s1 ? i + j : s0;  // past the range: a slot whose weight is dropped below
+      w[j] = plse[sj];
       x[j] = *reinterpret_cast<const float2*>(po + (size_t)sj * kD + 2 * lane);
+    }
+    if (n == 1) break;  // written by its work item (uniform across the workgroup)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool ok = i + j < s1 && i + j < n;
+      w[j] = ok ? w[j] : kNegInf;  // unused slots may hold anything, NaN included
+      x[j].x = ok ? x[j].x : 0.f;
+      x[j].y = ok ? x[j].y : 0.f;
     }
     float mc = M;
 #pragma unroll
@@ -428,6 +439,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(DecodeArgs a) {
     }
     M = mc;
   }
+  if (n == 1) return;  // uniform across the workgroup, before any barrier
   s_o[wave][lane] = make_float2(o0, o1);
   if (lane == 0) {
     s_max[wave] = M;
