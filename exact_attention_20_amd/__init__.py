@@ -27,6 +27,7 @@ __all__ = [
     "fa_kv_append", "PrefillPlan", "fa_prefill_paged_plan", "fa_prefill_paged_run",
     "fa_prefill_paged_plan_host", "fa_prefill_paged_workspace_size", "prefill_paged",
     "fa_decode_plan_cascade", "fa_decode_plan_cascade_host", "fa_decode_cascade_workspace_size",
+    "fa_prefill_fp8_fwd", "prefill_fp8",
 ]
 
 F32, BF16, FP8_E4M3FN = 0, 1, 2
@@ -91,6 +92,8 @@ def load():
     lib.fa_prefill_paged_plan_destroy.restype = None
     lib.fa_prefill_paged_run.argtypes = [vp, vp, vp, vp, vp, vp, vp, cf, vp, vp, vp, vp]
     lib.fa_prefill_paged_run.restype = ci
+    lib.fa_prefill_fp8_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, vp]
+    lib.fa_prefill_fp8_fwd.restype = ci
     lib.fa_decode_cascade_workspace_size.argtypes = [i32p, ci, ci, ci, ci, ci, i32p, i32p, ci, ci]
     lib.fa_decode_cascade_workspace_size.restype = csz
     lib.fa_decode_plan_cascade.argtypes = [i32p, i32p, ci, ci, ci, ci, ci, ci, i32p, i32p, ci, ci, vp, csz,
@@ -474,3 +477,30 @@ def fa_decode_plan_cascade(seqlens, page_table, num_pages, Hq, Hkv, prefix_group
     _check(lib.fa_decode_plan_cascade(sp, C.cast(ptp, i32), B, stride, int(num_pages), Hq, Hkv, D, gp, pp, ng,
                                       num_cus, _ptr(ws), ws_bytes, _stream(stream), C.byref(handle), C.byref(ns)))
     return DecodePlan(handle, ws, ns.value, B, Hq, Hkv, D, BF16, keep[0])
+
+
+# ------------------------------------------------------------------ fp8 prefill
+
+def fa_prefill_fp8_fwd(q8, k8, v8, q_scale, k_scale, v_scale, out, lse, causal=True, scale=0.0, stream=None):
+    """fp8 (e4m3fn codes, uint8) prefill into caller-owned out [B,Hq,Sq,128] bf16, lse [B,Hq,Sq] fp32."""
+    lib = load()
+    for t, n in ((q8, "q"), (k8, "k"), (v8, "v")):
+        _need(t, n, torch.uint8)
+    for t, n in ((q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale"), (lse, "lse")):
+        _need(t, n, torch.float32)
+    _need(out, "out", torch.bfloat16)
+    B, Hq, Sq, D = q8.shape
+    Hkv, Sk = k8.shape[1], k8.shape[2]
+    if k8.shape != (B, Hkv, Sk, D) or v8.shape != k8.shape or out.shape != q8.shape or lse.shape != (B, Hq, Sq) \
+            or q_scale.shape != (B, Hq) or k_scale.shape != (B, Hkv) or v_scale.shape != (B, Hkv):
+        raise FAError(1, "inconsistent shapes")
+    _check(lib.fa_prefill_fp8_fwd(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
+                                  _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk, D, int(bool(causal)),
+                                  float(scale or 0.0), _stream(stream)))
+    return out, lse
+
+
+def prefill_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal=True, scale=None, stream=None):
+    out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=q8.device)
+    return fa_prefill_fp8_fwd(q8, k8, v8, q_scale, k_scale, v_scale, out, lse, causal, scale or 0.0, stream)

@@ -114,6 +114,29 @@ int fa_prefill_fwd(const void* q, const void* k, const void* v, void* out, float
   return ok();
 }
 
+int fa_prefill_fp8_fwd(const void* q, const void* k, const void* v, const float* q_scale,
+                       const float* k_scale, const float* v_scale, void* out, float* lse, int B, int Hq,
+                       int Hkv, int Sq, int Sk, int D, int causal, float scale, void* stream) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 0 || Sk < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_fp8_fwd: need B,Hq,Hkv >= 1 and Sq,Sk >= 0");
+  if (Hq > fa::kMaxHeads || Hkv > fa::kMaxHeads)
+    return fail(FA_ERR_UNSUPPORTED, "fa_prefill_fp8_fwd: Hq and Hkv must be <= %d", fa::kMaxHeads);
+  if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_fp8_fwd: Hq %% Hkv != 0 (%d, %d)", Hq, Hkv);
+  if (D != 128) return fail(FA_ERR_UNSUPPORTED, "fa_prefill_fp8_fwd: D=%d not supported (128)", D);
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_fp8_fwd: causal must be 0 or 1");
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_fp8_fwd: scale is not finite");
+  if (Sq == 0) return ok();
+  if (!q || !out || !lse || !q_scale || (Sk > 0 && (!k || !v || !k_scale || !v_scale)))
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_fp8_fwd: null pointer");
+  if ((long long)Sk * 128 > 0x7fffffffLL)
+    return fail(FA_ERR_UNSUPPORTED, "fa_prefill_fp8_fwd: Sk * 128 must fit in 31 bits");
+  const float sc = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)D));
+  hipError_t e = fa::launch_prefill_fp8(q, k, v, q_scale, k_scale, v_scale, out, lse, B, Hq, Hkv, Sq, Sk, causal,
+                                        sc, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fa_prefill_fp8_fwd launch");
+  return ok();
+}
+
 static int check_decode_shape(int B, int Hq, int Hkv, int D) {
   if (B < 1 || Hq < 1 || Hkv < 1)
     return fail(FA_ERR_INVALID_ARGUMENT, "decode: need B, Hq, Hkv >= 1");

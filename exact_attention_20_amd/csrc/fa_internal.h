@@ -43,6 +43,10 @@ struct PrefillArgs {
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 
+hipError_t launch_prefill_fp8(const void* q, const void* k, const void* v, const float* q_scale,
+                              const float* k_scale, const float* v_scale, void* out, float* lse, int B,
+                              int Hq, int Hkv, int Sq, int Sk, int causal, float scale, hipStream_t s);
+
 // Query rows per work item of the bf16 prefill kernel (ragged plan unit).
 constexpr int kPrefillRows = 256;
 hipError_t launch_prefill_paged_bf16(const PrefillArgs& a, int n_items, hipStream_t s);

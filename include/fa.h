@@ -95,6 +95,31 @@ int fa_prefill_fwd(const void* q, const void* k, const void* v, void* out, float
                    float scale, const int32_t* kv_head_map, void* stream);
 
 /*
+ * fa_prefill_fp8_fwd -- exact attention forward with fp8 (OCP e4m3fn) inputs
+ * on the fp8 matrix cores. ("FIA / FlashAttention" Q&A, section 3: FP8
+ * inference kernels; section 1 for the method.)
+ *
+ *   q    [B, Hq,  Sq, 128]  uint8 e4m3fn codes; value = code * q_scale[b, h]
+ *   k, v [B, Hkv, Sk, 128]  uint8 e4m3fn codes; value = code * k_scale / v_scale[b, g]
+ *   q_scale [B, Hq], k_scale / v_scale [B, Hkv]  fp32 device arrays, finite and > 0
+ *   out  [B, Hq, Sq, 128] bf16 (nearest even), lse [B, Hq, Sq] fp32 natural log
+ *   causal, scale as for fa_prefill_fwd (bottom-right mask; <= 0 selects 1/sqrt(128));
+ *   query head h reads KV head h / (Hq / Hkv).
+ * Both products run on the fp8 matrix cores with fp32 accumulation: the
+ * scores are exact for the dequantised inputs up to fp32 rounding, the
+ * softmax weights P are rounded to e4m3 (nearest even) for the P V product,
+ * and O is divided by the fp32 sum of the unrounded weights. Each weight
+ * carries a relative error of at most 2^-4 before normalisation, so
+ * |O - O_exact| <= 2^-4 * sum_j w_j |v_j| (plus bf16 rounding) per element,
+ * with w the exact weights; the LSE is exact up to fp32 rounding.
+ * Limits: D = 128; Sk * 128 < 2^31.
+ */
+int fa_prefill_fp8_fwd(const void* q, const void* k, const void* v, const float* q_scale,
+                       const float* k_scale, const float* v_scale, void* out, float* lse, int B,
+                       int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale,
+                       void* stream);
+
+/*
  * Paged Flash-Decoding: plan once per batch composition, then run.
  * ("FIA / FlashAttention" Q&A, section 2: plan preprocesses ragged lengths
  * and balances load, run executes the batch; "Flash Attention & Paged

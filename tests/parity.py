@@ -57,3 +57,41 @@ def check(name, o_gpu, o_ref, lse_gpu, lse_ref, gate):
         assert m["rel_rms"] <= g["rel_rms"], f"{name}: rel_rms {m['rel_rms']:.3e} > {g['rel_rms']}"
     assert m["lse_abs"] <= g["lse_abs"], f"{name}: lse_abs {m['lse_abs']:.3e} > {g['lse_abs']}"
     return m
+
+
+def fp8_weight_bound(q, k, v, scale, causal, rows=None):
+    """Per-element bound on |O_gpu - O| when the softmax weights enter P V as
+    e4m3 (round to nearest even) and O is divided by the sum of the unrounded
+    weights. In the frame of the row's true max, p_j = exp(s_j - max) <= 1;
+    the kernel's (lazy) frame only scales p up, which never increases the
+    relative error. An e4m3 value carries relative error <= 2^-4 when normal
+    (p >= 2^-6) and absolute error <= 2^-10 when subnormal, so
+        |O_gpu - O| <= sum_j max(2^-4 p_j, 2^-10) |v_j| / sum_j p_j.
+    ``q`` [Sq, D], ``k``/``v`` [Sk, D] float64 (one head). Returns [R, D]."""
+    import oracle
+    Sq, Sk = q.shape[0], k.shape[0]
+    rows = np.arange(Sq) if rows is None else np.asarray(rows)
+    s = oracle.scores(q[rows], k, scale)
+    ok = oracle.causal_allowed(rows, Sq, Sk) if causal else np.ones_like(s, dtype=bool)
+    s = np.where(ok, s, -np.inf)
+    mx = s.max(axis=1, keepdims=True)
+    p = np.where(ok, np.exp(s - np.where(np.isfinite(mx), mx, 0.0)), 0.0)
+    w = np.where(ok, np.maximum(p * 2.0 ** -4, 2.0 ** -10), 0.0)
+    den = p.sum(axis=1, keepdims=True)
+    return (w @ np.abs(v)) / np.where(den > 0, den, 1.0)
+
+
+def check_fp8_prefill(name, o_gpu, o_ref, bound, lse_gpu, lse_ref):
+    """fp8 prefill gate: every element within its weight-rounding bound plus
+    bf16 output rounding (2^-8 |O|) and fp32 slack (1e-5); LSE within 1e-3."""
+    o_gpu, o_ref = np.asarray(o_gpu, np.float64), np.asarray(o_ref, np.float64)
+    m = metrics(o_gpu, o_ref, lse_gpu, lse_ref)
+    err = np.abs(o_gpu - o_ref)
+    lim = np.asarray(bound) + 2.0 ** -8 * np.abs(o_ref) + 1e-5
+    ratio = float((err / lim).max(initial=0.0))
+    say(f"[parity] {name}: max_abs={m['max_abs']:.3e} rel_rms={m['rel_rms']:.3e} lse_abs={m['lse_abs']:.3e} "
+        f"max(err/bound)={ratio:.3f} gate=fp8-prefill")
+    assert np.all(np.isfinite(o_gpu)), f"{name}: non-finite output"
+    assert ratio <= 1.0, f"{name}: error exceeds the fp8 weight-rounding bound (ratio {ratio:.3f})"
+    assert m["lse_abs"] <= 1e-3, f"{name}: lse_abs {m['lse_abs']:.3e} > 1e-3"
+    return m, ratio

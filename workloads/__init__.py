@@ -51,7 +51,7 @@ class PrefillWorkload:
     Hkv: int
     S: int
     D: int
-    dtype: str  # "f32" | "bf16"
+    dtype: str  # "f32" | "bf16" | "fp8" (e4m3fn codes with per-(batch, head) scales)
     causal: tuple = (True,)
 
     @property
@@ -132,6 +132,7 @@ WORKLOADS = {
                       ("loguniform", 4096, 131072)),
     6: RaggedPrefillWorkload(6, "ragged_paged_prefill_bf16_b16_hq32_hkv8_d128_new256-2048_prefix0-16384",
                              16, 32, 8, 128, ("uniform", 256, 2048), ("uniform", 0, 16384)),
+    8: PrefillWorkload(8, "causal_prefill_fp8_b4_h32_s4096_d128", 4, 32, 32, 4096, 128, "fp8", (True,)),
     7: SharedPrefixWorkload(7, "shared_prefix_decode_bf16_b64_hq32_hkv8_d128_prefix8192_suffix256-4096",
                             32, 8, 128, (64,), (128,), ("uniform", 256, 4096)),
 }
@@ -437,3 +438,27 @@ def workload_shared_prefix_inputs(w: SharedPrefixWorkload, nan_tails=True) -> Sh
     groups = np.concatenate([np.full(n, j, dtype=np.int32) for j, n in enumerate(w.group_sizes)])
     suffix = context_lengths(w.wid, w.B, w.suffix_lens)
     return shared_prefix_inputs(w.Hq, w.Hkv, w.D, groups, suffix, w.prefix_pages, w.wid, nan_tails)
+
+
+def quantise_heads_e4m3fn(x: np.ndarray):
+    """Input preparation for fp8 prefill: one fp32 scale per (batch, head) =
+    max|x| / 448 over that head (1.0 if the head is all zero), codes = OCP
+    e4m3fn round-to-nearest-even of x / scale (torch's CPU cast), as uint8.
+    ``x`` [B, H, S, D] float32. Returns (codes, scales [B, H])."""
+    amax = np.abs(x).reshape(x.shape[0], x.shape[1], -1).max(axis=2, initial=0.0).astype(np.float32)
+    scale = (amax / np.float32(448.0)).astype(np.float32)
+    scale[scale == 0] = np.float32(1.0)
+    codes = torch.from_numpy((x / scale[:, :, None, None]).astype(np.float32)).to(torch.float8_e4m3fn)
+    return codes.view(torch.uint8), torch.from_numpy(scale)
+
+
+def fp8_prefill_inputs(B, Hq, Hkv, Sq, Sk, D, wid):
+    """N(0,1) float32 Q [B,Hq,Sq,D], K/V [B,Hkv,Sk,D], quantised per head:
+    (q8, k8, v8, q_scale, k_scale, v_scale), host tensors."""
+    q = rng(wid, STREAM_Q).standard_normal(size=(B, Hq, Sq, D), dtype=np.float32)
+    k = rng(wid, STREAM_K).standard_normal(size=(B, Hkv, Sk, D), dtype=np.float32)
+    v = rng(wid, STREAM_V).standard_normal(size=(B, Hkv, Sk, D), dtype=np.float32)
+    q8, qs = quantise_heads_e4m3fn(q)
+    k8, ks = quantise_heads_e4m3fn(k)
+    v8, vs = quantise_heads_e4m3fn(v)
+    return q8, k8, v8, qs, ks, vs
