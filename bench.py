@@ -1,7 +1,7 @@
 """Benchmark of the exact-attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--prewarm-s S] [--no-cpu-baseline]
-                    [--only prefill|decode|ragged|cascade|copy] [--prefill-workload 2|3]
+                    [--only prefill|decode|ragged|cascade|fp8|copy] [--prefill-workload 2|3]
                     [--decode-workload 4|5]
 
 One step = one pass of the whole path over one synthetic batch:
@@ -16,7 +16,9 @@ new tokens (256..2048 each) into their paged caches, then fa_prefill_paged_run
 of those tokens over prefix + new keys (prefixes 0..16384), each timed on
 its own. A fourth, the ``shared_prefix_decode`` object, times the cascade
 decode of 64 requests sharing an 8192-token prefix (suffixes 256..4096)
-against plain split-KV decode of the same batch. Inputs are resident in HBM
+against plain split-KV decode of the same batch. A fifth, ``fp8_prefill``,
+times the fp8 (e4m3) causal prefill of the 4 x 32-head x 4096 shape.
+Inputs are resident in HBM
 before timing. Each leg first runs untimed for
 --prewarm-s seconds (default 1 s: GPU clocks and power reach steady state)
 and --warmup more times; each timed call is then bracketed by HIP events on
@@ -46,6 +48,7 @@ sys.path.insert(0, ROOT)
 METRIC = "causal bf16 prefill TFLOP/s (% MFMA peak); paged decode HBM GB/s (% peak)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 
 
 def prefill_bytes(w):
@@ -293,6 +296,37 @@ def cpu_baseline_cascade(w, r, budget_s=10.0):
                       f"definition), {dt:.1f} s wall, fp64 numpy, BLAS 1 thread per worker"}
 
 
+def cpu_baseline_fp8(w, q8, k8, v8, qs, ks, vs, budget_s=10.0):
+    """fp64 oracle on whole heads of the fp8 workload (dequantised inputs), threads over heads."""
+    import concurrent.futures as cf
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+
+    def one(bh):
+        b, h = bh
+        g = h // (w.Hq // w.Hkv)
+        qd = oracle.e4m3fn_to_float(q8[b, h].numpy()) * float(qs[b, h])
+        kd = oracle.e4m3fn_to_float(k8[b, g].numpy()) * float(ks[b, g])
+        vd = oracle.e4m3fn_to_float(v8[b, g].numpy()) * float(vs[b, g])
+        oracle.attention_head(qd, kd, vd, w.scale, True)
+
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1), cf.ThreadPoolExecutor(cores) as ex:
+        while done < len(heads) and time.perf_counter() - t0 < budget_s:
+            batch = heads[done:done + cores]
+            list(ex.map(one, batch))
+            done += len(batch)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.D * (w.S * (w.S + 1) // 2) * done
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {len(heads)} whole heads of the fp8 prefill workload (dequantised inputs), "
+                      f"{dt:.1f} s wall, fp64 numpy, BLAS 1 thread per worker"}
+
+
 COPY_BYTES = 1 << 30   # calibration copy: bytes read, and bytes written, per launch
 
 
@@ -329,6 +363,7 @@ PMC_LEGS = {
                            "exact_attention_20_amd/csrc/prefill_bf16.hip"),
     "cascade_wl7": ("--only cascade --no-plain-compare", ["prefill_bf16_kernel", "decode_mfma_kernel", "lse_merge_kernel"],
                     "exact_attention_20_amd/csrc/prefill_bf16.hip+" + DECODE_SRC),
+    "prefill_fp8_wl8": ("--only fp8", ["prefill_fp8_kernel"], "exact_attention_20_amd/csrc/prefill_fp8.hip"),
     "copy": ("--only copy", ["neg"], None),
 }
 PMC_RUN = "--steps 3 --warmup 1 --prewarm-s 0 --no-cpu-baseline"
@@ -391,7 +426,9 @@ def summarize_profiles(d):
         wk, _ = _pmc_means(f"{d}/pmc_{leg}_WRITE_SIZE", names)
         wid = int(leg.rsplit("wl", 1)[1])
         w = workloads.WORKLOADS[wid]
-        if leg.startswith("prefill"):
+        if leg.startswith("prefill_fp8"):
+            alg = w.B * w.S * w.D * (w.Hq + 2 * w.Hkv) + 2 * w.B * w.Hq * w.S * w.D + 4 * w.B * w.Hq * w.S
+        elif leg.startswith("prefill"):
             alg = prefill_bytes(w)
         elif leg.startswith("cascade"):
             x = workloads.workload_shared_prefix_inputs(w)
@@ -498,7 +535,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-plain-compare", action="store_true",
                     help="shared-prefix leg: skip timing plain decode of the same batch")
-    ap.add_argument("--only", choices=["prefill", "decode", "ragged", "cascade", "copy"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "ragged", "cascade", "fp8", "copy"], default=None)
     ap.add_argument("--prefill-workload", type=int, default=2, choices=[2, 3])
     ap.add_argument("--decode-workload", type=int, default=4, choices=[4, 5])
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
@@ -640,6 +677,20 @@ def main():
         res["cascade_cpu"] = None if args.no_cpu_baseline else cpu_baseline_cascade(wc, r)
         del d
 
+    if args.only in (None, "fp8"):
+        w8 = workloads.WORKLOADS[8]
+        log(f"[bench] generating fp8 prefill workload {w8.name}")
+        q8, k8, v8, qs, ks, vs = workloads.fp8_prefill_inputs(w8.B, w8.Hq, w8.Hkv, w8.S, w8.S, w8.D, w8.wid)
+        d = [x.cuda() for x in (q8, k8, v8, qs, ks, vs)]
+        out = torch.empty(q8.shape, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(q8.shape[:3], dtype=torch.float32, device="cuda")
+        f8 = lambda: fa.fa_prefill_fp8_fwd(*d, out, lse, True, w8.scale, stream)  # noqa: E731
+        t = time_calls(f8, args.steps, args.warmup, stream, args.prewarm_s)
+        res["fp8"] = dict(t=t, w=w8)
+        log(f"[bench] fp8 prefill median {statistics.median(t):.4f} ms")
+        res["fp8_cpu"] = None if args.no_cpu_baseline else cpu_baseline_fp8(w8, q8, k8, v8, qs, ks, vs)
+        del d
+
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic"}
@@ -730,6 +781,28 @@ def main():
             line["roofline"] = cas["roofline"]
             line["cpu_baseline"] = cas["cpu_baseline"]
             ms_step = tc
+    if "fp8" in res:
+        g = res["fp8"]
+        w8 = g["w"]
+        t8 = statistics.mean(g["t"])
+        flops = prefill_flops(w8)
+        tf = flops / (t8 * 1e-3) / 1e12
+        f8o = {"metric": "causal fp8 (e4m3) prefill TFLOP/s", "value": round(tf, 2), "unit": "TFLOP/s",
+               "ms_mean": round(t8, 5), "ms_median": round(statistics.median(g["t"]), 5),
+               "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                            "traffic": read_traffic("prefill_fp8_wl8_traffic.txt",
+                                                    "exact_attention_20_amd/csrc/prefill_fp8.hip"),
+                            "kernel": "prefill_fp8_kernel", "flops_per_launch": flops},
+               "cpu_baseline": res["fp8_cpu"],
+               "config": {"workload": w8.name, "B": w8.B, "Hq": w8.Hq, "Hkv": w8.Hkv, "S": w8.S, "D": w8.D,
+                          "causal": True, "dtype": "fp8 e4m3fn, per-(batch, head) scales"}}
+        line["fp8_prefill"] = f8o
+        if "value" not in line:
+            line.update(value=f8o["value"], unit="TFLOP/s", dtype="fp8")
+            line["roofline"] = f8o["roofline"]
+            line["cpu_baseline"] = f8o["cpu_baseline"]
+            ms_step = t8
     line["ms_per_step"] = round(ms_step, 5)
     cfg = {"workload": " + ".join(
         ([wp.name] if "prefill_ms" in res else []) + ([wd.name] if "decode_ms" in res else [])

@@ -32,6 +32,8 @@
 //  * LDS rows are 128 bytes with their 16-byte units XOR-swizzled per row
 //    (different functions for K and V, matched to their read patterns) so the
 //    lanes of one read pass use distinct banks.
+#include <type_traits>
+
 #include "fa_internal.h"
 #include "hip_common.h"
 
@@ -226,8 +228,10 @@ void prefill_fp8_kernel(Fp8Args a, int n_qtiles, int nbh) {
       m = mn;
     }
   };
-  // P = exp2(s*c - m) -> e4m3 bytes (byte 16*h2 + i), fp32 sums, O^T += V^T P^T.
-  auto exp_pv = [&](int vbuf, const f32x16_t (&s)[2]) {
+  // P = exp2(s*c - m) -> e4m3 bytes (byte 16*h2 + i), fp32 sums, O^T += V^T P^T;
+  // with kb >= 0 the next tile's S^T from K buffer kb is computed in the same
+  // straight-line block, one QK product after each PV product.
+  auto exp_pv_qk = [&](int vbuf, const f32x16_t (&s)[2], int kb, f32x16_t (&n)[2]) {
     const float mu = m == kNegInf ? 0.f : m;
     int pw[8];
 #pragma unroll
@@ -244,6 +248,7 @@ void prefill_fp8_kernel(Fp8Args a, int n_qtiles, int nbh) {
       }
     const i32x8_t pf = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
     const char* vl = v_lds + vbuf * kTile;
+    const char* kl = k_lds + (kb < 0 ? 0 : kb) * kTile;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const i32x2_t r0 = lds_read_tr8(vl + v_off[db][0]);
@@ -252,6 +257,13 @@ void prefill_fp8_kernel(Fp8Args a, int n_qtiles, int nbh) {
       const i32x2_t r3 = lds_read_tr8(vl + v_off[db][3]);
       const i32x8_t va = {r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
       o[db] = mfma8(va, pf, o[db]);
+      if (kb >= 0) {
+        const int h2 = db >> 1, kk = db & 1;
+        const uint4 x0 = *reinterpret_cast<const uint4*>(kl + k_off[h2][kk][0]);
+        const uint4 x1 = *reinterpret_cast<const uint4*>(kl + k_off[h2][kk][1]);
+        const i32x8_t av = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        n[h2] = kk == 0 ? mfma8_first(av, qreg[kk]) : mfma8(av, qreg[kk], n[h2]);
+      }
     }
   };
 
@@ -272,16 +284,48 @@ void prefill_fp8_kernel(Fp8Args a, int n_qtiles, int nbh) {
   if (n_kt > 0 && active(0)) qk(0, sc);
   __syncthreads();
 
-  for (int t = 0; t < n_kt; ++t) {
+  // Tiles below the whole workgroup's diagonal and inside Sk need no mask:
+  // a branch-free main loop, unrolled by two so the two score arrays swap
+  // roles (no copies) and the buffer parity is a compile-time constant. The
+  // next tile's scores are computed even past the last tile (from a stale
+  // buffer, then discarded).
+  int n_main = Sk / kBc;
+  if (a.causal) n_main = min(n_main, max(0, (q0 + off + 1) / kBc));
+  n_main = min(n_main, n_kt);
+  auto main_step = [&](auto par, int t, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
+    constexpr int PAR = decltype(par)::value;
+    prefetch(t);
+    update_max(cur);
+    exp_pv_qk(PAR, cur, 1 - PAR, nxt);
+    wait_loads();
+    __syncthreads();
+  };
+  int t = 0;
+  {
+    f32x16_t sn[2];
+    for (; t + 1 < n_main; t += 2) {
+      main_step(std::integral_constant<int, 0>{}, t, sc, sn);
+      main_step(std::integral_constant<int, 1>{}, t + 1, sn, sc);
+    }
+    if (t < n_main) {
+      main_step(std::integral_constant<int, 0>{}, t, sc, sn);
+      sc[0] = sn[0];
+      sc[1] = sn[1];
+      ++t;
+    }
+  }
+  // Diagonal and ragged-tail tiles: masked, per-wavefront skipping.
+  for (; t < n_kt; ++t) {
     f32x16_t sn[2];
     prefetch(t);
     const bool use = active(t);
     const bool next = t + 1 < n_kt && active(t + 1);
-    if (next) qk((t + 1) & 1, sn);
     if (use) {
       mask(t, sc);
       update_max(sc);
-      exp_pv(t & 1, sc);
+      exp_pv_qk(t & 1, sc, next ? (t + 1) & 1 : -1, sn);
+    } else if (next) {
+      qk((t + 1) & 1, sn);
     }
     if (next) {
       sc[0] = sn[0];
