@@ -490,6 +490,8 @@ def summarize_profiles(d):
                     leg = "ragged"
                 if k == "prefill_bf16_kernel<8, 1, 2>":
                     leg = "cascade"
+                if k.startswith("prefill_fp8"):
+                    leg = "fp8"
                 sub = leg
                 if leg in ("cascade", "cascade (plain-decode comparison)"):
                     if k.startswith("decode_"):
@@ -513,6 +515,8 @@ def summarize_profiles(d):
                     lines.append(f"bench decode step ms_mean: {b['decode'].get('ms_mean')}")
                 if "shared_prefix_decode" in b:
                     lines.append(f"bench shared-prefix decode step ms_mean: {b['shared_prefix_decode'].get('ms_mean')}")
+                if "fp8_prefill" in b:
+                    lines.append(f"bench fp8 prefill launch ms_mean: {b['fp8_prefill'].get('ms_mean')}")
                 if "ragged_prefill" in b:
                     rg = b["ragged_prefill"]
                     lines.append(f"bench ragged paged prefill launch ms_mean: {rg.get('ms_mean')}")
