@@ -14,6 +14,7 @@ live in ``tests/test_oracle_pins.py``; none of its functions is unpinned.
 from .attention import (  # noqa: F401
     NEG_INF,
     attention_head,
+    attention_head_backward,
     causal_allowed,
     e4m3fn_to_float,
     gather_pages,
@@ -24,6 +25,7 @@ from .attention import (  # noqa: F401
     paged_prefill,
     paged_prefill_request,
     prefill,
+    prefill_backward,
     scores,
     softmax_rows,
 )

@@ -19,6 +19,13 @@ Sources (titles of the pages, with the part used):
         [1,H,seq,d], scores / sqrt(head_dim), softmax, weights @ V).
   [ARC] "FlashAttention breakthrough architecture" article, "paged storage
         system" (64-token blocks behind a page table).
+  [FBW] the backward pass: "Flash Attention & Paged Attention" blog,
+        "1. FlashAttention" (recomputation: the backward does not keep the
+        N x N matrix but recomputes the attention gradients from the small
+        statistics the forward saved); "FasterTransformer vs FlashAttention",
+        section 3 (recomputation trades compute for memory); "FIA /
+        FlashAttention" Q&A, section 3's table (FlashAttention's backward is
+        complete and needed for training).
   [FPF] "Flash Attention & Paged Attention" blog, "FA and the prefill phase"
         (prefill attends over the whole prompt and stores the computed K and V
         in device memory as the initial KV cache).
@@ -310,3 +317,51 @@ def paged_prefill(q, k_pages, v_pages, page_table, seqlens, cu_seqlens_q, scale)
         O[s:e], LSE[s:e] = paged_prefill_request(q[s:e], k_pages, v_pages, page_table[b],
                                                  int(seqlens[b]), scale)
     return O, LSE
+
+
+# --------------------------------------------------------------------------
+# Backward: gradients of O = softmax(scale Q K^T) V with respect to Q, K, V.
+# --------------------------------------------------------------------------
+
+def attention_head_backward(q, k, v, do, scale, causal=False):
+    """Gradients of one head ([FBW]) by the chain rule on the definition.
+
+    With P the row softmax of the (masked) scores and O = P V, for an upstream
+    gradient dO:  dV = P^T dO;  dP = dO V^T;  dS = P * (dP - rowsum(dO * O))
+    (the softmax Jacobian applied row by row);  dQ = scale dS K;
+    dK = scale dS^T Q. Masked entries have P = 0 and so no gradient. Rows with
+    no visible key contribute nothing. All float64. Returns (dQ, dK, dV).
+    """
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    Sq, Sk = q.shape[0], k.shape[0]
+    s = scores(q, k, scale)
+    if causal:
+        s = np.where(causal_allowed(np.arange(Sq), Sq, Sk), s, NEG_INF)
+    P, _, _ = softmax_rows(s)
+    o = P @ v
+    dv = P.T @ do
+    dp = do @ v.T
+    Di = np.sum(do * o, axis=1)
+    ds = P * (dp - Di[:, None])
+    return float(scale) * (ds @ k), float(scale) * (ds.T @ q), dv
+
+
+def prefill_backward(q, k, v, do, scale, causal):
+    """Gradients over BHSD tensors: dQ [B, Hq, Sq, D], dK/dV [B, Hkv, Sk, D].
+
+    Query head h reads KV head h // (Hq / Hkv); a KV head's gradient is the sum
+    over the query heads that read it.
+    """
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    dq = np.zeros((B, Hq, Sq, D))
+    dk = np.zeros((B, Hkv, Sk, D))
+    dv = np.zeros((B, Hkv, Sk, v.shape[3]))
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            a, bb, c = attention_head_backward(q[b, h], k[b, g], v[b, g], do[b, h], scale, causal)
+            dq[b, h] = a
+            dk[b, g] += bb
+            dv[b, g] += c
+    return dq, dk, dv

@@ -545,4 +545,58 @@ def pin_shared_prefix_cascade():
             _close(ml, LSE[b, h], 1e-12, f"cascade LSE b={b} h={h}")
 
 
+# --------------------------------------------------------------------------
+# Backward
+# --------------------------------------------------------------------------
+
+def pin_backward_torch_autograd():
+    """dQ, dK, dV equal torch autograd through CPU SDPA in float64 (causal and not, GQA expanded)."""
+    g = _rng(30)
+    B, Hq, Hkv, S, D = 1, 4, 2, 19, 8
+    q, k, v, do = (g.standard_normal(s) for s in ((B, Hq, S, D), (B, Hkv, S, D), (B, Hkv, S, D), (B, Hq, S, D)))
+    for causal in (False, True):
+        dq, dk, dv = A.prefill_backward(q, k, v, do, 0.37, causal)
+        tq = torch.from_numpy(q).requires_grad_()
+        tk = torch.from_numpy(k).requires_grad_()
+        tv = torch.from_numpy(v).requires_grad_()
+        o = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk.repeat_interleave(Hq // Hkv, dim=1), tv.repeat_interleave(Hq // Hkv, dim=1),
+            is_causal=causal, scale=0.37)
+        o.backward(torch.from_numpy(do))
+        _close(dq, tq.grad.numpy(), 1e-12, f"autograd dQ causal={causal}")
+        _close(dk, tk.grad.numpy(), 1e-12, f"autograd dK causal={causal}")
+        _close(dv, tv.grad.numpy(), 1e-12, f"autograd dV causal={causal}")
+
+
+def pin_backward_finite_differences():
+    """Central differences of L = sum(dO * O) along random directions match the
+    gradients' inner products (brute force on a tiny head, Sq != Sk, causal)."""
+    g = _rng(31)
+    Sq, Sk, D = 3, 5, 4
+    q, k, v, do = g.standard_normal((Sq, D)), g.standard_normal((Sk, D)), g.standard_normal((Sk, D)), g.standard_normal((Sq, D))
+    dq, dk, dv = A.attention_head_backward(q, k, v, do, 0.8, True)
+    f = lambda q_, k_, v_: float(np.sum(do * A.attention_head(q_, k_, v_, 0.8, True)[0]))  # noqa: E731
+    eps = 1e-6
+    for name, grad, idx in (("dQ", dq, 0), ("dK", dk, 1), ("dV", dv, 2)):
+        u = g.standard_normal(grad.shape)
+        args_p = [q.copy(), k.copy(), v.copy()]
+        args_m = [q.copy(), k.copy(), v.copy()]
+        args_p[idx] += eps * u
+        args_m[idx] -= eps * u
+        fd = (f(*args_p) - f(*args_m)) / (2 * eps)
+        _close(fd, np.sum(grad * u), 1e-7, f"finite differences {name}")
+
+
+def pin_backward_gqa_sum():
+    """A shared KV head's gradient is the sum of the MHA gradients of the query heads that read it."""
+    g = _rng(32)
+    B, Hq, Hkv, S, D = 1, 4, 2, 7, 4
+    q, k, v, do = (g.standard_normal(s) for s in ((B, Hq, S, D), (B, Hkv, S, D), (B, Hkv, S, D), (B, Hq, S, D)))
+    _, dk, dv = A.prefill_backward(q, k, v, do, 0.5, True)
+    ke, ve = np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1)
+    _, dke, dve = A.prefill_backward(q, ke, ve, do, 0.5, True)
+    _close(dk, dke.reshape(B, Hkv, 2, S, D).sum(axis=2), 1e-12, "GQA dK sum")
+    _close(dv, dve.reshape(B, Hkv, 2, S, D).sum(axis=2), 1e-12, "GQA dV sum")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -13,7 +13,8 @@ from oracle import attention as A
 
 _orig = {n: getattr(A, n) for n in ("scores", "causal_allowed", "softmax_rows", "attention_head",
                                     "kv_head_of", "e4m3fn_to_float", "gather_pages", "lse_merge",
-                                    "kv_append", "paged_prefill_request", "paged_prefill")}
+                                    "kv_append", "paged_prefill_request", "paged_prefill",
+                                    "attention_head_backward", "prefill_backward")}
 
 
 def _scores_no_scale(q, k, scale):
@@ -199,6 +200,41 @@ def _ragged_prefix_keys_only(q, k_pages, v_pages, page_table, seqlens, cu, scale
     return O, LSE
 
 
+def _bwd_variant(kind):
+    def f(q, k, v, do, scale, causal=False):
+        q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+        Sq, Sk = q.shape[0], k.shape[0]
+        s = A.scores(q, k, scale)
+        if causal:
+            s = np.where(A.causal_allowed(np.arange(Sq), Sq, Sk), s, -np.inf)
+        P, _, _ = A.softmax_rows(s)
+        o = P @ v
+        dv = P.T @ do
+        dp = do @ v.T
+        Di = np.sum(do * o, axis=1)
+        ds = P * (dp - Di[:, None]) if kind != "no_rowsum" else P * dp
+        sc = float(scale) if kind != "no_scale" else 1.0
+        dk = sc * (ds.T @ q) if kind != "dk_from_p" else sc * (P.T @ q)
+        return sc * (ds @ k), dk, dv
+    return f
+
+
+def _bwd_gqa_first_head(q, k, v, do, scale, causal):
+    # KV gradient taken from the first query head of each group only
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    dq = np.zeros((B, Hq, Sq, D)); dk = np.zeros((B, Hkv, Sk, D)); dv = np.zeros((B, Hkv, Sk, D))
+    for b in range(B):
+        for h in range(Hq):
+            g = A.kv_head_of(h, Hq, Hkv)
+            a, bb, c = A.attention_head_backward(q[b, h], k[b, g], v[b, g], do[b, h], scale, causal)
+            dq[b, h] = a
+            if h % (Hq // Hkv) == 0:
+                dk[b, g] = bb
+                dv[b, g] = c
+    return dq, dk, dv
+
+
 MUTANTS = {
     "scores_no_scale": ("scores", _scores_no_scale),
     "scores_sqrt_scale": ("scores", _scores_sqrt_scale),
@@ -226,6 +262,10 @@ MUTANTS = {
     "ragged_top_left_mask": ("paged_prefill_request", _ragged_top_left),
     "ragged_non_causal": ("paged_prefill_request", _ragged_non_causal),
     "ragged_prefix_keys_only": ("paged_prefill", _ragged_prefix_keys_only),
+    "bwd_no_rowsum": ("attention_head_backward", _bwd_variant("no_rowsum")),
+    "bwd_no_scale": ("attention_head_backward", _bwd_variant("no_scale")),
+    "bwd_dk_from_p": ("attention_head_backward", _bwd_variant("dk_from_p")),
+    "bwd_gqa_first_head": ("prefill_backward", _bwd_gqa_first_head),
 }
 
 
