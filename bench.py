@@ -1,7 +1,7 @@
 """Benchmark of the exact-attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--prewarm-s S] [--no-cpu-baseline]
-                    [--only prefill|decode|ragged|cascade|fp8|copy] [--prefill-workload 2|3]
+                    [--only prefill|decode|ragged|cascade|fp8|bwd|copy] [--prefill-workload 2|3]
                     [--decode-workload 4|5]
 
 One step = one pass of the whole path over one synthetic batch:
@@ -17,7 +17,8 @@ of those tokens over prefix + new keys (prefixes 0..16384), each timed on
 its own. A fourth, the ``shared_prefix_decode`` object, times the cascade
 decode of 64 requests sharing an 8192-token prefix (suffixes 256..4096)
 against plain split-KV decode of the same batch. A fifth, ``fp8_prefill``,
-times the fp8 (e4m3) causal prefill of the 4 x 32-head x 4096 shape.
+times the fp8 (e4m3) causal prefill of the 4 x 32-head x 4096 shape, and a
+sixth, ``backward``, the gradients (dQ, dK, dV) of the bf16 prefill workload.
 Inputs are resident in HBM
 before timing. Each leg first runs untimed for
 --prewarm-s seconds (default 1 s: GPU clocks and power reach steady state)
@@ -327,6 +328,35 @@ def cpu_baseline_fp8(w, q8, k8, v8, qs, ks, vs, budget_s=10.0):
                       f"{dt:.1f} s wall, fp64 numpy, BLAS 1 thread per worker"}
 
 
+def cpu_baseline_bwd(w, q, k, v, do, budget_s=10.0):
+    """fp64 oracle backward on whole heads of the workload, threads over heads."""
+    import concurrent.futures as cf
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    qn, kn, vn, dn = (x.double().numpy() for x in (q, k, v, do))
+    heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+
+    def one(bh):
+        b, h = bh
+        g = h // (w.Hq // w.Hkv)
+        oracle.attention_head_backward(qn[b, h], kn[b, g], vn[b, g], dn[b, h], w.scale, True)
+
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1), cf.ThreadPoolExecutor(cores) as ex:
+        while done < len(heads) and time.perf_counter() - t0 < budget_s:
+            batch = heads[done:done + cores]
+            list(ex.map(one, batch))
+            done += len(batch)
+    dt = time.perf_counter() - t0
+    flops = 2.5 * 4.0 * w.D * (w.S * (w.S + 1) // 2) * done
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {len(heads)} whole heads of the backward workload, {dt:.1f} s wall, "
+                      f"fp64 numpy, BLAS 1 thread per worker"}
+
+
 COPY_BYTES = 1 << 30   # calibration copy: bytes read, and bytes written, per launch
 
 
@@ -539,7 +569,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-plain-compare", action="store_true",
                     help="shared-prefix leg: skip timing plain decode of the same batch")
-    ap.add_argument("--only", choices=["prefill", "decode", "ragged", "cascade", "fp8", "copy"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "ragged", "cascade", "fp8", "bwd", "copy"], default=None)
     ap.add_argument("--prefill-workload", type=int, default=2, choices=[2, 3])
     ap.add_argument("--decode-workload", type=int, default=4, choices=[4, 5])
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
@@ -695,6 +725,21 @@ def main():
         res["fp8_cpu"] = None if args.no_cpu_baseline else cpu_baseline_fp8(w8, q8, k8, v8, qs, ks, vs)
         del d
 
+    if args.only in (None, "bwd"):
+        wb = workloads.WORKLOADS[args.prefill_workload]
+        log(f"[bench] generating backward inputs for {wb.name}")
+        q, k, v, do = workloads.backward_inputs(wb.B, wb.Hq, wb.Hkv, wb.S, wb.S, wb.D, wb.wid)
+        qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+        o, lse = fa.prefill(qd, kd, vd, causal=True, scale=wb.scale)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        ws = torch.empty(fa.fa_prefill_bwd_workspace_size(wb.B, wb.Hq, wb.S), dtype=torch.uint8, device="cuda")
+        bw = lambda: fa.fa_prefill_bwd(qd, kd, vd, o, lse, dod, dq, dk, dv, True, wb.scale, ws, stream)  # noqa: E731
+        t = time_calls(bw, args.steps, args.warmup, stream, args.prewarm_s)
+        res["bwd"] = dict(t=t, w=wb)
+        log(f"[bench] backward median {statistics.median(t):.4f} ms")
+        res["bwd_cpu"] = None if args.no_cpu_baseline else cpu_baseline_bwd(wb, q, k, v, do)
+        del qd, kd, vd, dod, o, lse, dq, dk, dv, ws
+
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic"}
@@ -807,6 +852,27 @@ def main():
             line["roofline"] = f8o["roofline"]
             line["cpu_baseline"] = f8o["cpu_baseline"]
             ms_step = t8
+    if "bwd" in res:
+        g = res["bwd"]
+        wb = g["w"]
+        tb = statistics.mean(g["t"])
+        flops = 2.5 * prefill_flops(wb)  # five products of the forward's size: S, dP, dV, dK, dQ
+        tf = flops / (tb * 1e-3) / 1e12
+        bwo = {"metric": "causal bf16 attention backward TFLOP/s (5 products counted; S and dP are recomputed)",
+               "value": round(tf, 2), "unit": "TFLOP/s", "ms_mean": round(tb, 5),
+               "ms_median": round(statistics.median(g["t"]), 5),
+               "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                            "kernel": "bwd_delta_kernel + bwd_dq_kernel + bwd_dkdv_kernel", "flops_per_launch": flops},
+               "cpu_baseline": res["bwd_cpu"],
+               "config": {"workload": wb.name + " (backward)", "B": wb.B, "Hq": wb.Hq, "Hkv": wb.Hkv, "S": wb.S,
+                          "D": wb.D, "causal": True}}
+        line["backward"] = bwo
+        if "value" not in line:
+            line.update(value=bwo["value"], unit="TFLOP/s")
+            line["roofline"] = bwo["roofline"]
+            line["cpu_baseline"] = bwo["cpu_baseline"]
+            ms_step = tb
     line["ms_per_step"] = round(ms_step, 5)
     cfg = {"workload": " + ".join(
         ([wp.name] if "prefill_ms" in res else []) + ([wd.name] if "decode_ms" in res else [])

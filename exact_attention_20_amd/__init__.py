@@ -27,7 +27,7 @@ __all__ = [
     "fa_kv_append", "PrefillPlan", "fa_prefill_paged_plan", "fa_prefill_paged_run",
     "fa_prefill_paged_plan_host", "fa_prefill_paged_workspace_size", "prefill_paged",
     "fa_decode_plan_cascade", "fa_decode_plan_cascade_host", "fa_decode_cascade_workspace_size",
-    "fa_prefill_fp8_fwd", "prefill_fp8",
+    "fa_prefill_fp8_fwd", "prefill_fp8", "fa_prefill_bwd", "fa_prefill_bwd_workspace_size", "prefill_bwd",
 ]
 
 F32, BF16, FP8_E4M3FN = 0, 1, 2
@@ -92,6 +92,10 @@ def load():
     lib.fa_prefill_paged_plan_destroy.restype = None
     lib.fa_prefill_paged_run.argtypes = [vp, vp, vp, vp, vp, vp, vp, cf, vp, vp, vp, vp]
     lib.fa_prefill_paged_run.restype = ci
+    lib.fa_prefill_bwd_workspace_size.argtypes = [ci, ci, ci]
+    lib.fa_prefill_bwd_workspace_size.restype = csz
+    lib.fa_prefill_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, vp, csz, vp]
+    lib.fa_prefill_bwd.restype = ci
     lib.fa_prefill_fp8_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, vp]
     lib.fa_prefill_fp8_fwd.restype = ci
     lib.fa_decode_cascade_workspace_size.argtypes = [i32p, ci, ci, ci, ci, ci, i32p, i32p, ci, ci]
@@ -504,3 +508,36 @@ def prefill_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal=True, scale=None, 
     out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
     lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=q8.device)
     return fa_prefill_fp8_fwd(q8, k8, v8, q_scale, k_scale, v_scale, out, lse, causal, scale or 0.0, stream)
+
+
+# ------------------------------------------------------------------ backward
+
+def fa_prefill_bwd_workspace_size(B, Hq, Sq):
+    return load().fa_prefill_bwd_workspace_size(B, Hq, Sq)
+
+
+def fa_prefill_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal=True, scale=0.0, workspace=None, stream=None):
+    """Gradients into caller-owned dq [B,Hq,Sq,128], dk/dv [B,Hkv,Sk,128] (bf16)."""
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, n, torch.bfloat16)
+    _need(lse, "lse", torch.float32)
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    if k.shape != (B, Hkv, Sk, D) or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape \
+            or dq.shape != q.shape or dk.shape != k.shape or dv.shape != k.shape or lse.shape != (B, Hq, Sq):
+        raise FAError(1, "inconsistent shapes")
+    need = lib.fa_prefill_bwd_workspace_size(B, Hq, Sq)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib.fa_prefill_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                              _ptr(dv), B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), float(scale or 0.0),
+                              _ptr(workspace), workspace.numel(), _stream(stream)))
+    return dq, dk, dv
+
+
+def prefill_bwd(q, k, v, o, lse, dout, causal=True, scale=None, stream=None):
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    return fa_prefill_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal, scale or 0.0, None, stream)

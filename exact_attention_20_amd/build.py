@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 SOURCES = ["abi.cpp", "plan.cpp", "decode.hip", "decode_mfma.hip", "prefill_f32.hip", "prefill_bf16.hip",
-           "kv_append.hip", "prefill_fp8.hip"]
+           "kv_append.hip", "prefill_fp8.hip", "prefill_bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -35,7 +35,7 @@ COMMON = [
 
 # The attention kernels never create a NaN themselves (masked scores are -inf,
 # NaN page tails are zeroed before use), so max() needs no NaN quieting.
-PER_FILE = {"prefill_bf16.hip": ["-fno-honor-nans"], "prefill_fp8.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"],
+PER_FILE = {"prefill_bf16.hip": ["-fno-honor-nans"], "prefill_fp8.hip": ["-fno-honor-nans"], "prefill_bwd.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"],
             "decode_mfma.hip": ["-fno-honor-nans"]}
 
 

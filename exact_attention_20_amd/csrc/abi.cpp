@@ -137,6 +137,41 @@ int fa_prefill_fp8_fwd(const void* q, const void* k, const void* v, const float*
   return ok();
 }
 
+size_t fa_prefill_bwd_workspace_size(int B, int Hq, int Sq) {
+  if (B < 1 || Hq < 1 || Sq < 0) return 0;
+  return ((size_t)B * Hq * (size_t)Sq * sizeof(float) + 255) / 256 * 256 + 256;
+}
+
+int fa_prefill_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk,
+                   int D, int causal, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 0 || Sk < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_bwd: need B,Hq,Hkv >= 1 and Sq,Sk >= 0");
+  if (Hq > fa::kMaxHeads || Hkv > fa::kMaxHeads)
+    return fail(FA_ERR_UNSUPPORTED, "fa_prefill_bwd: Hq and Hkv must be <= %d", fa::kMaxHeads);
+  if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_bwd: Hq %% Hkv != 0 (%d, %d)", Hq, Hkv);
+  if (D != 128) return fail(FA_ERR_UNSUPPORTED, "fa_prefill_bwd: D=%d not supported (128)", D);
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_bwd: causal must be 0 or 1");
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_bwd: scale is not finite");
+  if ((long long)std::max(Sq, Sk) * 256 > 0x7fffffffLL)
+    return fail(FA_ERR_UNSUPPORTED, "fa_prefill_bwd: Sq and Sk must be below 2^23");
+  if (Sq == 0 && Sk == 0) return ok();
+  if ((Sq > 0 && (!q || !o || !lse || !dout || !dq)) || (Sk > 0 && (!k || !v || !dk || !dv)))
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_bwd: null tensor pointer");
+  const size_t need = fa_prefill_bwd_workspace_size(B, Hq, Sq);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "fa_prefill_bwd: workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  fa::BwdLaunch l;
+  l.q = q; l.k = k; l.v = v; l.o = o; l.dO = dout; l.lse = lse;
+  l.delta = (float*)workspace;
+  l.dq = dq; l.dk = dk; l.dv = dv;
+  l.B = B; l.Hq = Hq; l.Hkv = Hkv; l.Sq = Sq; l.Sk = Sk; l.causal = causal;
+  l.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)D));
+  hipError_t e = fa::launch_attention_bwd(l, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fa_prefill_bwd launch");
+  return ok();
+}
+
 static int check_decode_shape(int B, int Hq, int Hkv, int D) {
   if (B < 1 || Hq < 1 || Hkv < 1)
     return fail(FA_ERR_INVALID_ARGUMENT, "decode: need B, Hq, Hkv >= 1");

@@ -47,6 +47,17 @@ hipError_t launch_prefill_fp8(const void* q, const void* k, const void* v, const
                               const float* k_scale, const float* v_scale, void* out, float* lse, int B,
                               int Hq, int Hkv, int Sq, int Sk, int causal, float scale, hipStream_t s);
 
+// Attention backward (bf16, D = 128): delta, dQ and dK/dV kernels.
+struct BwdLaunch {
+  const void *q, *k, *v, *o, *dO;
+  const float* lse;
+  float* delta;   // [B, Hq, Sq] workspace
+  void *dq, *dk, *dv;
+  int B, Hq, Hkv, Sq, Sk, causal;
+  float scale;
+};
+hipError_t launch_attention_bwd(const BwdLaunch& l, hipStream_t s);
+
 // Query rows per work item of the bf16 prefill kernel (ragged plan unit).
 constexpr int kPrefillRows = 256;
 hipError_t launch_prefill_paged_bf16(const PrefillArgs& a, int n_items, hipStream_t s);

@@ -1,0 +1,444 @@
+// Backward of exact attention (bf16, D = 128) on gfx950 matrix cores.
+//
+// Recomputation ("Flash Attention & Paged Attention" blog, "1. FlashAttention";
+// "FasterTransformer vs FlashAttention", section 3): the backward keeps no
+// N x N matrix; from the forward's LSE it rebuilds P = exp(scale S - LSE)
+// tile by tile, and with D_i = sum_d dO_id O_id (the row term of the softmax
+// Jacobian) it forms dS = P * (dP - D) with dP = dO V^T, then
+//   dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO.
+//
+// Three kernels, no atomics:
+//  * bwd_delta_kernel: D_i, 16 lanes per row.
+//  * bwd_dq_kernel: shaped like the forward kernel. 8 wavefronts x 32 query
+//    rows; 64-key tiles of K and V stream through LDS. Per tile,
+//    S^T = K Q^T and dP^T = V dO^T (K, V rows from LDS in the permuted row
+//    order that makes each accumulator usable as a later operand; Q and dO in
+//    registers), dS^T = P^T (dP^T - D) packed to bf16, and dQ^T += K^T dS^T
+//    with K^T from gfx950's transposing LDS read (as V^T in the forward).
+//  * bwd_dkdv_kernel: the transposed twin. 8 wavefronts x 32 keys with their
+//    K and V rows in registers; 64-row tiles of Q and dO (and their LSE, D)
+//    stream through LDS for every query head that reads this KV head. Per
+//    32-row half, S = Q K^T and dP = dO V^T (Q, dO rows in permuted order),
+//    then dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T from transposing
+//    reads.
+// S and dP are computed in both kernels (7 products instead of 5) in exchange
+// for no atomic accumulation of dQ.
+#include "bf16_mfma.h"
+#include "fa_internal.h"
+#include "hip_common.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kBc = 64;       // keys per tile (dQ kernel), query rows per tile (dK/dV kernel)
+constexpr int kRow = kD * 2;  // 256 B per bf16 row; 16-byte units XOR-swizzled by row & 15
+constexpr int kTile = kBc * kRow;  // 16 KB
+constexpr int NW = 8;
+
+struct BwdArgs {
+  const uint16_t* q;    // [B, Hq, Sq, D]
+  const uint16_t* k;    // [B, Hkv, Sk, D]
+  const uint16_t* v;
+  const uint16_t* o;    // [B, Hq, Sq, D] forward output
+  const uint16_t* dO;   // [B, Hq, Sq, D]
+  const float* lse;     // [B, Hq, Sq] forward LSE (natural log)
+  float* delta;         // [B, Hq, Sq] D_i (written by the first kernel)
+  uint16_t* dq;         // [B, Hq, Sq, D]
+  uint16_t* dk;         // [B, Hkv, Sk, D]
+  uint16_t* dv;
+  int B, Hq, Hkv, Sq, Sk, causal;
+  float scale;
+};
+
+// ---- D_i = sum_d dO_id * O_id (fp32), 16 lanes x 8 dims per row.
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int c = threadIdx.x & 15;
+  float acc = 0.f;
+  if (row < rows) {
+    const uint4 x = reinterpret_cast<const uint4*>(a.dO + row * kD)[c];
+    const uint4 y = reinterpret_cast<const uint4*>(a.o + row * kD)[c];
+    acc = dot2_bf16(x.x, y.x, acc);
+    acc = dot2_bf16(x.y, y.y, acc);
+    acc = dot2_bf16(x.z, y.z, acc);
+    acc = dot2_bf16(x.w, y.w, acc);
+  }
+  acc = row16_sum(acc);
+  if (row < rows && c == 0) a.delta[row] = acc;
+}
+
+// Direct HBM -> LDS load of a 64-row tile: 16 blocks of 1 KB, two per
+// wavefront; lane l fills LDS unit (l & 15) of row 4j + (l >> 4) with the
+// global unit that the row's swizzle stores there.
+__device__ __forceinline__ void load_rows(const __amdgpu_buffer_rsrc_t& rs, int r0, char* buf, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int j = wave * 2 + i;
+    const int r = 4 * j + (lane >> 4);
+    const int unit = (lane & 15) ^ (r & 15);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(buf + j * 1024), 16,
+                                             (r0 + r) * kRow + unit * 16, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Row-operand offsets (A operand rows in kperm order, dims 16*kk + 8*hi).
+__device__ __forceinline__ void row_offsets(int col, int hi, int (&off)[8]) {
+  const int R = kperm(col);
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) off[kk] = R * kRow + 16 * ((2 * kk + hi) ^ (R & 15));
+}
+// Transposing-read offsets (A operand rows = dims 32*db + lane%32, k = rows
+// 16*ks + 8*hi + e; add 16*ks rows): lane L of 16-lane group g addresses row
+// 8*(g>>1) + 4*r + (L>>2), dims 32*db + 16*(g&1) + 4*(L&3). With the row &
+// 15 swizzle the offset does not depend on ks.
+__device__ __forceinline__ void tr_offsets(int lane, int (&off)[4][2]) {
+  const int g = lane >> 4, L = lane & 15;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int R = 8 * (g >> 1) + 4 * r + (L >> 2);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int u = 4 * db + 2 * (g & 1) + ((L & 3) >> 1);
+      off[db][r] = R * kRow + 16 * (u ^ (R & 15)) + 8 * (L & 1);
+    }
+  }
+}
+// The two reads (rows +0..3 and +4..7 of the 8-row group) have independent
+// swizzles, hence two offsets; shifting both by 16 rows keeps them valid.
+__device__ __forceinline__ bf16x8_t tr_operand(const char* base, int off0, int off1) {
+  const uint2 v0 = lds_read_tr16(base + off0);
+  const uint2 v1 = lds_read_tr16(base + off1);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
+}
+// The same offsets in XOR form, one register each: with s = row & 15, unit
+// (2*kk + hi) ^ s sits at byte 32*(kk ^ (s>>1)) + 16*(hi ^ (s&1)), so the
+// kk-th row offset is X ^ (32*kk); the transposing offsets are Y_r ^ (64*db).
+__device__ __forceinline__ int row_base(int R, int hi) {
+  const int sw = R & 15;
+  return R * kRow + 32 * (sw >> 1) + 16 * (hi ^ (sw & 1));
+}
+__device__ __forceinline__ void tr_bases(int lane, int (&y)[2]) {
+  const int g = lane >> 4, L = lane & 15;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int R = 8 * (g >> 1) + 4 * r + (L >> 2);
+    const int c0 = 32 * (g & 1) + 16 * ((L & 3) >> 1);
+    y[r] = R * kRow + 8 * (L & 1) + (c0 ^ (16 * (R & 15)));
+  }
+}
+
+__device__ __forceinline__ bf16x8_t pack8(const f32x16_t& x, int base) {
+  return __builtin_bit_cast(bf16x8_t, make_uint4(pack_bf16x2(x[base], x[base + 1]), pack_bf16x2(x[base + 2], x[base + 3]),
+                                                 pack_bf16x2(x[base + 4], x[base + 5]), pack_bf16x2(x[base + 6], x[base + 7])));
+}
+// Store a 32 x 128 block held as C^T accumulators (lane: row `row`, dims
+// 32*db + 8*gq + 4*hi .. +3) as bf16, multiplied by f.
+__device__ __forceinline__ void store_rows(uint16_t* dst, const f32x16_t (&acc)[4], int hi, float f) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int d = 32 * db + 8 * gq + 4 * hi;
+      *reinterpret_cast<uint2*>(dst + d) = make_uint2(pack_bf16x2(acc[db][4 * gq] * f, acc[db][4 * gq + 1] * f),
+                                                      pack_bf16x2(acc[db][4 * gq + 2] * f, acc[db][4 * gq + 3] * f));
+    }
+}
+
+// ---------------------------------------------------------------- dQ
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(BwdArgs a, int n_qtiles, int nbh) {
+  __shared__ __attribute__((aligned(16))) char k_lds[2 * kTile];
+  __shared__ __attribute__((aligned(16))) char v_lds[2 * kTile];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, col = lane & 31;
+  constexpr int BR = 32 * NW;
+
+  const int L = blockIdx.x;
+  const int qt = a.causal ? (n_qtiles - 1 - L / nbh) : (L / nbh);
+  const int e = L % nbh;
+  const int G = a.Hq / a.Hkv;
+  const int bg = e % (a.B * a.Hkv), j = e / (a.B * a.Hkv);
+  const int b = bg / a.Hkv, g = bg % a.Hkv, h = g * G + j;
+  const int Sq = a.Sq, Sk = a.Sk, off = Sk - Sq;
+  const int q0 = qt * BR;
+  int kend = Sk;
+  if (a.causal) kend = min(Sk, q0 + BR + off);
+  const int n_kt = kend > 0 ? (kend + kBc - 1) / kBc : 0;
+  const size_t bh = (size_t)b * a.Hq + h, bgk = (size_t)b * a.Hkv + g;
+
+  // Q and dO of this lane's row (B operands, dims 16*kk + 8*hi), its LSE in
+  // log2 units (+inf for a row without keys, so that P = 0) and D.
+  const int qrow = q0 + 32 * wave + col;
+  bf16x8_t qreg[8], dreg[8];
+  float lse2 = __builtin_inff(), dl = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
+    if (qrow < Sq) {
+      x = *reinterpret_cast<const uint4*>(a.q + (bh * Sq + qrow) * kD + 16 * kk + 8 * hi);
+      y = *reinterpret_cast<const uint4*>(a.dO + (bh * Sq + qrow) * kD + 16 * kk + 8 * hi);
+    }
+    qreg[kk] = __builtin_bit_cast(bf16x8_t, x);
+    dreg[kk] = __builtin_bit_cast(bf16x8_t, y);
+  }
+  if (qrow < Sq) {
+    const float l = a.lse[bh * Sq + qrow];
+    lse2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
+    dl = a.delta[bh * Sq + qrow];
+  }
+  const float c = a.scale * kLog2e;
+
+  f32x16_t acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+
+  const __amdgpu_buffer_rsrc_t k_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.k + bgk * (size_t)Sk * kD), (short)0, Sk * kRow, 0x00020000);
+  const __amdgpu_buffer_rsrc_t v_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.v + bgk * (size_t)Sk * kD), (short)0, Sk * kRow, 0x00020000);
+  int r_off[8], t_off[4][2];
+  row_offsets(col, hi, r_off);
+  tr_offsets(lane, t_off);
+
+  if (n_kt > 0) {
+    load_rows(k_rs, 0, k_lds, wave, lane);
+    load_rows(v_rs, 0, v_lds, wave, lane);
+  }
+  wait_vmem();
+  __syncthreads();
+
+  for (int t = 0; t < n_kt; ++t) {
+    if (t + 1 < n_kt) {
+      load_rows(k_rs, (t + 1) * kBc, k_lds + ((t + 1) & 1) * kTile, wave, lane);
+      load_rows(v_rs, (t + 1) * kBc, v_lds + ((t + 1) & 1) * kTile, wave, lane);
+    }
+    const char* kl = k_lds + (t & 1) * kTile;
+    const char* vl = v_lds + (t & 1) * kTile;
+    // S^T = K Q^T and dP^T = V dO^T: register i of lane l, half h2, is key
+    // 32*h2 + 16*(i/8) + 8*hi + (i%8) of the tile, query row `qrow`.
+    f32x16_t s[2], dp[2];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kl + r_off[kk] + 32 * h2 * kRow);
+        const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(vl + r_off[kk] + 32 * h2 * kRow);
+        s[h2] = kk == 0 ? mfma32_first(ka, qreg[kk]) : mfma32(ka, qreg[kk], s[h2]);
+        dp[h2] = kk == 0 ? mfma32_first(va, dreg[kk]) : mfma32(va, dreg[kk], dp[h2]);
+      }
+    }
+    // P^T = exp2(S^T c - lse2) with the causal / ragged-tail mask, dS^T.
+    const int lim = a.causal ? min(Sk - 1, qrow + off) : Sk - 1;
+    bf16x8_t dsf[4];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = t * kBc + 32 * h2 + 16 * (i >> 3) + 8 * hi + (i & 7);
+        const float p = key > lim ? 0.f : fast_exp2(__builtin_fmaf(s[h2][i], c, -lse2));
+        s[h2][i] = p * (dp[h2][i] - dl);
+      }
+      dsf[2 * h2] = pack8(s[h2], 0);
+      dsf[2 * h2 + 1] = pack8(s[h2], 8);
+    }
+    // dQ^T += K^T dS^T (k = keys 16*ks + 8*hi + e).
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16x8_t kt = tr_operand(kl + 16 * ks * kRow, t_off[db][0], t_off[db][1]);
+        acc[db] = mfma32(kt, dsf[ks], acc[db]);
+      }
+    wait_vmem();
+    __syncthreads();
+  }
+  if (qrow < Sq) store_rows(a.dq + (bh * Sq + qrow) * kD, acc, hi, a.scale);
+}
+
+// ---------------------------------------------------------------- dK, dV
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
+  __shared__ __attribute__((aligned(16))) char q_lds[2 * kTile];
+  __shared__ __attribute__((aligned(16))) char o_lds[2 * kTile];  // dO
+  __shared__ __attribute__((aligned(16))) float st_lse[2][kBc];
+  __shared__ __attribute__((aligned(16))) float st_d[2][kBc];
+  __shared__ __attribute__((aligned(16))) char v_res[32 * NW * kRow];  // this workgroup's V rows
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, col = lane & 31;
+  constexpr int BK = 32 * NW;  // keys per workgroup
+
+  // Key tiles with the most query rows first (causal: the first ones).
+  const int L = blockIdx.x;
+  const int kt = a.causal ? L / nbg : (n_ktiles - 1 - L / nbg);
+  const int e = L % nbg;
+  const int b = e / a.Hkv, g = e % a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int Sq = a.Sq, Sk = a.Sk, off = Sk - Sq;
+  const int kw0 = kt * BK + 32 * wave;  // this wavefront's first key
+  const int key = kw0 + col;           // this lane's key (column)
+  const size_t bgk = (size_t)b * a.Hkv + g;
+
+  // K of this lane's key in registers (B operand of S = Q K^T, dims
+  // 16*kk + 8*hi); the workgroup's V rows resident in LDS (B operand of
+  // dP = dO V^T, read per step), rows past Sk zero.
+  bf16x8_t kreg[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (key < Sk) x = *reinterpret_cast<const uint4*>(a.k + (bgk * Sk + key) * kD + 16 * kk + 8 * hi);
+    kreg[kk] = __builtin_bit_cast(bf16x8_t, x);
+  }
+  {
+    const __amdgpu_buffer_rsrc_t vs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.v + bgk * (size_t)Sk * kD), (short)0, Sk * kRow, 0x00020000);
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) load_rows(vs, kt * BK + 64 * c4, v_res + c4 * kTile, wave, lane);
+  }
+  const int v_base = row_base(32 * wave + col, hi);  // this lane's V row in v_res
+  f32x16_t dk[4], dv[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dk[db][i] = 0.f;
+      dv[db][i] = 0.f;
+    }
+  const float c = a.scale * kLog2e;
+
+  // Query tiles that can see any key of this workgroup: rows q with
+  // q + off >= first key.
+  const int n_qt = (Sq + kBc - 1) / kBc;
+  const int qt0 = a.causal ? max(0, (kt * BK - off) / kBc) : 0;
+  const int per_head = max(0, n_qt - qt0);
+  const int n_steps = per_head * G;
+
+  const int r_base = row_base(kperm(col), hi);
+  int t_base[2];
+  tr_bases(lane, t_base);
+
+  auto issue = [&](int step, int buf) {
+    const int jh = step / per_head, qt = qt0 + step % per_head;
+    const size_t bh = (size_t)b * a.Hq + g * G + jh;
+    const __amdgpu_buffer_rsrc_t qs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.q + bh * (size_t)Sq * kD), (short)0, Sq * kRow, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ds = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.dO + bh * (size_t)Sq * kD), (short)0, Sq * kRow, 0x00020000);
+    load_rows(qs, qt * kBc, q_lds + buf * kTile, wave, lane);
+    load_rows(ds, qt * kBc, o_lds + buf * kTile, wave, lane);
+    if (wave == 0) {
+      const __amdgpu_buffer_rsrc_t ls = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(a.lse + bh * (size_t)Sq), (short)0, Sq * 4, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ls, (__attribute__((address_space(3))) void*)(&st_lse[buf][0]), 4,
+                                               (qt * kBc + lane) * 4, 0, 0, 0);
+    } else if (wave == 1) {
+      const __amdgpu_buffer_rsrc_t dsr = __builtin_amdgcn_make_buffer_rsrc(
+          a.delta + bh * (size_t)Sq, (short)0, Sq * 4, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(dsr, (__attribute__((address_space(3))) void*)(&st_d[buf][0]), 4,
+                                               (qt * kBc + lane) * 4, 0, 0, 0);
+    }
+  };
+
+  if (n_steps > 0) issue(0, 0);
+  wait_vmem();
+  __syncthreads();
+
+  for (int st = 0; st < n_steps; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < n_steps) issue(st + 1, buf ^ 1);
+    const int q0 = (qt0 + st % per_head) * kBc;
+    const char* ql = q_lds + buf * kTile;
+    const char* ol = o_lds + buf * kTile;
+#pragma unroll
+    for (int hq = 0; hq < 2; ++hq) {
+      // S = Q K^T and dP = dO V^T for rows 32*hq .. +31 of the tile: register
+      // i of lane l is row 32*hq + 16*(i/8) + 8*hi + (i%8), key `key`.
+      f32x16_t s, dp;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const int ro = (r_base ^ (32 * kk)) + 32 * hq * kRow;
+        const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(ql + ro);
+        const bf16x8_t oa = *reinterpret_cast<const bf16x8_t*>(ol + ro);
+        s = kk == 0 ? mfma32_first(qa, kreg[kk]) : mfma32(qa, kreg[kk], s);
+        const bf16x8_t vb = *reinterpret_cast<const bf16x8_t*>(v_res + (v_base ^ (32 * kk)));
+        dp = kk == 0 ? mfma32_first(oa, vb) : mfma32(oa, vb, dp);
+      }
+      // P and dS; rows past Sq, masked keys and keys past Sk give 0.
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        const int rb = 32 * hq + 16 * h8 + 8 * hi;  // first row of these 8 registers
+        const float4 l0 = *reinterpret_cast<const float4*>(&st_lse[buf][rb]);
+        const float4 l1 = *reinterpret_cast<const float4*>(&st_lse[buf][rb + 4]);
+        const float4 d0 = *reinterpret_cast<const float4*>(&st_d[buf][rb]);
+        const float4 d1 = *reinterpret_cast<const float4*>(&st_d[buf][rb + 4]);
+        const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+        const float dvv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int i = 8 * h8 + x;
+          const int q = q0 + rb + x;
+          const bool ok = q < Sq && key < Sk && (!a.causal || key <= q + off) && lv[x] != kNegInf;
+          const float p = ok ? fast_exp2(__builtin_fmaf(s[i], c, -lv[x] * kLog2e)) : 0.f;
+          s[i] = p;
+          dp[i] = p * (dp[i] - dvv[x]);
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS (k = rows 16*ks + 8*hi + e of this half).
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8_t pf = pack8(s, 8 * ks);
+        const bf16x8_t sf = pack8(dp, 8 * ks);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int ro = (32 * hq + 16 * ks) * kRow;
+          const int o0 = t_base[0] ^ (64 * db), o1 = t_base[1] ^ (64 * db);
+          dv[db] = mfma32(tr_operand(ol + ro, o0, o1), pf, dv[db]);
+          dk[db] = mfma32(tr_operand(ql + ro, o0, o1), sf, dk[db]);
+        }
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+  if (key < Sk) {
+    store_rows(a.dk + (bgk * Sk + key) * kD, dk, hi, a.scale);
+    store_rows(a.dv + (bgk * Sk + key) * kD, dv, hi, 1.f);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attention_bwd(const BwdLaunch& l, hipStream_t s) {
+  BwdArgs a;
+  a.q = reinterpret_cast<const uint16_t*>(l.q);
+  a.k = reinterpret_cast<const uint16_t*>(l.k);
+  a.v = reinterpret_cast<const uint16_t*>(l.v);
+  a.o = reinterpret_cast<const uint16_t*>(l.o);
+  a.dO = reinterpret_cast<const uint16_t*>(l.dO);
+  a.lse = l.lse;
+  a.delta = l.delta;
+  a.dq = reinterpret_cast<uint16_t*>(l.dq);
+  a.dk = reinterpret_cast<uint16_t*>(l.dk);
+  a.dv = reinterpret_cast<uint16_t*>(l.dv);
+  a.B = l.B; a.Hq = l.Hq; a.Hkv = l.Hkv; a.Sq = l.Sq; a.Sk = l.Sk; a.causal = l.causal;
+  a.scale = l.scale;
+  const int64_t rows = (int64_t)l.B * l.Hq * l.Sq;
+  if (rows > 0) {
+    hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a);
+    const int n_qtiles = (l.Sq + 32 * NW - 1) / (32 * NW);
+    const int nbh = l.B * l.Hq;
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((int64_t)n_qtiles * nbh)), dim3(64 * NW), 0, s, a, n_qtiles, nbh);
+  }
+  if (l.Sk > 0) {
+    const int n_ktiles = (l.Sk + 32 * NW - 1) / (32 * NW);
+    const int nbg = l.B * l.Hkv;
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)((int64_t)n_ktiles * nbg)), dim3(64 * NW), 0, s, a, n_ktiles, nbg);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fa

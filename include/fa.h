@@ -120,6 +120,34 @@ int fa_prefill_fp8_fwd(const void* q, const void* k, const void* v, const float*
                        void* stream);
 
 /*
+ * fa_prefill_bwd -- gradients of the bf16 prefill: dQ, dK, dV from dO.
+ * ("Flash Attention & Paged Attention" blog, "1. FlashAttention" and
+ * "FasterTransformer vs FlashAttention", section 3: recomputation -- the
+ * backward rebuilds the attention weights from the LSE the forward saved
+ * instead of storing the N x N matrix; "FIA / FlashAttention" Q&A, section
+ * 3: FlashAttention's backward is what training needs.)
+ *
+ *   q, k, v   as given to fa_prefill_fwd (bf16, D = 128, contiguous BHSD)
+ *   o, lse    fa_prefill_fwd's outputs for them (same causal flag and scale)
+ *   dout      [B, Hq, Sq, 128] bf16 upstream gradient dO
+ *   dq        [B, Hq, Sq, 128] bf16, written
+ *   dk, dv    [B, Hkv, Sk, 128] bf16, written; a KV head's gradient sums the
+ *             query heads h with h / (Hq / Hkv) equal to it
+ *   workspace device buffer of >= fa_prefill_bwd_workspace_size(B, Hq, Sq)
+ *             bytes (holds D_i = sum_d dO_id O_id)
+ * dS = P * (dP - D) with P = exp(scale S - LSE), dP = dO V^T; dQ = scale dS K,
+ * dK = scale dS^T Q, dV = P^T dO; fp32 accumulation, bf16 products (P and dS
+ * are rounded to bf16 for the matrix cores). Three kernels on `stream`, no
+ * atomics. Limits: D = 128, Hq % Hkv == 0, Sq and Sk below 2^23.
+ */
+size_t fa_prefill_bwd_workspace_size(int B, int Hq, int Sq);
+
+int fa_prefill_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
+                   int Sk, int D, int causal, float scale, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
  * Paged Flash-Decoding: plan once per batch composition, then run.
  * ("FIA / FlashAttention" Q&A, section 2: plan preprocesses ragged lengths
  * and balances load, run executes the batch; "Flash Attention & Paged

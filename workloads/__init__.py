@@ -40,6 +40,7 @@ PAGE = 64  # tokens per KV page
 
 STREAM_LENGTHS, STREAM_PERM, STREAM_Q, STREAM_K, STREAM_V = 0, 1, 2, 3, 4
 STREAM_PREFIX, STREAM_KNEW, STREAM_VNEW = 5, 6, 7
+STREAM_DO = 8
 
 
 @dataclass(frozen=True)
@@ -462,3 +463,10 @@ def fp8_prefill_inputs(B, Hq, Hkv, Sq, Sk, D, wid):
     k8, ks = quantise_heads_e4m3fn(k)
     v8, vs = quantise_heads_e4m3fn(v)
     return q8, k8, v8, qs, ks, vs
+
+
+def backward_inputs(B, Hq, Hkv, Sq, Sk, D, wid):
+    """Q, K, V as prefill_inputs plus an upstream gradient dO [B, Hq, Sq, D], all N(0,1) bf16."""
+    q, k, v = prefill_inputs(B, Hq, Hkv, Sq, Sk, D, "bf16", wid)
+    do = normal(wid, STREAM_DO, (B, Hq, Sq, D), "bf16")
+    return q, k, v, do
