@@ -70,13 +70,14 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
   if (row < rows && c == 0) a.delta[row] = acc;
 }
 
-// Direct HBM -> LDS load of a 64-row tile: 16 blocks of 1 KB, two per
-// wavefront; lane l fills LDS unit (l & 15) of row 4j + (l >> 4) with the
+// Direct HBM -> LDS load of a 64-row tile: 16 blocks of 1 KB shared by the
+// W wavefronts; lane l fills LDS unit (l & 15) of row 4j + (l >> 4) with the
 // global unit that the row's swizzle stores there.
+template <int W = NW>
 __device__ __forceinline__ void load_rows(const __amdgpu_buffer_rsrc_t& rs, int r0, char* buf, int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int j = wave * 2 + i;
+  for (int i = 0; i < 16 / W; ++i) {
+    const int j = wave * (16 / W) + i;
     const int r = 4 * j + (lane >> 4);
     const int unit = (lane & 15) ^ (r & 15);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(buf + j * 1024), 16,
@@ -262,15 +263,20 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles, int nbh) {
 }
 
 // ---------------------------------------------------------------- dK, dV
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// KW wavefronts of 32 keys each, two per SIMD. (Four wavefronts, one per
+// SIMD with the full register file, avoid the few spills of this
+// configuration but measured 16% slower overall.)
+constexpr int KW = 8;
+__global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(KW / 4, KW / 4)))
 void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
   __shared__ __attribute__((aligned(16))) char q_lds[2 * kTile];
   __shared__ __attribute__((aligned(16))) char o_lds[2 * kTile];  // dO
   __shared__ __attribute__((aligned(16))) float st_lse[2][kBc];
   __shared__ __attribute__((aligned(16))) float st_d[2][kBc];
-  __shared__ __attribute__((aligned(16))) char v_res[32 * NW * kRow];  // this workgroup's V rows
+  __shared__ __attribute__((aligned(16))) char v_res[32 * KW * kRow];  // this workgroup's V rows
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, col = lane & 31;
-  constexpr int BK = 32 * NW;  // keys per workgroup
+  constexpr int BK = 32 * KW;  // keys per workgroup
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy (scalar branches)
 
   // Key tiles with the most query rows first (causal: the first ones).
   const int L = blockIdx.x;
@@ -297,7 +303,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
     const __amdgpu_buffer_rsrc_t vs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(a.v + bgk * (size_t)Sk * kD), (short)0, Sk * kRow, 0x00020000);
 #pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) load_rows(vs, kt * BK + 64 * c4, v_res + c4 * kTile, wave, lane);
+    for (int c4 = 0; c4 < BK / 64; ++c4) load_rows<KW>(vs, kt * BK + 64 * c4, v_res + c4 * kTile, wave, lane);
   }
   const int v_base = row_base(32 * wave + col, hi);  // this lane's V row in v_res
   f32x16_t dk[4], dv[4];
@@ -328,14 +334,14 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
         const_cast<uint16_t*>(a.q + bh * (size_t)Sq * kD), (short)0, Sq * kRow, 0x00020000);
     const __amdgpu_buffer_rsrc_t ds = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(a.dO + bh * (size_t)Sq * kD), (short)0, Sq * kRow, 0x00020000);
-    load_rows(qs, qt * kBc, q_lds + buf * kTile, wave, lane);
-    load_rows(ds, qt * kBc, o_lds + buf * kTile, wave, lane);
-    if (wave == 0) {
+    load_rows<KW>(qs, qt * kBc, q_lds + buf * kTile, wave, lane);
+    load_rows<KW>(ds, qt * kBc, o_lds + buf * kTile, wave, lane);
+    if (wave_u == 0) {
       const __amdgpu_buffer_rsrc_t ls = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<float*>(a.lse + bh * (size_t)Sq), (short)0, Sq * 4, 0x00020000);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ls, (__attribute__((address_space(3))) void*)(&st_lse[buf][0]), 4,
                                                (qt * kBc + lane) * 4, 0, 0, 0);
-    } else if (wave == 1) {
+    } else if (wave_u == 1) {
       const __amdgpu_buffer_rsrc_t dsr = __builtin_amdgcn_make_buffer_rsrc(
           a.delta + bh * (size_t)Sq, (short)0, Sq * 4, 0x00020000);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(dsr, (__attribute__((address_space(3))) void*)(&st_d[buf][0]), 4,
@@ -357,13 +363,18 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
     for (int hq = 0; hq < 2; ++hq) {
       // S = Q K^T and dP = dO V^T for rows 32*hq .. +31 of the tile: register
       // i of lane l is row 32*hq + 16*(i/8) + 8*hi + (i%8), key `key`.
+      // S first, then dP: only one product's operands are live at a time.
       f32x16_t s, dp;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         const int ro = (r_base ^ (32 * kk)) + 32 * hq * kRow;
         const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(ql + ro);
-        const bf16x8_t oa = *reinterpret_cast<const bf16x8_t*>(ol + ro);
         s = kk == 0 ? mfma32_first(qa, kreg[kk]) : mfma32(qa, kreg[kk], s);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const int ro = (r_base ^ (32 * kk)) + 32 * hq * kRow;
+        const bf16x8_t oa = *reinterpret_cast<const bf16x8_t*>(ol + ro);
         const bf16x8_t vb = *reinterpret_cast<const bf16x8_t*>(v_res + (v_base ^ (32 * kk)));
         dp = kk == 0 ? mfma32_first(oa, vb) : mfma32(oa, vb, dp);
       }
@@ -434,9 +445,9 @@ hipError_t launch_attention_bwd(const BwdLaunch& l, hipStream_t s) {
     hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((int64_t)n_qtiles * nbh)), dim3(64 * NW), 0, s, a, n_qtiles, nbh);
   }
   if (l.Sk > 0) {
-    const int n_ktiles = (l.Sk + 32 * NW - 1) / (32 * NW);
+    const int n_ktiles = (l.Sk + 32 * KW - 1) / (32 * KW);
     const int nbg = l.B * l.Hkv;
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)((int64_t)n_ktiles * nbg)), dim3(64 * NW), 0, s, a, n_ktiles, nbg);
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)((int64_t)n_ktiles * nbg)), dim3(64 * KW), 0, s, a, n_ktiles, nbg);
   }
   return hipGetLastError();
 }
