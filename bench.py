@@ -394,6 +394,8 @@ PMC_LEGS = {
     "cascade_wl7": ("--only cascade --no-plain-compare", ["prefill_bf16_kernel", "decode_mfma_kernel", "lse_merge_kernel"],
                     "exact_attention_20_amd/csrc/prefill_bf16.hip+" + DECODE_SRC),
     "prefill_fp8_wl8": ("--only fp8", ["prefill_fp8_kernel"], "exact_attention_20_amd/csrc/prefill_fp8.hip"),
+    "backward_wl2": ("--only bwd", ["bwd_delta_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel"],
+                     "exact_attention_20_amd/csrc/prefill_bwd.hip"),
     "copy": ("--only copy", ["neg"], None),
 }
 PMC_RUN = "--steps 3 --warmup 1 --prewarm-s 0 --no-cpu-baseline"
@@ -456,7 +458,11 @@ def summarize_profiles(d):
         wk, _ = _pmc_means(f"{d}/pmc_{leg}_WRITE_SIZE", names)
         wid = int(leg.rsplit("wl", 1)[1])
         w = workloads.WORKLOADS[wid]
-        if leg.startswith("prefill_fp8"):
+        if leg.startswith("backward"):
+            # q, o, dO read and dq written (Hq heads), k, v read and dk, dv written (Hkv heads), once
+            # each in bf16; lse read, D written and read (fp32)
+            alg = 2 * w.B * w.S * w.D * (4 * w.Hq + 4 * w.Hkv) + 12 * w.B * w.Hq * w.S
+        elif leg.startswith("prefill_fp8"):
             alg = w.B * w.S * w.D * (w.Hq + 2 * w.Hkv) + 2 * w.B * w.Hq * w.S * w.D + 4 * w.B * w.Hq * w.S
         elif leg.startswith("prefill"):
             alg = prefill_bytes(w)
@@ -522,6 +528,8 @@ def summarize_profiles(d):
                     leg = "cascade"
                 if k.startswith("prefill_fp8"):
                     leg = "fp8"
+                if k.startswith("bwd_") or (k == "prefill_bf16_kernel<8, 1, 0>" and leg != "prefill"):
+                    leg = "backward"  # the backward leg starts with one forward call for O and LSE
                 sub = leg
                 if leg in ("cascade", "cascade (plain-decode comparison)"):
                     if k.startswith("decode_"):
@@ -545,6 +553,8 @@ def summarize_profiles(d):
                     lines.append(f"bench decode step ms_mean: {b['decode'].get('ms_mean')}")
                 if "shared_prefix_decode" in b:
                     lines.append(f"bench shared-prefix decode step ms_mean: {b['shared_prefix_decode'].get('ms_mean')}")
+                if "backward" in b:
+                    lines.append(f"bench backward step ms_mean: {b['backward'].get('ms_mean')}")
                 if "fp8_prefill" in b:
                     lines.append(f"bench fp8 prefill launch ms_mean: {b['fp8_prefill'].get('ms_mean')}")
                 if "ragged_prefill" in b:
@@ -862,7 +872,8 @@ def main():
                "value": round(tf, 2), "unit": "TFLOP/s", "ms_mean": round(tb, 5),
                "ms_median": round(statistics.median(g["t"]), 5),
                "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                            "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                            "traffic": read_traffic("backward_wl2_traffic.txt", "exact_attention_20_amd/csrc/prefill_bwd.hip"),
                             "kernel": "bwd_delta_kernel + bwd_dq_kernel + bwd_dkdv_kernel", "flops_per_launch": flops},
                "cpu_baseline": res["bwd_cpu"],
                "config": {"workload": wb.name + " (backward)", "B": wb.B, "Hq": wb.Hq, "Hkv": wb.Hkv, "S": wb.S,
