@@ -502,10 +502,10 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   for (int qb = 0; qb < QB; ++qb) {
     const float lrt = xor32_sum((lr[qb][0] + lr[qb][1]) + (lr[qb][2] + lr[qb][3]));
     const float let_ = xor32_sum((le[qb][0] + le[qb][1]) + (le[qb][2] + le[qb][3]));
-    if (qrow[qb] >= Sq) continue;
     const float inv = lrt > 0.f ? 1.f / lrt : 0.f;
     const float lse_val = let_ > 0.f ? (m[qb] + __log2f(let_)) * kLn2 : kNegInf;
     if constexpr (MODE == kPrefix) {
+      if (qrow[qb] >= Sq) continue;
       // The request's only slot: final bf16 output; else this chunk's
       // normalised partial output and LSE for the merge.
       const size_t pr = prefix_row(qrow[qb]);
@@ -536,18 +536,31 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
       }
       continue;
     }
-    uint16_t* O = reinterpret_cast<uint16_t*>(a.out) + qo_base + (size_t)qrow[qb] * row_stride;
+    // The block's 32 bf16 output rows go through this wavefront's 8 KB of
+    // the (now idle) K/V buffers, so that each store writes whole 256-byte
+    // rows: lane (col, hi) holds dims 32*db + 8*gq + 4*hi .. +3 of row col,
+    // stored in 16-byte unit 4*db + gq (XOR-swizzled by row & 15, which
+    // keeps both the writes and the row reads free of bank conflicts). A
+    // wavefront's LDS operations complete in order, so no barrier is needed.
+    char* st = (wave < 4 ? k_lds : v_lds) + (wave & 3) * (32 * kRow);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        const int d = 32 * db + 8 * gq + 4 * hi;
         const uint2 w = make_uint2(pack_bf16x2(o[qb][db][4 * gq] * inv, o[qb][db][4 * gq + 1] * inv),
                                    pack_bf16x2(o[qb][db][4 * gq + 2] * inv, o[qb][db][4 * gq + 3] * inv));
-        *reinterpret_cast<uint2*>(O + d) = w;
+        *reinterpret_cast<uint2*>(st + col * kRow + 16 * ((4 * db + gq) ^ (col & 15)) + 8 * hi) = w;
       }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rr = 4 * i + (lane >> 4), u = lane & 15;
+      const uint4 v = *reinterpret_cast<const uint4*>(st + rr * kRow + 16 * (u ^ (rr & 15)));
+      if (wq0[qb] + rr < Sq)
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + qo_base + (size_t)(wq0[qb] + rr) * row_stride +
+                                  8 * u) = v;
+    }
     const size_t lse_idx = PAGED ? (tok0 + qrow[qb]) * a.Hq + h : ((size_t)b * a.Hq + h) * Sq + qrow[qb];
-    if (hi == 0) a.lse[lse_idx] = lse_val;
+    if (hi == 0 && qrow[qb] < Sq) a.lse[lse_idx] = lse_val;
   }
 }
 
