@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -39,6 +40,9 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(FA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Plan workspaces hold 16-byte work items and float4 partial results.
+bool misaligned(const void* p) { return ((uintptr_t)p & 15) != 0; }
+
 int device_cus(int* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -57,11 +61,13 @@ struct fa_decode_plan_s {
   std::vector<fa::PrefixItem> prefix_items;  // cascade plans only
   std::vector<int32_t> group_reqs;
   fa::WorkspaceLayout layout;
+  const void* workspace;  // the buffer holding this plan's work list
 };
 
 struct fa_prefill_plan_s {
   int B, stride, num_pages, Hq, Hkv, D, n_items;
-  size_t bytes;  // workspace bytes the work list occupies
+  size_t bytes;           // workspace bytes the work list occupies
+  const void* workspace;  // the buffer holding the work list
 };
 
 extern "C" {
@@ -86,6 +92,9 @@ int fa_prefill_fwd(const void* q, const void* k, const void* v, void* out, float
       return fail(FA_ERR_UNSUPPORTED, "fa_prefill_fwd: fp32 supports D in {64,128} (got %d)", D);
   } else if (dtype == FA_DTYPE_BF16) {
     if (D != 128) return fail(FA_ERR_UNSUPPORTED, "fa_prefill_fwd: bf16 supports D=128 (got %d)", D);
+    // K/V tiles are read through a buffer resource of Sk * 256 bytes per head.
+    if ((long long)Sk * 256 > 0x7fffffffLL)
+      return fail(FA_ERR_UNSUPPORTED, "fa_prefill_fwd: bf16 needs Sk below 2^23 (got %d)", Sk);
   } else {
     return fail(FA_ERR_UNSUPPORTED, "fa_prefill_fwd: dtype %d not supported (F32 or BF16)", dtype);
   }
@@ -285,6 +294,11 @@ int fa_decode_plan(const int32_t* seqlens_host, const int32_t* page_table_host, 
     delete p;
     return fail(FA_ERR_WORKSPACE, "fa_decode_plan: workspace needs %zu bytes (got %zu)", need, workspace_bytes);
   }
+  if (misaligned(workspace)) {
+    delete p;
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan: workspace must be 16-byte aligned");
+  }
+  p->workspace = workspace;
   // Work list and split counts into one host staging block, one upload.
   std::vector<char> stage(p->layout.part_o_off, 0);
   if (r.n_items) std::memcpy(stage.data() + p->layout.items_off, p->items.data(), sizeof(fa::WorkItem) * r.n_items);
@@ -327,6 +341,8 @@ int fa_decode_run(const fa_decode_plan_t* plan, const void* q, const void* k_pag
     return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_run: num_splits %d != plan's %d", num_splits, plan->num_splits);
   if (!q || !out || !lse || !workspace || !seqlens)
     return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_run: null pointer (q/out/lse/workspace/seqlens)");
+  if (workspace != plan->workspace)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_run: workspace is not the buffer the plan was built in");
   if ((!plan->items.empty() || !plan->prefix_items.empty()) && (!k_pages || !v_pages || !page_table))
     return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_run: null KV pool or page table");
   bool fp8 = plan->kv_dtype == FA_DTYPE_FP8_E4M3FN;
@@ -502,6 +518,11 @@ int fa_decode_plan_cascade(const int32_t* seqlens_host, const int32_t* page_tabl
     delete p;
     return fail(FA_ERR_WORKSPACE, "fa_decode_plan_cascade: workspace needs %zu bytes (got %zu)", need, workspace_bytes);
   }
+  if (misaligned(workspace)) {
+    delete p;
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan_cascade: workspace must be 16-byte aligned");
+  }
+  p->workspace = workspace;
   // The metadata before and after the partial-result area, staged and
   // uploaded in two copies (the partials themselves need no initial value).
   const fa::WorkspaceLayout& w = p->layout;
@@ -610,12 +631,15 @@ int fa_prefill_paged_plan(const int32_t* seqlens_host, const int32_t* cu_seqlens
   const size_t need = fa_prefill_paged_workspace_size(seqlens_host, cu_seqlens_q_host, B);
   if (!workspace || workspace_bytes < need)
     return fail(FA_ERR_WORKSPACE, "fa_prefill_paged_plan: workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  if (misaligned(workspace))
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_paged_plan: workspace must be 16-byte aligned");
   items.resize(2 * (size_t)std::max(n, 1), 0);
   fa::plan_prefill_host(seqlens_host, cu_seqlens_q_host, B, items.data(), n);
   fa_prefill_plan_t* p = new (std::nothrow) fa_prefill_plan_t;
   if (!p) return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_paged_plan: out of host memory");
   p->B = B; p->stride = max_pages_per_req; p->num_pages = num_pages;
   p->Hq = Hq; p->Hkv = Hkv; p->D = D; p->n_items = n; p->bytes = need;
+  p->workspace = workspace;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipMemcpyAsync(workspace, items.data(), items.size() * sizeof(int32_t), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);  // the host list is freed on return
@@ -635,6 +659,8 @@ int fa_prefill_paged_run(const fa_prefill_plan_t* plan, const void* q, const voi
                          void* workspace, void* stream) {
   if (!plan) return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_paged_run: plan is null");
   if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_paged_run: scale is not finite");
+  if (workspace != plan->workspace)
+    return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_paged_run: workspace is not the buffer the plan was built in");
   if (plan->n_items == 0) return ok();
   if (!q || !k_pages || !v_pages || !page_table || !seqlens || !cu_seqlens_q || !out || !lse || !workspace)
     return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_paged_run: null pointer");

@@ -88,7 +88,7 @@ int fa_abi_version(void);
  *                must be 0). Entries must lie in [0, Hkv).
  * Limits: B, Hq, Hkv >= 1; Hq, Hkv <= 256; Sq, Sk >= 0 (0 is a no-op for
  * Sq = 0; Sk = 0 gives out = 0, lse = -inf); B*Hq*Sq*D and B*Hkv*Sk*D must fit in
- * int64 and Sq, Sk < 2^31.
+ * int64 and Sq, Sk < 2^31; bf16 also needs Sk < 2^23 (FA_ERR_UNSUPPORTED).
  */
 int fa_prefill_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                    int B, int Hq, int Hkv, int Sq, int Sk, int D, int dtype, int causal,
@@ -188,9 +188,9 @@ size_t fa_decode_workspace_size(const int32_t* seqlens_host, int B, int Hq, int 
  *                      device's CUs; k > 0 = split every request into
  *                      min(k, pages_b) near-equal page ranges.
  *   num_cus            0 = query the current device, else use this count.
- *   workspace          device buffer of >= fa_decode_workspace_size bytes; the
- *                      plan uploads its work list there with one
- *                      hipMemcpyAsync on `stream`.
+ *   workspace          16-byte aligned device buffer of >=
+ *                      fa_decode_workspace_size bytes; the plan uploads its
+ *                      work list there with one hipMemcpyAsync on `stream`.
  *   plan_out           receives a host plan object (free with
  *                      fa_decode_plan_destroy, after the runs that use it).
  *   num_splits_out     receives the largest split count of any request: the
@@ -246,7 +246,8 @@ int fa_decode_plan_host(const int32_t* seqlens_host, int B, int max_pages_per_re
  *   out        [B, Hq, D] bf16, written; lse [B, Hq] fp32, written. A request
  *              with L_b = 0 gets out = 0 and lse = -inf.
  *   workspace  the buffer given to the plan (it holds the work list and the
- *              per-split partial results)
+ *              per-split partial results); any other pointer is rejected
+ *              with FA_ERR_INVALID_ARGUMENT
  */
 int fa_decode_run(const fa_decode_plan_t* plan, const void* q, const void* k_pages,
                   const void* v_pages, const float* k_scale, const float* v_scale,
@@ -320,9 +321,11 @@ size_t fa_prefill_paged_workspace_size(const int32_t* seqlens_host,
  *                    every entry the run reads is checked to lie in
  *                    [0, num_pages) (FA_ERR_INVALID_ARGUMENT otherwise).
  *   Hq, Hkv, D       heads and head size (D = 128, Hq % Hkv == 0, <= 256)
- *   workspace        device buffer of >= fa_prefill_paged_workspace_size
- *                    bytes; the work list is uploaded there with one
- *                    hipMemcpyAsync on `stream` followed by a wait on it.
+ *   workspace        16-byte aligned device buffer of >=
+ *                    fa_prefill_paged_workspace_size bytes; the work list is
+ *                    uploaded there with one hipMemcpyAsync on `stream`
+ *                    followed by a wait on it. fa_prefill_paged_run must be
+ *                    given this same buffer (FA_ERR_INVALID_ARGUMENT otherwise).
  *   plan_out         receives a host plan object (fa_prefill_paged_plan_destroy).
  */
 int fa_prefill_paged_plan(const int32_t* seqlens_host, const int32_t* cu_seqlens_q_host,
@@ -377,8 +380,8 @@ int fa_prefill_paged_run(const fa_prefill_plan_t* plan, const void* q, const voi
  * The plan checks, on the host page table, that every member shares its
  * group's prefix pages (FA_ERR_INVALID_ARGUMENT otherwise). The plan object
  * is used with fa_decode_run and freed with fa_decode_plan_destroy like any
- * decode plan; fa_decode_run then launches three kernels (prefix pass,
- * split-KV kernel, merge).
+ * decode plan (the workspace rules of fa_decode_plan apply); fa_decode_run
+ * then launches three kernels (prefix pass, split-KV kernel, merge).
  */
 size_t fa_decode_cascade_workspace_size(const int32_t* seqlens_host, int B, int max_pages_per_req,
                                         int Hq, int Hkv, int D, const int32_t* prefix_group_host,

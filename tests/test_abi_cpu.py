@@ -62,6 +62,7 @@ def _prefill(lib, **kw):
     (dict(causal=2), 1), (dict(scale=float("nan")), 1), (dict(Hq=3, Hkv=2), 1),
     (dict(D=64), 2), (dict(dtype=fa.F32, D=96), 2), (dict(dtype=7), 2), (dict(dtype=fa.FP8_E4M3FN), 2),
     (dict(Hq=300, Hkv=300), 2), (dict(q=None), 1), (dict(k=None), 1), (dict(lse=None), 1),
+    (dict(Sk=1 << 23), 2),  # bf16 K/V buffer resource is Sk * 256 bytes
 ])
 def test_prefill_rejects(lib, kw, code):
     assert _prefill(lib, **kw) == code
@@ -94,7 +95,7 @@ def _plan(lib, seqlens, table=None, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(Hq=6, Hkv=4), 1), (dict(Hq=24, Hkv=2), 2), (dict(D=64), 2), (dict(dt=fa.F32), 2),
     (dict(stride=1), 1), (dict(P=0), 1), (dict(ns=-1), 1), (dict(cus=-1), 1),
-    (dict(ws=None), 3), (dict(wsb=16), 3),
+    (dict(ws=None), 3), (dict(wsb=16), 3), (dict(ws=C.c_void_p(264)), 1),  # misaligned workspace
 ])
 def test_plan_rejects(lib, kw, code):
     assert _plan(lib, [100, 300], **kw) == code

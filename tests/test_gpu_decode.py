@@ -120,6 +120,24 @@ def test_num_splits_invariance():
         assert (l - res[0][1]).abs().max().item() <= 1e-4
 
 
+def test_run_rejects_a_foreign_workspace():
+    """A run handed any buffer but the plan's own is refused before a launch
+    (the work list lives in the plan's workspace); the plan still runs after."""
+    fa = need_gpu()
+    kv = workloads.paged_inputs(2, 8, 2, 128, "bf16", [300, 1000], 35, nan_tails=True)
+    d = to_dev(kv)
+    out, lse, plan = run(fa, kv, d, 0)
+    own = plan.workspace
+    plan.workspace = torch.zeros_like(own)
+    with pytest.raises(fa.FAError) as e:
+        fa.decode(plan, d["q"], d["k"], d["v"], d["pt"], d["sl"], d["ks"], d["vs"])
+    assert e.value.status == 1 and "workspace" in str(e.value)
+    plan.workspace = own
+    out2, lse2 = fa.decode(plan, d["q"], d["k"], d["v"], d["pt"], d["sl"], d["ks"], d["vs"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
 @pytest.mark.parametrize("wid", [4, 5])
 def test_full_workload(wid):
     """Full-size decode workloads in the benchmark's launch configuration (plan-chosen splits)."""

@@ -98,6 +98,23 @@ def test_matches_contiguous_kernel_bitwise(n, prefix):
     assert torch.equal(lse, lc[0].T), "paged LSE differs from the contiguous kernel"
 
 
+def test_run_rejects_a_foreign_workspace():
+    """fa_prefill_paged_run refuses a workspace other than the plan's."""
+    fa = need_gpu()
+    r = workloads.ragged_inputs(8, 2, 128, [300, 5], [64, 0], wid=54)
+    d = to_dev(r)
+    out, lse, plan = append_and_run(fa, r, d)
+    own = plan.workspace
+    plan.workspace = torch.zeros_like(own)
+    with pytest.raises(fa.FAError) as e:
+        fa.prefill_paged(plan, d["q"], d["k"], d["v"], d["pt"], d["sl"], d["cu"], SCALE)
+    assert e.value.status == 1 and "workspace" in str(e.value)
+    plan.workspace = own
+    out2, lse2 = fa.prefill_paged(plan, d["q"], d["k"], d["v"], d["pt"], d["sl"], d["cu"], SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
 def test_page_permutation_bitwise():
     """The same logical caches under another physical page permutation give identical bits."""
     fa = need_gpu()

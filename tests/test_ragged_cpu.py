@@ -104,7 +104,7 @@ def _plan(lib, **kw):
     (dict(stride=0), 1), (dict(P=0), 1), (dict(cu=[0, 6, 5]), 1), (dict(L=[5, 3]), 1),
     (dict(table=[0, 7, 2, -1]), 1),          # page id outside the pool
     (dict(L=[200, 3], cu=[0, 6, 9]), 1),     # needs 4 pages > stride 2
-    (dict(ws=None), 3), (dict(ws_bytes=8), 3),
+    (dict(ws=None), 3), (dict(ws_bytes=8), 3), (dict(ws=C.c_void_p(260)), 1),  # misaligned workspace
 ])
 def test_paged_plan_rejects_before_device_work(lib, kw, code):
     assert _plan(lib, **kw) == code
