@@ -73,7 +73,7 @@ def load():
     lib.fa_decode_plan_items.argtypes = [vp, i32p, ci, i32p, C.POINTER(ci)]
     lib.fa_decode_plan_items.restype = ci
     lib.fa_decode_plan_host.argtypes = [i32p, ci, ci, ci, ci, ci, ci, i32p, ci, i32p,
-                                        C.POINTER(ci), C.POINTER(ci)]
+                                        C.POINTER(ci), C.POINTER(ci), C.POINTER(ci)]
     lib.fa_decode_plan_host.restype = ci
     lib.fa_decode_run.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, cf, vp, vp, vp, vp]
     lib.fa_decode_run.restype = ci
@@ -188,23 +188,26 @@ def fa_decode_workspace_size(seqlens, Hq, Hkv, D=128, num_splits=0, num_cus=0):
 
 
 def fa_decode_plan_host(seqlens, max_pages, Hq, Hkv, num_splits=0, num_cus=256):
-    """Pure host planning: (items [n,4] int32 tensor, splits [B], num_splits, chunk_pages)."""
+    """Pure host planning: (items [n,4] int32 tensor, splits [B], num_splits, chunk_pages, grid).
+
+    ``grid`` is the number of split-kernel workgroups; workgroup w runs items
+    w, w + grid, ... (items with b = -1 are padding)."""
     lib = load()
     sl, p = _i32_host(seqlens)
     B = sl.numel()
-    ns, ch = C.c_int(0), C.c_int(0)
+    ns, ch, gr = C.c_int(0), C.c_int(0), C.c_int(0)
     i32 = C.POINTER(C.c_int32)
     n = lib.fa_decode_plan_host(C.cast(p, i32), B, max_pages, Hq, Hkv, num_splits, num_cus, None, 0,
-                                None, C.byref(ns), C.byref(ch))
+                                None, C.byref(ns), C.byref(ch), C.byref(gr))
     if n < 0:
         _check(-n)
     items = torch.zeros((max(n, 1), 4), dtype=torch.int32)
     splits = torch.zeros(B, dtype=torch.int32)
     n2 = lib.fa_decode_plan_host(C.cast(p, i32), B, max_pages, Hq, Hkv, num_splits, num_cus,
                                  C.cast(items.data_ptr(), i32), n, C.cast(splits.data_ptr(), i32),
-                                 C.byref(ns), C.byref(ch))
+                                 C.byref(ns), C.byref(ch), C.byref(gr))
     assert n2 == n
-    return items[:n], splits, ns.value, ch.value
+    return items[:n], splits, ns.value, ch.value, gr.value
 
 
 class DecodePlan:

@@ -56,6 +56,7 @@ int device_cus(int* out) {
 
 struct fa_decode_plan_s {
   int B, stride, num_pages, Hq, Hkv, D, kv_dtype, num_splits, chunk_pages;
+  int grid;  // split-kernel workgroups (each runs items w, w + grid, ...)
   std::vector<fa::WorkItem> items;
   std::vector<int32_t> splits;
   std::vector<fa::PrefixItem> prefix_items;  // cascade plans only
@@ -74,7 +75,7 @@ extern "C" {
 
 const char* fa_last_error(void) { return g_err.c_str(); }
 
-int fa_abi_version(void) { return 1; }
+int fa_abi_version(void) { return 2; }
 
 int fa_prefill_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                    int Hq, int Hkv, int Sq, int Sk, int D, int dtype, int causal, float scale,
@@ -212,7 +213,7 @@ size_t fa_decode_workspace_size(const int32_t* seqlens_host, int B, int Hq, int 
 
 int fa_decode_plan_host(const int32_t* seqlens_host, int B, int max_pages_per_req, int Hq, int Hkv,
                         int num_splits_request, int num_cus, int32_t* items_out, int capacity,
-                        int32_t* splits_out, int* num_splits_out, int* chunk_pages_out) {
+                        int32_t* splits_out, int* num_splits_out, int* chunk_pages_out, int* grid_out) {
   if (!seqlens_host || B < 1 || Hkv < 1 || Hq < 1 || max_pages_per_req < 1 || num_cus < 1 ||
       capacity < 0 || num_splits_request < 0) {
     fail(FA_ERR_INVALID_ARGUMENT, "fa_decode_plan_host: invalid argument");
@@ -237,6 +238,7 @@ int fa_decode_plan_host(const int32_t* seqlens_host, int B, int max_pages_per_re
   }
   if (num_splits_out) *num_splits_out = r.num_splits;
   if (chunk_pages_out) *chunk_pages_out = r.chunk_pages;
+  if (grid_out) *grid_out = r.grid;
   ok();
   return r.n_items;
 }
@@ -287,6 +289,7 @@ int fa_decode_plan(const int32_t* seqlens_host, const int32_t* page_table_host, 
   p->B = B; p->stride = max_pages_per_req; p->num_pages = num_pages;
   p->Hq = Hq; p->Hkv = Hkv; p->D = D; p->kv_dtype = kv_dtype;
   p->num_splits = r.num_splits; p->chunk_pages = r.chunk_pages;
+  p->grid = r.grid;
   p->items.resize(r.n_items);
   p->layout = fa::workspace_layout(r.n_items, B, Hq, D, r.num_splits);
   if (!workspace || workspace_bytes < p->layout.total) {
@@ -353,6 +356,7 @@ int fa_decode_run(const fa_decode_plan_t* plan, const void* q, const void* k_pag
   fa::DecodeArgs a;
   a.items = (const fa::WorkItem*)(ws + plan->layout.items_off);
   a.n_items = (int)plan->items.size();
+  a.grid = plan->grid;
   a.splits_per_req = (const int32_t*)(ws + plan->layout.splits_off);
   a.q = q; a.k_pages = k_pages; a.v_pages = v_pages; a.k_scale = k_scale; a.v_scale = v_scale;
   a.page_table = page_table; a.seqlens = seqlens;
@@ -507,6 +511,7 @@ int fa_decode_plan_cascade(const int32_t* seqlens_host, const int32_t* page_tabl
   p->B = B; p->stride = max_pages_per_req; p->num_pages = num_pages;
   p->Hq = Hq; p->Hkv = Hkv; p->D = D; p->kv_dtype = FA_DTYPE_BF16;
   p->num_splits = cp.num_splits; p->chunk_pages = cp.prefix_chunk_pages;
+  p->grid = (int)cp.items.size();
   p->items = std::move(cp.items);
   p->splits = std::move(cp.splits);
   p->prefix_items = std::move(cp.prefix_items);

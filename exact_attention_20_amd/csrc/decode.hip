@@ -131,248 +131,254 @@ struct PageBuf {
 template <int G, bool FP8, int NB>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   constexpr int kElem = FP8 ? 1 : 2;
-  const WorkItem it = a.items[blockIdx.x];
-  const int b = it.b;
-  const int g = it.g_split & 255;
-  const int split = it.g_split >> 8;
-  const int p0 = it.page_begin, p1 = it.page_end;
-  const int L = a.seqlens[b];
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int row = lane >> 4, dc = lane & 15;
+  // Workgroup w runs items w, w + grid, ... (one item unless the plan
+  // packed several segments per workgroup).
+  for (int ii = blockIdx.x; ii < a.n_items; ii += gridDim.x) {
+    const WorkItem it = a.items[ii];
+    if (it.b < 0) continue;  // padding of a balanced plan
+    const int b = it.b;
+    const int g = it.g_split & 255;
+    const int split = it.g_split >> 8;
+    const int p0 = it.page_begin, p1 = it.page_end;
+    const int L = a.seqlens[b];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int row = lane >> 4, dc = lane & 15;
 
-  // Query rows of the G heads of this KV group: 8 bf16 (4 pairs) per lane.
-  uint32_t qd[G][4];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint4 v = *reinterpret_cast<const uint4*>(
-        reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + g * G + h) * kD + dc * 8);
-    qd[h][0] = v.x; qd[h][1] = v.y; qd[h][2] = v.z; qd[h][3] = v.w;
-  }
-  const float c_base = a.scale * kLog2e;
-
-  float m[G], l[G], acc[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = kNegInf;
-    l[h] = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
-  }
-
-  const int blk_bytes = 64 * kD * kElem;  // one (page, KV head) block
-  const char* kpool = reinterpret_cast<const char*>(a.k_pages);
-  const char* vpool = reinterpret_cast<const char*>(a.v_pages);
-  const int32_t* table = a.page_table + (size_t)b * a.stride;
-  // Byte offset of this lane's slot i inside a block: token wave*16 + 4i + row,
-  // dims dc*8 .. dc*8+7.
-  int slot_off[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) slot_off[i] = ((wave * 16 + 4 * i + row) * kD + dc * 8) * kElem;
-
-  // Page ids of the item, 64 pages per window: lane i holds the id of page
-  // w0 + i (and for fp8 that page's K and V scales), read with one vector
-  // load each, so no page waits on a dependent page-table or scale load.
-  int w0 = p0;
-  int tbl = -1;
-  float kscl = 0.f, vscl = 0.f;
-  auto load_window = [&]() {
-    const int pp = w0 + lane;
-    tbl = pp < p1 ? table[pp] : -1;
-    if constexpr (FP8) {
-      const bool ok = (unsigned)tbl < (unsigned)a.num_pages;
-      kscl = ok ? a.k_scale[(size_t)tbl * a.Hkv + g] : 0.f;
-      vscl = ok ? a.v_scale[(size_t)tbl * a.Hkv + g] : 0.f;
-    }
-  };
-  load_window();
-
-  // Ring of NB page buffers: page p lives in buf[(p - p0) % NB], and its
-  // loads are issued NB-1 pages ahead of its use, so each wavefront keeps
-  // NB-1 pages of K and V in flight while it computes on the current one.
-  // The page's block address is wave-uniform (scalar registers), so the
-  // per-page address work is scalar and the lane offsets are fixed.
-  PageBuf<FP8> buf[NB];
-  auto issue = [&](PageBuf<FP8>& d, int p) {
-    if (p - w0 == 64) {
-      w0 += 64;
-      load_window();
-    }
-    const int pid = __builtin_amdgcn_readlane(tbl, p - w0);
-    d.pid = pid;
-    if constexpr (FP8) {
-      d.c = c_base * __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, kscl), p - w0));
-      d.vsc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, vscl), p - w0));
-    } else {
-      d.c = c_base;
-      d.vsc = 1.f;
-    }
-    // The block offset is uniform; readfirstlane makes that visible to the
-    // compiler, which otherwise wraps each buffer load in a waterfall loop.
-    const size_t off_v = ((size_t)(((unsigned)pid < (unsigned)a.num_pages) ? pid : 0) * a.Hkv + g) * blk_bytes;
-    const size_t off = ((size_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(off_v >> 32)) << 32) |
-                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)off_v);
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kpool + off), (short)0, blk_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vpool + off), (short)0, blk_bytes, 0x00020000);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      load_slot<FP8>(d.k[i], rk, slot_off[i]);
-      load_slot<FP8>(d.v[i], rv, slot_off[i]);
-    }
-  };
-
-  auto consume = [&](PageBuf<FP8>& cur, int p) {
-    // Tokens of this page that belong to the request: all 64 except on the
-    // request's last page; an out-of-range page id contributes nothing. Only
-    // such a partial page takes the masking path (a wave-uniform branch).
-    const int nvalid = ((unsigned)cur.pid < (unsigned)a.num_pages) ? min(64, L - p * 64) : 0;
-    const bool partial = nvalid < 64;
-    bool tok_ok[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) tok_ok[i] = (wave * 16 + 4 * i + row) < nvalid;
-    if (partial) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (!tok_ok[i]) {  // tail slots may hold anything (NaN): never use them
-          zero_slot<FP8>(cur.k[i]);
-          zero_slot<FP8>(cur.v[i]);
-        }
-    }
-
-    // Raw dot products q.k for this lane's 4 tokens, summed over the 16 lanes
-    // that share a token.
-    float s[4][G];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t kp[4];
-      slot_pairs<FP8>(cur.k[i], kp);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float d = dot2_bf16(qd[h][0], kp[0], 0.f);
-        d = dot2_bf16(qd[h][1], kp[1], d);
-        d = dot2_bf16(qd[h][2], kp[2], d);
-        d = dot2_bf16(qd[h][3], kp[3], d);
-        s[i][h] = row16_sum(d);
-      }
-    }
-    if (partial) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int h = 0; h < G; ++h) s[i][h] = tok_ok[i] ? s[i][h] : kNegInf;
-    }
-
-    // Lazy running max in log2 units: the score is c*s with c >= 0, so the
-    // tile max is c * max(s). It moves only when some score exceeds it by
-    // more than kTau; after the first full page it is finite.
-    const float c = cur.c;
-    bool need = false;
-    float smax[G];
+    // Query rows of the G heads of this KV group: 8 bf16 (4 pairs) per lane.
+    uint32_t qd[G][4];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      smax[h] = fmaxf(fmaxf(s[0][h], s[1][h]), fmaxf(s[2][h], s[3][h]));
-      need |= smax[h] * c > m[h] + kTau;
+      const uint4 v = *reinterpret_cast<const uint4*>(
+          reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + g * G + h) * kD + dc * 8);
+      qd[h][0] = v.x; qd[h][1] = v.y; qd[h][2] = v.z; qd[h][3] = v.w;
     }
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float x = fmaxf(smax[h], shfl_xor_f32(smax[h], 16));
-        x = fmaxf(x, shfl_xor_f32(x, 32));
-        const float mn = fmaxf(m[h], x * c);
-        const float alpha = fast_exp2(m[h] - mn);  // 0 when m was -inf
-        l[h] *= alpha;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[h][j] *= alpha;
-        m[h] = mn;
-      }
-    }
+    const float c_base = a.scale * kLog2e;
 
-    // p = 2^(c*s - m); the fp8 V scale is folded into the weights that
-    // multiply V, not into the normaliser.
-    float e[4][G];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) e[i][h] = fast_exp2(__builtin_fmaf(s[i][h], c, -m[h]));
-    if (partial) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int h = 0; h < G; ++h) e[i][h] = tok_ok[i] ? e[i][h] : 0.f;
-    }
-    uint32_t pp01[G], pp23[G];
+    float m[G], l[G], acc[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      l[h] += (e[0][h] + e[1][h]) + (e[2][h] + e[3][h]);
+      m[h] = kNegInf;
+      l[h] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
+    }
+
+    const int blk_bytes = 64 * kD * kElem;  // one (page, KV head) block
+    const char* kpool = reinterpret_cast<const char*>(a.k_pages);
+    const char* vpool = reinterpret_cast<const char*>(a.v_pages);
+    const int32_t* table = a.page_table + (size_t)b * a.stride;
+    // Byte offset of this lane's slot i inside a block: token wave*16 + 4i + row,
+    // dims dc*8 .. dc*8+7.
+    int slot_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) slot_off[i] = ((wave * 16 + 4 * i + row) * kD + dc * 8) * kElem;
+
+    // Page ids of the item, 64 pages per window: lane i holds the id of page
+    // w0 + i (and for fp8 that page's K and V scales), read with one vector
+    // load each, so no page waits on a dependent page-table or scale load.
+    int w0 = p0;
+    int tbl = -1;
+    float kscl = 0.f, vscl = 0.f;
+    auto load_window = [&]() {
+      const int pp = w0 + lane;
+      tbl = pp < p1 ? table[pp] : -1;
       if constexpr (FP8) {
-        const float vsc = cur.vsc;
-        pp01[h] = pack_bf16x2(e[0][h] * vsc, e[1][h] * vsc);
-        pp23[h] = pack_bf16x2(e[2][h] * vsc, e[3][h] * vsc);
+        const bool ok = (unsigned)tbl < (unsigned)a.num_pages;
+        kscl = ok ? a.k_scale[(size_t)tbl * a.Hkv + g] : 0.f;
+        vscl = ok ? a.v_scale[(size_t)tbl * a.Hkv + g] : 0.f;
+      }
+    };
+    load_window();
+
+    // Ring of NB page buffers: page p lives in buf[(p - p0) % NB], and its
+    // loads are issued NB-1 pages ahead of its use, so each wavefront keeps
+    // NB-1 pages of K and V in flight while it computes on the current one.
+    // The page's block address is wave-uniform (scalar registers), so the
+    // per-page address work is scalar and the lane offsets are fixed.
+    PageBuf<FP8> buf[NB];
+    auto issue = [&](PageBuf<FP8>& d, int p) {
+      if (p - w0 == 64) {
+        w0 += 64;
+        load_window();
+      }
+      const int pid = __builtin_amdgcn_readlane(tbl, p - w0);
+      d.pid = pid;
+      if constexpr (FP8) {
+        d.c = c_base * __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, kscl), p - w0));
+        d.vsc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, vscl), p - w0));
       } else {
-        pp01[h] = pack_bf16x2(e[0][h], e[1][h]);
-        pp23[h] = pack_bf16x2(e[2][h], e[3][h]);
+        d.c = c_base;
+        d.vsc = 1.f;
+      }
+      // The block offset is uniform; readfirstlane makes that visible to the
+      // compiler, which otherwise wraps each buffer load in a waterfall loop.
+      const size_t off_v = ((size_t)(((unsigned)pid < (unsigned)a.num_pages) ? pid : 0) * a.Hkv + g) * blk_bytes;
+      const size_t off = ((size_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(off_v >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)off_v);
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kpool + off), (short)0, blk_bytes, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vpool + off), (short)0, blk_bytes, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        load_slot<FP8>(d.k[i], rk, slot_off[i]);
+        load_slot<FP8>(d.v[i], rv, slot_off[i]);
+      }
+    };
+
+    auto consume = [&](PageBuf<FP8>& cur, int p) {
+      // Tokens of this page that belong to the request: all 64 except on the
+      // request's last page; an out-of-range page id contributes nothing. Only
+      // such a partial page takes the masking path (a wave-uniform branch).
+      const int nvalid = ((unsigned)cur.pid < (unsigned)a.num_pages) ? min(64, L - p * 64) : 0;
+      const bool partial = nvalid < 64;
+      bool tok_ok[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tok_ok[i] = (wave * 16 + 4 * i + row) < nvalid;
+      if (partial) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!tok_ok[i]) {  // tail slots may hold anything (NaN): never use them
+            zero_slot<FP8>(cur.k[i]);
+            zero_slot<FP8>(cur.v[i]);
+          }
+      }
+
+      // Raw dot products q.k for this lane's 4 tokens, summed over the 16 lanes
+      // that share a token.
+      float s[4][G];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t kp[4];
+        slot_pairs<FP8>(cur.k[i], kp);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float d = dot2_bf16(qd[h][0], kp[0], 0.f);
+          d = dot2_bf16(qd[h][1], kp[1], d);
+          d = dot2_bf16(qd[h][2], kp[2], d);
+          d = dot2_bf16(qd[h][3], kp[3], d);
+          s[i][h] = row16_sum(d);
+        }
+      }
+      if (partial) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int h = 0; h < G; ++h) s[i][h] = tok_ok[i] ? s[i][h] : kNegInf;
+      }
+
+      // Lazy running max in log2 units: the score is c*s with c >= 0, so the
+      // tile max is c * max(s). It moves only when some score exceeds it by
+      // more than kTau; after the first full page it is finite.
+      const float c = cur.c;
+      bool need = false;
+      float smax[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        smax[h] = fmaxf(fmaxf(s[0][h], s[1][h]), fmaxf(s[2][h], s[3][h]));
+        need |= smax[h] * c > m[h] + kTau;
+      }
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float x = fmaxf(smax[h], shfl_xor_f32(smax[h], 16));
+          x = fmaxf(x, shfl_xor_f32(x, 32));
+          const float mn = fmaxf(m[h], x * c);
+          const float alpha = fast_exp2(m[h] - mn);  // 0 when m was -inf
+          l[h] *= alpha;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[h][j] *= alpha;
+          m[h] = mn;
+        }
+      }
+
+      // p = 2^(c*s - m); the fp8 V scale is folded into the weights that
+      // multiply V, not into the normaliser.
+      float e[4][G];
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[i][h] = fast_exp2(__builtin_fmaf(s[i][h], c, -m[h]));
+      if (partial) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int h = 0; h < G; ++h) e[i][h] = tok_ok[i] ? e[i][h] : 0.f;
+      }
+      uint32_t pp01[G], pp23[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        l[h] += (e[0][h] + e[1][h]) + (e[2][h] + e[3][h]);
+        if constexpr (FP8) {
+          const float vsc = cur.vsc;
+          pp01[h] = pack_bf16x2(e[0][h] * vsc, e[1][h] * vsc);
+          pp23[h] = pack_bf16x2(e[2][h] * vsc, e[3][h] * vsc);
+        } else {
+          pp01[h] = pack_bf16x2(e[0][h], e[1][h]);
+          pp23[h] = pack_bf16x2(e[2][h], e[3][h]);
+        }
+      }
+
+      uint32_t v01[8], v23[8];
+      token_pairs<FP8>(cur.v[0], cur.v[1], v01);
+      token_pairs<FP8>(cur.v[2], cur.v[3], v23);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          acc[h][j] = dot2_bf16(pp01[h], v01[j], acc[h][j]);
+          acc[h][j] = dot2_bf16(pp23[h], v23[j], acc[h][j]);
+        }
+    };
+
+#pragma unroll
+    for (int j = 0; j < NB - 1; ++j)
+      if (p0 + j < p1) issue(buf[j], p0 + j);
+    // Unrolled by NB so that every buffer index is a compile-time constant.
+    for (int p = p0; p < p1; p += NB) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if (p + j < p1) {
+          if (p + j + NB - 1 < p1) issue(buf[(j + NB - 1) % NB], p + j + NB - 1);
+          consume(buf[j], p + j);
+        }
       }
     }
 
-    uint32_t v01[8], v23[8];
-    token_pairs<FP8>(cur.v[0], cur.v[1], v01);
-    token_pairs<FP8>(cur.v[2], cur.v[3], v23);
+    // Combine the 4 token rows of the wave (same running max), then the 4
+    // waves through LDS, into this split's normalised partial output and LSE.
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int h = 0; h < G; ++h) {
+      l[h] += shfl_xor_f32(l[h], 16);
+      l[h] += shfl_xor_f32(l[h], 32);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        acc[h][j] = dot2_bf16(pp01[h], v01[j], acc[h][j]);
-        acc[h][j] = dot2_bf16(pp23[h], v23[j], acc[h][j]);
-      }
-  };
-
-#pragma unroll
-  for (int j = 0; j < NB - 1; ++j)
-    if (p0 + j < p1) issue(buf[j], p0 + j);
-  // Unrolled by NB so that every buffer index is a compile-time constant.
-  for (int p = p0; p < p1; p += NB) {
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      if (p + j < p1) {
-        if (p + j + NB - 1 < p1) issue(buf[(j + NB - 1) % NB], p + j + NB - 1);
-        consume(buf[j], p + j);
+        acc[h][j] += shfl_xor_f32(acc[h][j], 16);
+        acc[h][j] += shfl_xor_f32(acc[h][j], 32);
       }
     }
-  }
-
-  // Combine the 4 token rows of the wave (same running max), then the 4
-  // waves through LDS, into this split's normalised partial output and LSE.
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    l[h] += shfl_xor_f32(l[h], 16);
-    l[h] += shfl_xor_f32(l[h], 32);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      acc[h][j] += shfl_xor_f32(acc[h][j], 16);
-      acc[h][j] += shfl_xor_f32(acc[h][j], 32);
-    }
-  }
-  __shared__ float s_o[4 * G * kD];
-  __shared__ float s_m[64], s_l[64];
-  if (row == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      *reinterpret_cast<float4*>(&s_o[(wave * G + h) * kD + dc * 8]) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-      *reinterpret_cast<float4*>(&s_o[(wave * G + h) * kD + dc * 8 + 4]) =
-          make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
-    }
-    if (dc == 0) {
+    __shared__ float s_o[4 * G * kD];
+    __shared__ float s_m[64], s_l[64];
+    if (row == 0) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        s_m[16 * wave + h] = m[h];
-        s_l[16 * wave + h] = l[h];
+        *reinterpret_cast<float4*>(&s_o[(wave * G + h) * kD + dc * 8]) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+        *reinterpret_cast<float4*>(&s_o[(wave * G + h) * kD + dc * 8 + 4]) =
+            make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+      }
+      if (dc == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          s_m[16 * wave + h] = m[h];
+          s_l[16 * wave + h] = l[h];
+        }
       }
     }
+    __syncthreads();
+    finish_work_item<G>(a, b, g, split, s_m, s_l, s_o);
+    __syncthreads();  // the next item reuses this workgroup's LDS
   }
-  __syncthreads();
-  finish_work_item<G>(a, b, g, split, s_m, s_l, s_o);
 }
 
 // One workgroup of 4 wavefronts per (request, query head) merges that
@@ -483,9 +489,9 @@ __global__ void gather_kv_kernel(const char* pages, int elem_bytes, const int32_
 template <int G>
 hipError_t launch_split_g(const DecodeArgs& a, int fp8, hipStream_t s) {
   if (fp8)
-    hipLaunchKernelGGL((decode_split_kernel<G, true, kRingFp8>), dim3(a.n_items), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_split_kernel<G, true, kRingFp8>), dim3(a.grid), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_split_kernel<G, false, kRingBf16>), dim3(a.n_items), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_split_kernel<G, false, kRingBf16>), dim3(a.grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -117,261 +117,267 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int kLdsB = kRingB > kEpiB ? kRingB : kEpiB;
   __shared__ __attribute__((aligned(16))) char lds[kLdsB];
 
-  const WorkItem it = a.items[blockIdx.x];
-  const int b = it.b;
-  const int g = it.g_split & 255;
-  const int split = it.g_split >> 8;
-  const int p0 = it.page_begin, p1 = it.page_end;
-  const int L = a.seqlens[b];
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int col = lane & 15, grp = lane >> 4;
-  char* vring = lds + wave * kSlots * kVq;
+  // Workgroup w runs items w, w + grid, ... (one item unless the plan
+  // packed several segments per workgroup).
+  for (int ii = blockIdx.x; ii < a.n_items; ii += gridDim.x) {
+    const WorkItem it = a.items[ii];
+    if (it.b < 0) continue;  // padding of a balanced plan
+    const int b = it.b;
+    const int g = it.g_split & 255;
+    const int split = it.g_split >> 8;
+    const int p0 = it.page_begin, p1 = it.page_end;
+    const int L = a.seqlens[b];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int col = lane & 15, grp = lane >> 4;
+    char* vring = lds + wave * kSlots * kVq;
 
-  // ---- Q^T as the B operand of S = K Q^T: lane (col = head, grp), MFMA kk,
-  // k-element e is dim dim_of(kk, grp, e); heads past G are zero columns.
-  // The dim order of the contraction is free; it is chosen so that each K
-  // fragment is one 16-byte load (fp8: one load feeds two MFMAs).
-  auto dim0 = [&](int kk) { return FP8 ? 64 * (kk >> 1) + 16 * grp + 8 * (kk & 1) : 32 * kk + 8 * grp; };
-  bf16x8_t qf[4];
-  {
-    const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + g * G + (col < G ? col : 0)) * kD;
+    // ---- Q^T as the B operand of S = K Q^T: lane (col = head, grp), MFMA kk,
+    // k-element e is dim dim_of(kk, grp, e); heads past G are zero columns.
+    // The dim order of the contraction is free; it is chosen so that each K
+    // fragment is one 16-byte load (fp8: one load feeds two MFMAs).
+    auto dim0 = [&](int kk) { return FP8 ? 64 * (kk >> 1) + 16 * grp + 8 * (kk & 1) : 32 * kk + 8 * grp; };
+    bf16x8_t qf[4];
+    {
+      const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + g * G + (col < G ? col : 0)) * kD;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (col < G) v = *reinterpret_cast<const uint4*>(qh + dim0(kk));
-      qf[kk] = __builtin_bit_cast(bf16x8_t, v);
+      for (int kk = 0; kk < 4; ++kk) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (col < G) v = *reinterpret_cast<const uint4*>(qh + dim0(kk));
+        qf[kk] = __builtin_bit_cast(bf16x8_t, v);
+      }
     }
-  }
-  const float c_base = a.scale * kLog2e;
+    const float c_base = a.scale * kLog2e;
 
-  // ---- per-lane state: m, l of head `col` (log2 units; equal in the four
-  // lanes of a head), O of heads 4*grp + e and dims 16*nb + col.
-  float m = kNegInf, l = 0.f;
-  f32x4_t acc[8];
+    // ---- per-lane state: m, l of head `col` (log2 units; equal in the four
+    // lanes of a head), O of heads 4*grp + e and dims 16*nb + col.
+    float m = kNegInf, l = 0.f;
+    f32x4_t acc[8];
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const char* kpool = reinterpret_cast<const char*>(a.k_pages);
-  const char* vpool = reinterpret_cast<const char*>(a.v_pages);
-  const int32_t* table = a.page_table + (size_t)b * a.stride;
+    const char* kpool = reinterpret_cast<const char*>(a.k_pages);
+    const char* vpool = reinterpret_cast<const char*>(a.v_pages);
+    const int32_t* table = a.page_table + (size_t)b * a.stride;
 
-  // Byte offsets inside a (page, KV head) block.
-  //   K fragment: token 16*wave + col, dims dim0(kk) .. +7 (fp8: +15).
-  //   bf16 V direct load i: LDS row r = 4i + grp of the slot, 16-byte
-  //     position col holds global unit col ^ 2*(r & 7) of token 16*wave + r
-  //     (32-byte segments XOR-swizzled by row, for conflict-free
-  //     transposing reads).
-  //   fp8 V load m: token 16*wave + 8m + lane/8, 16 codes at 16*(lane & 7).
-  int k_off[FP8 ? 2 : 4];
+    // Byte offsets inside a (page, KV head) block.
+    //   K fragment: token 16*wave + col, dims dim0(kk) .. +7 (fp8: +15).
+    //   bf16 V direct load i: LDS row r = 4i + grp of the slot, 16-byte
+    //     position col holds global unit col ^ 2*(r & 7) of token 16*wave + r
+    //     (32-byte segments XOR-swizzled by row, for conflict-free
+    //     transposing reads).
+    //   fp8 V load m: token 16*wave + 8m + lane/8, 16 codes at 16*(lane & 7).
+    int k_off[FP8 ? 2 : 4];
 #pragma unroll
-  for (int i = 0; i < (FP8 ? 2 : 4); ++i)
-    k_off[i] = (16 * wave + col) * kRowB + (FP8 ? 64 * i + 16 * grp : (32 * i + 8 * grp) * 2);
-  int v_off[FP8 ? 2 : 4];
-#pragma unroll
-  for (int i = 0; i < (FP8 ? 2 : 4); ++i) {
-    if constexpr (FP8) {
-      v_off[i] = (16 * wave + 8 * i + (lane >> 3)) * kRowB + 16 * (lane & 7);
-    } else {
-      const int r = 4 * i + grp;
-      v_off[i] = (16 * wave + r) * kRowB + 16 * (col ^ (2 * (r & 7)));
-    }
-  }
-  // Transposing read of dim block nb: lane (grp, col) addresses row
-  // 4*grp + (col >> 2), dims 16*nb + 4*(col & 3) .. +3 (after the swizzle).
-  const int tr_row = 4 * grp + (col >> 2);
-  const int tr_base = tr_row * (kD * 2) + 8 * (col & 3);
-  const int tr_swz = tr_row & 7;
-
-  // ---- Page ids (and fp8 scales), 64 pages per window: lane i holds page
-  // w0 + i, read with one vector load each.
-  int w0 = p0;
-  int tbl = -1;
-  float kscl = 0.f, vscl = 0.f;
-  auto load_window = [&]() {
-    const int pp = w0 + lane;
-    tbl = pp < p1 ? table[pp] : -1;
-    if constexpr (FP8) {
-      const bool ok = (unsigned)tbl < (unsigned)a.num_pages;
-      kscl = ok ? a.k_scale[(size_t)tbl * a.Hkv + g] : 0.f;
-      vscl = ok ? a.v_scale[(size_t)tbl * a.Hkv + g] : 0.f;
-    }
-  };
-  load_window();
-
-  // ---- Ring of NB pages: page p lives in buf[(p - p0) % NB] (and, bf16, in
-  // LDS slot (p - p0) % NB); its loads are issued NB-1 pages ahead of use.
-  MPage<FP8> buf[NB];
-  auto issue = [&](MPage<FP8>& d, int p, int slot) {
-    if (p - w0 == 64) {
-      w0 += 64;
-      load_window();
-    }
-    const int pid = __builtin_amdgcn_readlane(tbl, p - w0);
-    const bool ok = (unsigned)pid < (unsigned)a.num_pages;
-    d.nvalid = ok ? min(64, L - p * 64) : 0;
-    if constexpr (FP8) {
-      d.c = c_base * __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, kscl), p - w0));
-      d.vsc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, vscl), p - w0));
-    } else {
-      d.c = c_base;
-      d.vsc = 1.f;
-    }
-    // The block offset is uniform; readfirstlane makes that visible to the
-    // compiler (otherwise each buffer load gets a waterfall loop).
-    const size_t off_v = ((size_t)(ok ? pid : 0) * a.Hkv + g) * kBlk;
-    const size_t off = ((size_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(off_v >> 32)) << 32) |
-                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)off_v);
-    // Resources end at the last valid token: the tail reads as zeros.
-    const int nbytes = __builtin_amdgcn_readfirstlane(d.nvalid * kRowB);
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kpool + off), (short)0, nbytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vpool + off), (short)0, nbytes, 0x00020000);
+    for (int i = 0; i < (FP8 ? 2 : 4); ++i)
+      k_off[i] = (16 * wave + col) * kRowB + (FP8 ? 64 * i + 16 * grp : (32 * i + 8 * grp) * 2);
+    int v_off[FP8 ? 2 : 4];
 #pragma unroll
     for (int i = 0; i < (FP8 ? 2 : 4); ++i) {
-      const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(rk, k_off[i], 0, kNT);
-      d.k[i] = make_uint4(t.x, t.y, t.z, t.w);
-    }
-    if constexpr (FP8) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(rv, v_off[i], 0, kNT);
-        d.v[i] = make_uint4(t.x, t.y, t.z, t.w);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        load_to_lds16(rv, vring + slot * kVq + i * 1024, v_off[i]);
-    }
-  };
-
-  auto consume = [&](MPage<FP8>& cur, int p, int slot, int younger_pages) {
-    // S = K Q^T for this wavefront's 16 tokens.
-    bf16x8_t kf[4];
-    if constexpr (FP8) {
-      fp8x16_to_bf16(cur.k[0], kf[0], kf[1]);
-      fp8x16_to_bf16(cur.k[1], kf[2], kf[3]);
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) kf[kk] = __builtin_bit_cast(bf16x8_t, cur.k[kk]);
-    }
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) s = mfma_qk(kf[kk], qf[kk], s);
-
-    // fp8: this page's V, converted to bf16, into the wavefront's LDS slot
-    // (row t = 8i + lane/8, 32-byte segment lane & 7 stored at (lane & 7) ^ (t & 7)).
-    if constexpr (FP8) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        bf16x8_t lo, hi;
-        fp8x16_to_bf16(cur.v[i], lo, hi);
-        const int t = 8 * i + (lane >> 3);
-        char* dst = vring + t * (kD * 2) + 32 * ((lane & 7) ^ (t & 7));
-        *reinterpret_cast<bf16x8_t*>(dst) = lo;
-        *reinterpret_cast<bf16x8_t*>(dst + 16) = hi;
+      if constexpr (FP8) {
+        v_off[i] = (16 * wave + 8 * i + (lane >> 3)) * kRowB + 16 * (lane & 7);
+      } else {
+        const int r = 4 * i + grp;
+        v_off[i] = (16 * wave + r) * kRowB + 16 * (col ^ (2 * (r & 7)));
       }
     }
+    // Transposing read of dim block nb: lane (grp, col) addresses row
+    // 4*grp + (col >> 2), dims 16*nb + 4*(col & 3) .. +3 (after the swizzle).
+    const int tr_row = 4 * grp + (col >> 2);
+    const int tr_base = tr_row * (kD * 2) + 8 * (col & 3);
+    const int tr_swz = tr_row & 7;
 
-    // Tail tokens of a partial page: scores -inf, weights 0.
-    const bool partial = cur.nvalid < 64;
-    bool ok[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ok[e] = 16 * wave + 4 * grp + e < cur.nvalid;
-    if (partial) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s[e] = ok[e] ? s[e] : kNegInf;
-    }
+    // ---- Page ids (and fp8 scales), 64 pages per window: lane i holds page
+    // w0 + i, read with one vector load each.
+    int w0 = p0;
+    int tbl = -1;
+    float kscl = 0.f, vscl = 0.f;
+    auto load_window = [&]() {
+      const int pp = w0 + lane;
+      tbl = pp < p1 ? table[pp] : -1;
+      if constexpr (FP8) {
+        const bool ok = (unsigned)tbl < (unsigned)a.num_pages;
+        kscl = ok ? a.k_scale[(size_t)tbl * a.Hkv + g] : 0.f;
+        vscl = ok ? a.v_scale[(size_t)tbl * a.Hkv + g] : 0.f;
+      }
+    };
+    load_window();
 
-    // Lazy running max of head `col`: c*s with c >= 0.
-    const float c = cur.c;
-    const float lmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    if (__builtin_amdgcn_ballot_w64(lmax * c > m + kTau) != 0) {
-      float x = fmaxf(lmax, shfl_xor_f32(lmax, 16));
-      x = fmaxf(x, shfl_xor_f32(x, 32));
-      const float mn = fmaxf(m, x * c);
-      const float alpha = fast_exp2(m - mn);  // 0 while m is -inf
-      l *= alpha;
-      m = mn;
-      // O rows are heads 4*grp + e: their factors come from lanes 4*grp + e.
+    // ---- Ring of NB pages: page p lives in buf[(p - p0) % NB] (and, bf16, in
+    // LDS slot (p - p0) % NB); its loads are issued NB-1 pages ahead of use.
+    MPage<FP8> buf[NB];
+    auto issue = [&](MPage<FP8>& d, int p, int slot) {
+      if (p - w0 == 64) {
+        w0 += 64;
+        load_window();
+      }
+      const int pid = __builtin_amdgcn_readlane(tbl, p - w0);
+      const bool ok = (unsigned)pid < (unsigned)a.num_pages;
+      d.nvalid = ok ? min(64, L - p * 64) : 0;
+      if constexpr (FP8) {
+        d.c = c_base * __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, kscl), p - w0));
+        d.vsc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, vscl), p - w0));
+      } else {
+        d.c = c_base;
+        d.vsc = 1.f;
+      }
+      // The block offset is uniform; readfirstlane makes that visible to the
+      // compiler (otherwise each buffer load gets a waterfall loop).
+      const size_t off_v = ((size_t)(ok ? pid : 0) * a.Hkv + g) * kBlk;
+      const size_t off = ((size_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(off_v >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)off_v);
+      // Resources end at the last valid token: the tail reads as zeros.
+      const int nbytes = __builtin_amdgcn_readfirstlane(d.nvalid * kRowB);
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kpool + off), (short)0, nbytes, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vpool + off), (short)0, nbytes, 0x00020000);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float ae = __shfl(alpha, 4 * grp + e, 64);
+      for (int i = 0; i < (FP8 ? 2 : 4); ++i) {
+        const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(rk, k_off[i], 0, kNT);
+        d.k[i] = make_uint4(t.x, t.y, t.z, t.w);
+      }
+      if constexpr (FP8) {
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) acc[nb][e] *= ae;
+        for (int i = 0; i < 2; ++i) {
+          const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(rv, v_off[i], 0, kNT);
+          d.v[i] = make_uint4(t.x, t.y, t.z, t.w);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          load_to_lds16(rv, vring + slot * kVq + i * 1024, v_off[i]);
+      }
+    };
+
+    auto consume = [&](MPage<FP8>& cur, int p, int slot, int younger_pages) {
+      // S = K Q^T for this wavefront's 16 tokens.
+      bf16x8_t kf[4];
+      if constexpr (FP8) {
+        fp8x16_to_bf16(cur.k[0], kf[0], kf[1]);
+        fp8x16_to_bf16(cur.k[1], kf[2], kf[3]);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) kf[kk] = __builtin_bit_cast(bf16x8_t, cur.k[kk]);
+      }
+      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) s = mfma_qk(kf[kk], qf[kk], s);
+
+      // fp8: this page's V, converted to bf16, into the wavefront's LDS slot
+      // (row t = 8i + lane/8, 32-byte segment lane & 7 stored at (lane & 7) ^ (t & 7)).
+      if constexpr (FP8) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          bf16x8_t lo, hi;
+          fp8x16_to_bf16(cur.v[i], lo, hi);
+          const int t = 8 * i + (lane >> 3);
+          char* dst = vring + t * (kD * 2) + 32 * ((lane & 7) ^ (t & 7));
+          *reinterpret_cast<bf16x8_t*>(dst) = lo;
+          *reinterpret_cast<bf16x8_t*>(dst + 16) = hi;
+        }
+      }
+
+      // Tail tokens of a partial page: scores -inf, weights 0.
+      const bool partial = cur.nvalid < 64;
+      bool ok[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ok[e] = 16 * wave + 4 * grp + e < cur.nvalid;
+      if (partial) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[e] = ok[e] ? s[e] : kNegInf;
+      }
+
+      // Lazy running max of head `col`: c*s with c >= 0.
+      const float c = cur.c;
+      const float lmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      if (__builtin_amdgcn_ballot_w64(lmax * c > m + kTau) != 0) {
+        float x = fmaxf(lmax, shfl_xor_f32(lmax, 16));
+        x = fmaxf(x, shfl_xor_f32(x, 32));
+        const float mn = fmaxf(m, x * c);
+        const float alpha = fast_exp2(m - mn);  // 0 while m is -inf
+        l *= alpha;
+        m = mn;
+        // O rows are heads 4*grp + e: their factors come from lanes 4*grp + e.
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ae = __shfl(alpha, 4 * grp + e, 64);
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) acc[nb][e] *= ae;
+        }
+      }
+
+      // P = 2^(c*s - m) (fp8: times the V scale), already in A-operand layout.
+      float pe[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pe[e] = fast_exp2(__builtin_fmaf(s[e], c, -m));
+      if (partial) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pe[e] = ok[e] ? pe[e] : 0.f;
+      }
+      l += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+      const float vsc = cur.vsc;
+      const bf16x4_t pa = __builtin_bit_cast(
+          bf16x4_t, make_uint2(pack_bf16x2(pe[0] * vsc, pe[1] * vsc), pack_bf16x2(pe[2] * vsc, pe[3] * vsc)));
+
+      // O += P V, V^T blocks of 16 dims through the transposing read.
+      if constexpr (!FP8) wait_vmem_pages(younger_pages);
+      const char* vs = vring + slot * kVq + tr_base;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const bf16x4_t vb = lds_read_tr16(vs + 32 * (nb ^ tr_swz));
+        acc[nb] = mfma_pv(pa, vb, acc[nb]);
+      }
+    };
+
+#pragma unroll
+    for (int j = 0; j < NB - 1; ++j)
+      if (p0 + j < p1) issue(buf[j], p0 + j, j);
+    // Unrolled by NB so that buffer and slot indices are compile-time constants.
+    for (int p = p0; p < p1; p += NB) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if (p + j < p1) {
+          const int nxt = p + j + NB - 1;
+          if (nxt < p1) issue(buf[(j + NB - 1) % NB], nxt, FP8 ? 0 : (j + NB - 1) % NB);
+          consume(buf[j], p + j, FP8 ? 0 : j, min(NB - 1, p1 - 1 - (p + j)));
+        }
       }
     }
 
-    // P = 2^(c*s - m) (fp8: times the V scale), already in A-operand layout.
-    float pe[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) pe[e] = fast_exp2(__builtin_fmaf(s[e], c, -m));
-    if (partial) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pe[e] = ok[e] ? pe[e] : 0.f;
+    // ---- Epilogue: l summed over the four lanes of each head, then the four
+    // wavefronts' (m, l, O) merged through LDS into this split's normalised
+    // partial output and LSE.
+    l += shfl_xor_f32(l, 16);
+    l += shfl_xor_f32(l, 32);
+    __syncthreads();  // every wavefront is done with its ring
+    float* s_m = reinterpret_cast<float*>(lds);  // [4][16]
+    float* s_l = s_m + 64;                       // [4][16]
+    float* s_o = s_l + 64;                       // [4][G][128]
+    if (grp == 0) {
+      s_m[wave * 16 + col] = m;
+      s_l[wave * 16 + col] = l;
     }
-    l += (pe[0] + pe[1]) + (pe[2] + pe[3]);
-    const float vsc = cur.vsc;
-    const bf16x4_t pa = __builtin_bit_cast(
-        bf16x4_t, make_uint2(pack_bf16x2(pe[0] * vsc, pe[1] * vsc), pack_bf16x2(pe[2] * vsc, pe[3] * vsc)));
-
-    // O += P V, V^T blocks of 16 dims through the transposing read.
-    if constexpr (!FP8) wait_vmem_pages(younger_pages);
-    const char* vs = vring + slot * kVq + tr_base;
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const bf16x4_t vb = lds_read_tr16(vs + 32 * (nb ^ tr_swz));
-      acc[nb] = mfma_pv(pa, vb, acc[nb]);
-    }
-  };
-
+    for (int e = 0; e < 4; ++e) {
+      const int h = 4 * grp + e;
+      if (h < G) {
 #pragma unroll
-  for (int j = 0; j < NB - 1; ++j)
-    if (p0 + j < p1) issue(buf[j], p0 + j, j);
-  // Unrolled by NB so that buffer and slot indices are compile-time constants.
-  for (int p = p0; p < p1; p += NB) {
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      if (p + j < p1) {
-        const int nxt = p + j + NB - 1;
-        if (nxt < p1) issue(buf[(j + NB - 1) % NB], nxt, FP8 ? 0 : (j + NB - 1) % NB);
-        consume(buf[j], p + j, FP8 ? 0 : j, min(NB - 1, p1 - 1 - (p + j)));
+        for (int nb = 0; nb < 8; ++nb) s_o[(wave * G + h) * kD + 16 * nb + col] = acc[nb][e];
       }
     }
+    __syncthreads();
+    finish_work_item<G>(a, b, g, split, s_m, s_l, s_o);
+    __syncthreads();  // the next item reuses this workgroup's LDS
   }
-
-  // ---- Epilogue: l summed over the four lanes of each head, then the four
-  // wavefronts' (m, l, O) merged through LDS into this split's normalised
-  // partial output and LSE.
-  l += shfl_xor_f32(l, 16);
-  l += shfl_xor_f32(l, 32);
-  __syncthreads();  // every wavefront is done with its ring
-  float* s_m = reinterpret_cast<float*>(lds);  // [4][16]
-  float* s_l = s_m + 64;                       // [4][16]
-  float* s_o = s_l + 64;                       // [4][G][128]
-  if (grp == 0) {
-    s_m[wave * 16 + col] = m;
-    s_l[wave * 16 + col] = l;
-  }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int h = 4 * grp + e;
-    if (h < G) {
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) s_o[(wave * G + h) * kD + 16 * nb + col] = acc[nb][e];
-    }
-  }
-  __syncthreads();
-  finish_work_item<G>(a, b, g, split, s_m, s_l, s_o);
 }
 
 template <int G>
 hipError_t launch_g(const DecodeArgs& a, int fp8, hipStream_t s) {
   if (fp8)
-    hipLaunchKernelGGL((decode_mfma_kernel<G, true, 4>), dim3(a.n_items), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<G, true, 4>), dim3(a.grid), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<G, false, 3>), dim3(a.n_items), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<G, false, 3>), dim3(a.grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

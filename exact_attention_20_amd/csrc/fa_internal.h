@@ -105,6 +105,7 @@ struct WorkItem {
 struct DecodeArgs {
   const WorkItem* items;
   int n_items;
+  int grid;                       // workgroups; workgroup w runs items w, w + grid, ... (b < 0: padding)
   const int32_t* splits_per_req;  // [B]
   const void* q;                  // [B, Hq, D] bf16
   const void* k_pages;            // [P, Hkv, 64, D]
@@ -136,14 +137,17 @@ hipError_t launch_gather_kv(const void* pages, int elem_bytes, const int32_t* pa
 struct PlanResult {
   int num_splits = 0;   // max split count over requests
   int chunk_pages = 0;  // target pages per work item (auto mode)
-  int n_items = 0;
+  int n_items = 0;      // including padding items (b = -1)
+  int grid = 0;         // workgroups to launch (each runs items w, w + grid, ...)
 };
 
 // Returns 0 or a negative fa_status. `items` (capacity entries) and
-// `splits` (B entries) may be null to only count.
+// `splits` (B entries) may be null to only count. With `windows` (auto mode
+// only) the plan may instead cut every KV head's pages into cost-balanced
+// windows, one per workgroup of a single round.
 int plan_decode_host(const int32_t* seqlens, int B, int stride, int Hkv, int num_splits_request,
                      int num_cus, WorkItem* items, int capacity, int32_t* splits,
-                     PlanResult* res);
+                     PlanResult* res, bool windows = true);
 
 // Ragged prefill work list: (request, query tile) pairs of kPrefillRows new
 // tokens, sorted by decreasing key count. Returns the item count, or a

@@ -8,6 +8,7 @@
 //
 // Pure host code (no HIP call): it is unit-tested on the CPU.
 #include <algorithm>
+#include <climits>
 #include <cstdint>
 #include <cstdlib>
 #include <functional>
@@ -32,6 +33,10 @@ constexpr int kResidentPerCU = 2;
 // Fixed cost of one work item in page-equivalents (query load, first-page
 // latency, epilogue and partial write), used to compare chunk sizes.
 constexpr double kItemCost = 2.0;
+
+// The same cost for a segment of a balanced window (a workgroup's second
+// item starts only after its first has finished).
+constexpr int64_t kWindowItemCost = 2;
 
 // Number of work items for a given chunk size.
 int64_t count_items(const std::vector<int>& pages, int Hkv, int chunk) {
@@ -98,11 +103,49 @@ int auto_chunk(const std::vector<int>& pages, int Hkv, int num_cus) {
   return best;
 }
 
+// Balanced windows for a single round of workgroups. The pages of all
+// requests, concatenated in request order (the same for every KV head), are
+// cut into at most `per_head` windows of cost at most C, where a window's cost
+// is its pages plus kItemCost for each of its segments (its parts inside one
+// request). Returns the number of windows needed for bound C (a huge number
+// if some window could take no page).
+int64_t count_windows(const std::vector<int>& pages, int64_t C) {
+  int64_t windows = 0;
+  size_t b = 0;
+  int64_t rem = 0;
+  auto next = [&] {
+    while (b < pages.size() && pages[b] == 0) ++b;
+    rem = b < pages.size() ? pages[b] : 0;
+  };
+  next();
+  while (rem > 0) {
+    ++windows;
+    int64_t cost = 0;
+    while (rem > 0) {
+      const int64_t avail = C - cost - kWindowItemCost;
+      if (avail < 1) {
+        if (cost == 0) return INT64_MAX;
+        break;
+      }
+      const int64_t take = std::min(avail, rem);
+      cost += kWindowItemCost + take;
+      rem -= take;
+      if (rem == 0) {
+        ++b;
+        next();
+      } else {
+        break;
+      }
+    }
+  }
+  return windows;
+}
+
 }  // namespace
 
 int plan_decode_host(const int32_t* seqlens, int B, int stride, int Hkv, int num_splits_request,
                      int num_cus, WorkItem* items, int capacity, int32_t* splits,
-                     PlanResult* res) {
+                     PlanResult* res, bool windows) {
   if (!seqlens || B < 1 || stride < 1 || Hkv < 1 || Hkv > kMaxHeads || num_cus < 1 ||
       num_splits_request < 0 || !res)
     return -1;
@@ -118,6 +161,83 @@ int plan_decode_host(const int32_t* seqlens, int B, int stride, int Hkv, int num
   int chunk = 0;
   if (num_splits_request == 0 && total_units > 0) chunk = auto_chunk(pages, Hkv, num_cus);
   if (num_splits_request == 0 && chunk < 1) chunk = kMinChunkPages;
+
+  // A chunk plan that fits one round of the resident workgroups is bounded by
+  // its largest item, so near-equal splits per request leave slots idle at
+  // the end. Cost-balanced windows over all requests fill every slot evenly
+  // at the price of a second segment (item) where a window crosses a request
+  // boundary; they are used when their estimated duration is shorter.
+  const int slots = std::max(1, num_cus * kResidentPerCU);
+  const int per_head = slots / Hkv;
+  if (windows && num_splits_request == 0 && total_units > 0 && per_head >= 1 &&
+      count_items(pages, Hkv, chunk) <= slots) {
+    int64_t P = 0, maxp = 0;
+    for (int n : pages) {
+      P += n;
+      maxp = std::max<int64_t>(maxp, n);
+    }
+    int64_t lo = 1 + kWindowItemCost, hi = maxp + 2 * kWindowItemCost;  // hi: one window per request
+    if (count_windows(pages, hi) > per_head) hi = P + kWindowItemCost * B + 1;
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo) / 2;
+      if (count_windows(pages, mid) <= per_head) hi = mid; else lo = mid + 1;
+    }
+    const double chunk_t = makespan(pages, Hkv, chunk, slots);
+    if (count_windows(pages, lo) <= per_head && (double)lo < chunk_t - 0.5) {
+      // Window w of head g runs on workgroup g * n_win + w; its r-th segment
+      // is item r * grid + (g * n_win + w); missing segments are padding.
+      struct Seg {
+        int b, p0, p1;
+      };
+      std::vector<std::vector<Seg>> win;
+      std::vector<int> nseg(B, 0);
+      size_t b = 0;
+      int64_t pos = 0;  // pages of request b already placed
+      while (b < pages.size() && pages[b] == 0) ++b;
+      while (b < pages.size()) {
+        win.emplace_back();
+        int64_t cost = 0;
+        while (b < pages.size()) {
+          const int64_t avail = lo - cost - kWindowItemCost;
+          if (avail < 1) break;
+          const int64_t take = std::min<int64_t>(avail, pages[b] - pos);
+          win.back().push_back(Seg{(int)b, (int)pos, (int)(pos + take)});
+          cost += kWindowItemCost + take;
+          pos += take;
+          if (pos == pages[b]) {
+            ++b;
+            pos = 0;
+            while (b < pages.size() && pages[b] == 0) ++b;
+          } else {
+            break;
+          }
+        }
+      }
+      const int n_win = (int)win.size();
+      const int grid = n_win * Hkv;
+      size_t rounds = 0;
+      for (const auto& w : win) rounds = std::max(rounds, w.size());
+      std::vector<WorkItem> list(rounds * (size_t)grid, WorkItem{-1, 0, 0, 0});
+      for (int w = 0; w < n_win; ++w)
+        for (size_t r = 0; r < win[w].size(); ++r) {
+          const Seg& sg = win[w][r];
+          const int split = nseg[sg.b]++;
+          for (int g = 0; g < Hkv; ++g)
+            list[r * grid + (size_t)g * n_win + w] = WorkItem{sg.b, g | (split << 8), sg.p0, sg.p1};
+        }
+      int max_splits = 0;
+      for (int bb = 0; bb < B; ++bb) {
+        if (splits) splits[bb] = nseg[bb];
+        max_splits = std::max(max_splits, nseg[bb]);
+      }
+      res->num_splits = max_splits;
+      res->chunk_pages = (int)lo;
+      res->n_items = (int)list.size();
+      res->grid = grid;
+      if (items) std::copy(list.begin(), list.begin() + std::min<int>(capacity, (int)list.size()), items);
+      return 0;
+    }
+  }
   // Split counts and near-equal page ranges per request.
   std::vector<WorkItem> list;
   int max_splits = 0;
@@ -141,6 +261,7 @@ int plan_decode_host(const int32_t* seqlens, int B, int stride, int Hkv, int num
   res->num_splits = max_splits;
   res->chunk_pages = chunk;
   res->n_items = (int)list.size();
+  res->grid = (int)list.size();
   if (items) {
     int n = std::min<int>(capacity, (int)list.size());
     std::copy(list.begin(), list.begin() + n, items);
@@ -270,10 +391,11 @@ int plan_cascade_host(const int32_t* seqlens, int B, int stride, int Hq, int Hkv
   });
   // Suffixes: an ordinary decode plan on the suffix lengths, then shifted.
   PlanResult r;
-  if (plan_decode_host(suffix.data(), B, stride, Hkv, 0, num_cus, nullptr, 0, nullptr, &r) != 0) return -1;
+  if (plan_decode_host(suffix.data(), B, stride, Hkv, 0, num_cus, nullptr, 0, nullptr, &r, false) != 0) return -1;
   out->items.assign(std::max(r.n_items, 1), WorkItem{});
   out->splits.assign(B, 0);
-  plan_decode_host(suffix.data(), B, stride, Hkv, 0, num_cus, out->items.data(), r.n_items, out->splits.data(), &r);
+  plan_decode_host(suffix.data(), B, stride, Hkv, 0, num_cus, out->items.data(), r.n_items, out->splits.data(), &r,
+                   false);
   out->items.resize(r.n_items);
   for (WorkItem& it : out->items) {
     const int b = it.b;

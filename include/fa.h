@@ -208,8 +208,9 @@ void fa_decode_plan_destroy(fa_decode_plan_t* plan);
 /*
  * Host view of a plan, for inspection and tests. Copies up to `capacity`
  * work items into items_out as int32 quadruples
- * (request b, kv head g, first page, end page (exclusive)) and each request's
- * split count into splits_out[B] (either pointer may be NULL).
+ * (request b, kv head g | split << 8, first page, end page (exclusive)) and
+ * each request's split count into splits_out[B] (either pointer may be NULL).
+ * Items with b = -1 are padding (see fa_decode_plan_host).
  * Returns the number of work items, or -1 on a NULL plan.
  */
 int fa_decode_plan_items(const fa_decode_plan_t* plan, int32_t* items_out, int capacity,
@@ -221,11 +222,21 @@ int fa_decode_plan_items(const fa_decode_plan_t* plan, int32_t* items_out, int c
  * quadruples as in fa_decode_plan_items and each request's split count into
  * splits_out[B]. Returns the number of work items, or a negative fa_status
  * on invalid arguments.
+ *   grid_out  receives the number of split-kernel workgroups; workgroup w
+ *             runs items w, w + grid, w + 2 grid, ... In the usual plan grid
+ *             equals the item count (one item each, longest first). When
+ *             every item fits one round of the resident workgroups, the
+ *             auto plan may instead cut each KV head's pages, concatenated
+ *             over the requests, into windows of equal estimated cost (pages
+ *             plus a fixed cost per item), one per workgroup; a window that
+ *             crosses a request boundary is two items in successive rounds,
+ *             and rounds are padded with b = -1 items. chunk_pages_out then
+ *             receives that cost bound.
  */
 int fa_decode_plan_host(const int32_t* seqlens_host, int B, int max_pages_per_req, int Hq,
                         int Hkv, int num_splits_request, int num_cus, int32_t* items_out,
                         int capacity, int32_t* splits_out, int* num_splits_out,
-                        int* chunk_pages_out);
+                        int* chunk_pages_out, int* grid_out);
 
 /*
  * fa_decode_run -- split-KV decode plus LSE merge; two kernels on `stream`,

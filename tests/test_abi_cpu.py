@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
     assert not missing, f"declared but not exported: {missing}"
     for n in declared_functions():
         assert hasattr(lib, n)
-    assert lib.fa_abi_version() == 1
+    assert lib.fa_abi_version() == 2
 
 
 def _prefill(lib, **kw):
@@ -124,9 +124,23 @@ def test_gather_rejects(lib):
 
 # ------------------------------------------------------------------ plan properties
 
-def _check_plan(seqlens, items, splits, num_splits, Hkv, forced=0):
+def _check_plan(seqlens, items, splits, num_splits, Hkv, forced=0, grid=None, chunk=None):
+    """Exact coverage and split numbering of a decode plan; an equal-chunk plan
+    (grid == item count) also has near-equal splits, longest items first; a
+    window plan keeps every workgroup's items (w, w + grid, ...) within the
+    cost bound (pages + 2 per item)."""
     L = np.asarray(seqlens)
     pages = (L + 63) // 64
+    windows = grid is not None and grid != len(items)
+    if windows:
+        assert len(items) % grid == 0 and not forced
+        for w in range(grid):
+            own = [it for it in items[w::grid].tolist() if it[0] >= 0]
+            assert own, "idle workgroup"
+            assert sum(p1 - p0 + 2 for _, _, p0, p1 in own) <= chunk
+        items = items[items[:, 0] >= 0]
+    else:
+        assert (items[:, 0] >= 0).all(), "padding outside a window plan"
     cover = {}
     for b, gs, p0, p1 in items.tolist():
         g, s = gs & 255, gs >> 8
@@ -150,12 +164,16 @@ def _check_plan(seqlens, items, splits, num_splits, Hkv, forced=0):
             if bb == b and g == 0:
                 sizes[s] = sizes.get(s, 0) + 1
         assert sorted(sizes) == list(range(splits[b]))
-        assert max(sizes.values()) - min(sizes.values()) <= 1
+        first = {s: min(p for (bb, g, p), ss in cover.items() if bb == b and g == 0 and ss == s) for s in sizes}
+        assert [first[s] for s in range(splits[b])] == sorted(first.values()), "splits out of page order"
+        if not windows:
+            assert max(sizes.values()) - min(sizes.values()) <= 1
         if forced:
             assert splits[b] == min(forced, pages[b])
     assert num_splits == max(splits.tolist() + [0])
-    lens = (items[:, 3] - items[:, 2]).tolist()
-    assert lens == sorted(lens, reverse=True), "longest items first"
+    if not windows:
+        lens = (items[:, 3] - items[:, 2]).tolist()
+        assert lens == sorted(lens, reverse=True), "longest items first"
 
 
 @pytest.mark.parametrize("wid", [4, 5])
@@ -163,12 +181,12 @@ def test_plan_workloads(lib, wid):
     w = workloads.WORKLOADS[wid]
     L = workloads.context_lengths(wid, w.B, w.lengths)
     stride = int(((L + 63) // 64).max())
-    items, splits, ns, chunk = fa.fa_decode_plan_host(L, stride, w.Hq, w.Hkv, 0, 256)
-    _check_plan(L, items, splits, ns, w.Hkv)
+    items, splits, ns, chunk, grid = fa.fa_decode_plan_host(L, stride, w.Hq, w.Hkv, 0, 256)
+    _check_plan(L, items, splits, ns, w.Hkv, grid=grid, chunk=chunk)
     total = int(((L + 63) // 64).sum()) * w.Hkv
-    # balance: every item holds at most one chunk; enough items to fill 256 CUs
+    # balance: every item holds at most one chunk; enough work to fill 256 CUs
     assert int((items[:, 3] - items[:, 2]).max()) <= chunk
-    assert len(items) >= 256 or total < 256 * 4
+    assert grid >= 256 or total < 256 * 4
 
 
 @pytest.mark.parametrize("seqlens", [[1], [0, 5, 0], [64, 65, 4096, 1, 0], list(range(0, 2000, 97))])
@@ -176,8 +194,25 @@ def test_plan_workloads(lib, wid):
 def test_plan_edge_lengths(lib, seqlens, forced):
     L = np.asarray(seqlens, dtype=np.int32)
     stride = max(1, int(((L + 63) // 64).max()))
-    items, splits, ns, _ = fa.fa_decode_plan_host(L, stride, 8, 2, forced, 16)
-    _check_plan(L, items, splits, ns, 2, forced)
+    items, splits, ns, chunk, grid = fa.fa_decode_plan_host(L, stride, 8, 2, forced, 16)
+    _check_plan(L, items, splits, ns, 2, forced, grid=grid, chunk=chunk)
+
+
+@pytest.mark.parametrize("seqlens", [
+    [3362, 320, 997, 1431, 3493, 237, 1691], [785, 1231, 211, 2060, 2061, 167, 676, 1710, 246],
+    [932, 2912, 576, 2164, 699, 207, 1597], [548, 418, 3068, 883, 47, 1706, 1381],
+])
+def test_window_plans(lib, seqlens):
+    """Batches whose equal-chunk plan fits one round get cost-balanced windows
+    (some crossing two request boundaries): exact coverage, splits in page
+    order, every workgroup within the bound, padding only in later rounds."""
+    L = np.asarray(seqlens, dtype=np.int32)
+    items, splits, ns, chunk, grid = fa.fa_decode_plan_host(L, int(((L + 63) // 64).max()), 8, 2, 0, 16)
+    assert grid < len(items), "expected a window plan"
+    _check_plan(L, items, splits, ns, 2, grid=grid, chunk=chunk)
+    it = items.numpy()
+    assert (it[:grid, 0] >= 0).all(), "the first round has no padding"
+    assert max(sum(1 for b in it[w::grid, 0] if b >= 0) for w in range(grid)) == 3
 
 
 def test_plan_is_deterministic(lib):
@@ -190,5 +225,5 @@ def test_plan_is_deterministic(lib):
 def test_workspace_size(lib):
     L = [100, 300, 0]
     n = fa.fa_decode_workspace_size(L, 8, 2, 128, 0, 16)
-    items, splits, ns, _ = fa.fa_decode_plan_host(L, 8, 8, 2, 0, 16)
+    items, splits, ns, _, _ = fa.fa_decode_plan_host(L, 8, 8, 2, 0, 16)
     assert n >= len(items) * 16 + 3 * 4 + 3 * 8 * ns * 129 * 4

@@ -7,6 +7,8 @@ import oracle
 import workloads
 from parity import check, f64, need_gpu, say
 
+SCALE = float(np.float32(1 / np.sqrt(128)))
+
 pytestmark = pytest.mark.gpu
 
 
@@ -118,6 +120,34 @@ def test_num_splits_invariance():
     for o, l in res[1:]:
         assert (o.float() - res[0][0].float()).abs().max().item() <= 4e-3
         assert (l - res[0][1]).abs().max().item() <= 1e-4
+
+
+WINDOW_CASES = [
+    # (lengths, Hq, Hkv, kv_dtype, num_cus): planned for a small CU count so
+    # that the auto plan cuts cost-balanced windows (several items per
+    # workgroup, windows crossing request boundaries, padding items)
+    ([3362, 320, 997, 1431, 3493, 237, 1691], 8, 2, "bf16", 16),
+    ([785, 1231, 211, 2060, 2061, 167, 676, 1710, 246], 8, 2, "fp8", 16),
+    ([932, 2912, 576, 2164, 699, 207, 1597], 2, 2, "bf16", 16),
+    ([1784, 1727, 425, 379, 628, 947], 4, 4, "fp8", 16),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=lambda c: f"{c[3]}-G{c[1] // c[2]}-B{len(c[0])}")
+def test_window_plans(case):
+    fa = need_gpu()
+    L, Hq, Hkv, dt, cus = case
+    say(f"[case] window plan L={L} Hq={Hq} Hkv={Hkv} {dt} cus={cus}")
+    kv = workloads.paged_inputs(len(L), Hq, Hkv, 128, dt, L, 36, nan_tails=True)
+    items, _, _, _, grid = fa.fa_decode_plan_host(kv.seqlens, kv.page_table.shape[1], Hq, Hkv, 0, cus)
+    assert grid < len(items), "the case must exercise a window plan"
+    d = to_dev(kv)
+    plan = fa.fa_decode_plan(kv.seqlens, kv.page_table, kv.num_pages, Hq, Hkv, 128,
+                             fa.BF16 if dt == "bf16" else fa.FP8_E4M3FN, 0, cus)
+    out, lse = fa.decode(plan, d["q"], d["k"], d["v"], d["pt"], d["sl"], d["ks"], d["vs"], SCALE)
+    torch.cuda.synchronize()
+    O, LSE = oracle_decode(kv, SCALE)
+    check(f"window plan {case}", f64(out), O, f64(lse), LSE, dt)
 
 
 def test_run_rejects_a_foreign_workspace():
