@@ -242,7 +242,8 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles, int nbh) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = t * kBc + 32 * h2 + 16 * (i >> 3) + 8 * hi + (i & 7);
-        const float p = key > lim ? 0.f : fast_exp2(__builtin_fmaf(s[h2][i], c, -lse2));
+        // Masked entries get a -inf argument (exp2 -> 0): a select, not a branch per element.
+        const float p = fast_exp2(key > lim ? kNegInf : __builtin_fmaf(s[h2][i], c, -lse2));
         s[h2][i] = p * (dp[h2][i] - dl);
       }
       dsf[2 * h2] = pack8(s[h2], 0);
@@ -388,15 +389,22 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
         const float4 d1 = *reinterpret_cast<const float4*>(&st_d[buf][rb + 4]);
         const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
         const float dvv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+        // Rows x of these 8 that this lane's key sees: x in [xlo, xhi) (row
+        // below Sq, causal key <= row + off, key below Sk). Masked entries
+        // get a -inf argument (exp2 -> 0), and a row without keys (LSE -inf)
+        // a +inf one: selects, where the per-element conditional form
+        // compiled to a divergent branch for every element.
+        const int xlo = a.causal ? key - off - (q0 + rb) : 0;
+        const int xhi = key < Sk ? Sq - (q0 + rb) : 0;
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           const int i = 8 * h8 + x;
-          const int q = q0 + rb + x;
-          const bool ok = q < Sq && key < Sk && (!a.causal || key <= q + off) && lv[x] != kNegInf;
-          const float p = ok ? fast_exp2(__builtin_fmaf(s[i], c, -lv[x] * kLog2e)) : 0.f;
+          const float l2 = lv[x] == kNegInf ? __builtin_inff() : lv[x] * kLog2e;
+          const float p = fast_exp2((x >= xlo) & (x < xhi) ? __builtin_fmaf(s[i], c, -l2) : kNegInf);
           s[i] = p;
           dp[i] = p * (dp[i] - dvv[x]);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
       // dV^T += dO^T P and dK^T += Q^T dS (k = rows 16*ks + 8*hi + e of this half).
 #pragma unroll
