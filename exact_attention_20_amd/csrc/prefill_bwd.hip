@@ -306,7 +306,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
 #pragma unroll
     for (int c4 = 0; c4 < BK / 64; ++c4) load_rows<KW>(vs, kt * BK + 64 * c4, v_res + c4 * kTile, wave, lane);
   }
-  const int v_base = row_base(32 * wave + col, hi);  // this lane's V row in v_res
+  int v_base = row_base(32 * wave + col, hi);  // this lane's V row in v_res
   f32x16_t dk[4], dv[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -324,7 +324,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
   const int per_head = max(0, n_qt - qt0);
   const int n_steps = per_head * G;
 
-  const int r_base = row_base(kperm(col), hi);
+  int r_base = row_base(kperm(col), hi);
   int t_base[2];
   tr_bases(lane, t_base);
 
@@ -355,6 +355,9 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
   __syncthreads();
 
   for (int st = 0; st < n_steps; ++st) {
+    // The per-step offsets base ^ const are cheap to form where they are
+    // used; kept from outside the loop they would be spilled.
+    asm volatile("" : "+v"(r_base), "+v"(v_base), "+v"(t_base[0]), "+v"(t_base[1]));
     const int buf = st & 1;
     if (st + 1 < n_steps) issue(st + 1, buf ^ 1);
     const int q0 = (qt0 + st % per_head) * kBc;
