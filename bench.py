@@ -394,7 +394,7 @@ PMC_LEGS = {
     "cascade_wl7": ("--only cascade --no-plain-compare", ["prefill_bf16_kernel", "decode_mfma_kernel", "lse_merge_kernel"],
                     "exact_attention_20_amd/csrc/prefill_bf16.hip+" + DECODE_SRC),
     "prefill_fp8_wl8": ("--only fp8", ["prefill_fp8_kernel"], "exact_attention_20_amd/csrc/prefill_fp8.hip"),
-    "backward_wl2": ("--only bwd", ["bwd_delta_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel"],
+    "backward_wl2": ("--only bwd", ["bwd_dq_kernel", "bwd_dkdv_kernel"],
                      "exact_attention_20_amd/csrc/prefill_bwd.hip"),
     "copy": ("--only copy", ["neg"], None),
 }
@@ -874,7 +874,7 @@ def main():
                "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                             "traffic": read_traffic("backward_wl2_traffic.txt", "exact_attention_20_amd/csrc/prefill_bwd.hip"),
-                            "kernel": "bwd_delta_kernel + bwd_dq_kernel + bwd_dkdv_kernel", "flops_per_launch": flops},
+                            "kernel": "bwd_dq_kernel + bwd_dkdv_kernel", "flops_per_launch": flops},
                "cpu_baseline": res["bwd_cpu"],
                "config": {"workload": wb.name + " (backward)", "B": wb.B, "Hq": wb.Hq, "Hkv": wb.Hkv, "S": wb.S,
                           "D": wb.D, "causal": True}}

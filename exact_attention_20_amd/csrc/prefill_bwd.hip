@@ -7,16 +7,18 @@
 // Jacobian) it forms dS = P * (dP - D) with dP = dO V^T, then
 //   dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO.
 //
-// Three kernels, no atomics:
-//  * bwd_delta_kernel: D_i, 16 lanes per row.
+// Two kernels, no atomics:
 //  * bwd_dq_kernel: shaped like the forward kernel. 8 wavefronts x 32 query
-//    rows; 64-key tiles of K and V stream through LDS. Per tile,
+//    rows; it first forms D_i from the dO row it holds and the O row (and
+//    writes it for the second kernel); 64-key tiles of K and V stream
+//    through LDS. Per tile,
 //    S^T = K Q^T and dP^T = V dO^T (K, V rows from LDS in the permuted row
 //    order that makes each accumulator usable as a later operand; Q and dO in
 //    registers), dS^T = P^T (dP^T - D) packed to bf16, and dQ^T += K^T dS^T
 //    with K^T from gfx950's transposing LDS read (as V^T in the forward).
-//  * bwd_dkdv_kernel: the transposed twin. 8 wavefronts x 32 keys with their
-//    K and V rows in registers; 64-row tiles of Q and dO (and their LSE, D)
+//  * bwd_dkdv_kernel: the transposed twin. 8 wavefronts x 32 keys, their K
+//    rows in registers and the workgroup's V rows resident in LDS; 64-row
+//    tiles of Q and dO (and their LSE, D)
 //    stream through LDS for every query head that reads this KV head. Per
 //    32-row half, S = Q K^T and dP = dO V^T (Q, dO rows in permuted order),
 //    then dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T from transposing
@@ -44,31 +46,13 @@ struct BwdArgs {
   const uint16_t* o;    // [B, Hq, Sq, D] forward output
   const uint16_t* dO;   // [B, Hq, Sq, D]
   const float* lse;     // [B, Hq, Sq] forward LSE (natural log)
-  float* delta;         // [B, Hq, Sq] D_i (written by the first kernel)
+  float* delta;         // [B, Hq, Sq] D_i (written by the dQ kernel, read by dK/dV)
   uint16_t* dq;         // [B, Hq, Sq, D]
   uint16_t* dk;         // [B, Hkv, Sk, D]
   uint16_t* dv;
   int B, Hq, Hkv, Sq, Sk, causal;
   float scale;
 };
-
-// ---- D_i = sum_d dO_id * O_id (fp32), 16 lanes x 8 dims per row.
-__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
-  const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int c = threadIdx.x & 15;
-  float acc = 0.f;
-  if (row < rows) {
-    const uint4 x = reinterpret_cast<const uint4*>(a.dO + row * kD)[c];
-    const uint4 y = reinterpret_cast<const uint4*>(a.o + row * kD)[c];
-    acc = dot2_bf16(x.x, y.x, acc);
-    acc = dot2_bf16(x.y, y.y, acc);
-    acc = dot2_bf16(x.z, y.z, acc);
-    acc = dot2_bf16(x.w, y.w, acc);
-  }
-  acc = row16_sum(acc);
-  if (row < rows && c == 0) a.delta[row] = acc;
-}
 
 // Direct HBM -> LDS load of a 64-row tile: 16 blocks of 1 KB shared by the
 // W wavefronts; lane l fills LDS unit (l & 15) of row 4j + (l >> 4) with the
@@ -175,21 +159,30 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles, int nbh) {
   // log2 units (+inf for a row without keys, so that P = 0) and D.
   const int qrow = q0 + 32 * wave + col;
   bf16x8_t qreg[8], dreg[8];
+  // D_i = sum_d dO_id O_id (fp32, bf16 pair products) from the dO row in
+  // registers and the O row: half of the dims per half-wavefront, summed
+  // across the halves; written for the dK/dV kernel.
   float lse2 = __builtin_inff(), dl = 0.f;
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
-    uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
+    uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0), z = make_uint4(0, 0, 0, 0);
     if (qrow < Sq) {
       x = *reinterpret_cast<const uint4*>(a.q + (bh * Sq + qrow) * kD + 16 * kk + 8 * hi);
       y = *reinterpret_cast<const uint4*>(a.dO + (bh * Sq + qrow) * kD + 16 * kk + 8 * hi);
+      z = *reinterpret_cast<const uint4*>(a.o + (bh * Sq + qrow) * kD + 16 * kk + 8 * hi);
     }
     qreg[kk] = __builtin_bit_cast(bf16x8_t, x);
     dreg[kk] = __builtin_bit_cast(bf16x8_t, y);
+    dl = dot2_bf16(y.x, z.x, dl);
+    dl = dot2_bf16(y.y, z.y, dl);
+    dl = dot2_bf16(y.z, z.z, dl);
+    dl = dot2_bf16(y.w, z.w, dl);
   }
+  dl = xor32_sum(dl);
   if (qrow < Sq) {
     const float l = a.lse[bh * Sq + qrow];
     lse2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
-    dl = a.delta[bh * Sq + qrow];
+    if (hi == 0) a.delta[bh * Sq + qrow] = dl;
   }
   const float c = a.scale * kLog2e;
 
@@ -450,7 +443,6 @@ hipError_t launch_attention_bwd(const BwdLaunch& l, hipStream_t s) {
   a.scale = l.scale;
   const int64_t rows = (int64_t)l.B * l.Hq * l.Sq;
   if (rows > 0) {
-    hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a);
     const int n_qtiles = (l.Sq + 32 * NW - 1) / (32 * NW);
     const int nbh = l.B * l.Hq;
     hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((int64_t)n_qtiles * nbh)), dim3(64 * NW), 0, s, a, n_qtiles, nbh);
