@@ -122,6 +122,42 @@ def test_num_splits_invariance():
         assert (l - res[0][1]).abs().max().item() <= 1e-4
 
 
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_repeated_runs_and_graph_replays(num_splits):
+    """A run allocates nothing and leaves no state behind in the plan's workspace, so it can be
+    captured in a graph: later runs of the same plan, eager or replays of the captured graph with
+    eager runs between them, give the same bits as the first (which matches the oracle)."""
+    fa = need_gpu()
+    for L, Hq, Hkv in (([700, 0, 129, 4097], 8, 2), ([5000, 17, 640], 4, 2)):
+        say(f"[case] repeated decode runs L={L} Hq={Hq} Hkv={Hkv} num_splits={num_splits}")
+        kv = workloads.paged_inputs(len(L), Hq, Hkv, 128, "bf16", L, 36, nan_tails=True)
+        d = to_dev(kv)
+        plan = fa.fa_decode_plan(kv.seqlens, kv.page_table, kv.num_pages, Hq, Hkv, 128, fa.BF16, num_splits)
+        args = (plan, d["q"], d["k"], d["v"], d["pt"], d["sl"], None, None, SCALE)
+        o0, l0 = fa.decode(*args)
+        torch.cuda.synchronize()
+        O, LSE = oracle_decode(kv, SCALE)
+        check(f"decode first run {L}", f64(o0), O, f64(l0), LSE, "bf16")
+        for _ in range(2):
+            o, l = fa.decode(*args)
+            torch.cuda.synchronize()
+            assert torch.equal(o, o0) and torch.equal(l, l0)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side), torch.cuda.graph(g):
+            og, lg = fa.decode(*args)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            og.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(og, o0) and torch.equal(lg, l0)
+            o, l = fa.decode(*args)
+            torch.cuda.synchronize()
+            assert torch.equal(o, o0) and torch.equal(l, l0)
+
+
 WINDOW_CASES = [
     # (lengths, Hq, Hkv, kv_dtype, num_cus): planned for a small CU count so
     # that the auto plan cuts cost-balanced windows (several items per
