@@ -63,6 +63,26 @@ def test_append_bit_exact(case):
     assert np.array_equal(bits(d["v"]), vp), "V pool differs from the oracle's append"
 
 
+@pytest.mark.parametrize("B", [1024, 1100])
+def test_append_large_batches(B):
+    """Batches of up to 1024 requests have their lengths searched in on-chip memory; larger
+    ones search device memory. Both give the oracle's pools bit for bit (empty requests and
+    requests whose new tokens start mid-page included)."""
+    fa = need_gpu()
+    rng = np.random.default_rng(B)
+    nq = rng.integers(0, 4, B)
+    pre = rng.integers(0, 130, B)
+    say(f"[case] kv_append B={B} T={int(nq.sum())}")
+    r = workloads.ragged_inputs(8, 2, 128, nq, pre, wid=52, extra_pages=3)
+    d = to_dev(r)
+    fa.fa_kv_append(d["kn"], d["vn"], d["k"], d["v"], d["pt"], d["sl"], d["cu"])
+    torch.cuda.synchronize()
+    kp, vp = oracle.kv_append(bits(r.k_pages), bits(r.v_pages), r.page_table.numpy(), r.seqlens.numpy(),
+                              r.cu_seqlens_q.numpy(), bits(r.k_new), bits(r.v_new))
+    assert np.array_equal(bits(d["k"]), kp), "K pool differs from the oracle's append"
+    assert np.array_equal(bits(d["v"]), vp), "V pool differs from the oracle's append"
+
+
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"G{c[2] // c[3]}-B{len(c[0])}")
 def test_ragged_prefill(case):
     fa = need_gpu()
