@@ -39,7 +39,10 @@
 //    the O^T rescale happens only on the first tiles of a row. Two normalisers
 //    are kept: the sum of the bf16-rounded P that the second MFMA consumes
 //    (one v_dot2 with ones per pair) divides O, so the normalisation matches
-//    the weights applied; the fp32 sum of P gives the LSE.
+//    the weights applied; the fp32 sum of P gives the LSE. Dividing by the
+//    fp32 sum alone would save the v_dot2s but leave a row dominated by one
+//    key (whose weight, relative to the lazy max, is rarely a bf16 value)
+//    with an error of up to 2^-9 |v| instead of 2^-9 |v - O|.
 //  * Grid: one workgroup per (query tile, batch, head). With causal masking
 //    the heaviest query tiles (most keys) are issued first. Heads are ordered
 //    so that workgroups with equal id mod 8 -- which the dispatcher places on

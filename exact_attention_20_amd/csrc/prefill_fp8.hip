@@ -210,9 +210,14 @@ void prefill_fp8_kernel(Fp8Args a, int n_qtiles, int nbh) {
         if (t * kBc + 32 * h2 + 8 * (i >> 2) + 4 * hi + (i & 3) > lim) s[h2][i] = kNegInf;
   };
   auto update_max = [&](const f32x16_t (&s)[2]) {
-    float mx = kNegInf;
+    // Max over the lane's 32 scores as a tree of 3-input maxes (v_max3_f32).
+    auto max3 = [](float x, float y, float z) { return fmaxf(fmaxf(x, y), z); };
+    auto sv = [&](int i) { return s[i >> 4][i & 15]; };
+    float t[11];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(s[0][i], s[1][i]));
+    for (int i = 0; i < 10; ++i) t[i] = max3(sv(3 * i), sv(3 * i + 1), sv(3 * i + 2));
+    t[10] = fmaxf(sv(30), sv(31));
+    float mx = fmaxf(max3(max3(t[0], t[1], t[2]), max3(t[3], t[4], t[5]), max3(t[6], t[7], t[8])), fmaxf(t[9], t[10]));
     mx = xor32_max(mx) * c;
     const bool need = mx > m + kTau;
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
