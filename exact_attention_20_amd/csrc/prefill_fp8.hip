@@ -236,9 +236,13 @@ void prefill_fp8_kernel(Fp8Args a, int n_qtiles, int nbh) {
   // P = exp2(s*c - m) -> e4m3 bytes (byte 16*h2 + i), fp32 sums, O^T += V^T P^T;
   // with kb >= 0 the next tile's S^T from K buffer kb is computed in the same
   // straight-line block, one QK product after each PV product.
+  // P bytes of the current tile, kept in one place across tiles: each
+  // conversion below keeps the other half of its register, so giving it the
+  // previous tile's word (overwritten in full by the pair of conversions)
+  // saves a register clear or copy per word.
+  int pw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   auto exp_pv_qk = [&](int vbuf, const f32x16_t (&s)[2], int kb, f32x16_t (&n)[2]) {
     const float mu = m == kNegInf ? 0.f : m;
-    int pw[8];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -246,9 +250,9 @@ void prefill_fp8_kernel(Fp8Args a, int n_qtiles, int nbh) {
         float p[4];
 #pragma unroll
         for (int x = 0; x < 4; ++x) p[x] = fast_exp2(__builtin_fmaf(s[h2][4 * w + x], c, -mu));
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        int& word = pw[4 * h2 + w];
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], word, false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
-        pw[4 * h2 + w] = word;
         le[w] += (p[0] + p[1]) + (p[2] + p[3]);
       }
     const i32x8_t pf = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
