@@ -149,7 +149,8 @@ int fa_prefill_fp8_fwd(const void* q, const void* k, const void* v, const float*
 
 size_t fa_prefill_bwd_workspace_size(int B, int Hq, int Sq) {
   if (B < 1 || Hq < 1 || Sq < 0) return 0;
-  return ((size_t)B * Hq * (size_t)Sq * sizeof(float) + 255) / 256 * 256 + 256;
+  // D_i, then LSE_i in log2 units, one fp32 array each.
+  return 2 * (((size_t)B * Hq * (size_t)Sq * sizeof(float) + 255) / 256 * 256) + 256;
 }
 
 int fa_prefill_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -174,6 +175,7 @@ int fa_prefill_bwd(const void* q, const void* k, const void* v, const void* o, c
   fa::BwdLaunch l;
   l.q = q; l.k = k; l.v = v; l.o = o; l.dO = dout; l.lse = lse;
   l.delta = (float*)workspace;
+  l.lse2 = (float*)((char*)workspace + ((size_t)B * Hq * (size_t)Sq * sizeof(float) + 255) / 256 * 256);
   l.dq = dq; l.dk = dk; l.dv = dv;
   l.B = B; l.Hq = Hq; l.Hkv = Hkv; l.Sq = Sq; l.Sk = Sk; l.causal = causal;
   l.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)D));

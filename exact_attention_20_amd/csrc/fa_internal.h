@@ -52,6 +52,7 @@ struct BwdLaunch {
   const void *q, *k, *v, *o, *dO;
   const float* lse;
   float* delta;   // [B, Hq, Sq] workspace
+  float* lse2;    // [B, Hq, Sq] workspace: LSE in log2 units, +inf for a row without keys
   void *dq, *dk, *dv;
   int B, Hq, Hkv, Sq, Sk, causal;
   float scale;

@@ -25,6 +25,8 @@
 //    reads.
 // S and dP are computed in both kernels (7 products instead of 5) in exchange
 // for no atomic accumulation of dQ.
+#include <type_traits>
+
 #include "bf16_mfma.h"
 #include "fa_internal.h"
 #include "hip_common.h"
@@ -47,6 +49,7 @@ struct BwdArgs {
   const uint16_t* dO;   // [B, Hq, Sq, D]
   const float* lse;     // [B, Hq, Sq] forward LSE (natural log)
   float* delta;         // [B, Hq, Sq] D_i (written by the dQ kernel, read by dK/dV)
+  float* lse2;          // [B, Hq, Sq] LSE * log2 e, +inf for a row without keys (likewise)
   uint16_t* dq;         // [B, Hq, Sq, D]
   uint16_t* dk;         // [B, Hkv, Sk, D]
   uint16_t* dv;
@@ -182,7 +185,10 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles, int nbh) {
   if (qrow < Sq) {
     const float l = a.lse[bh * Sq + qrow];
     lse2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
-    if (hi == 0) a.delta[bh * Sq + qrow] = dl;
+    if (hi == 0) {
+      a.delta[bh * Sq + qrow] = dl;
+      a.lse2[bh * Sq + qrow] = lse2;
+    }
   }
   const float c = a.scale * kLog2e;
 
@@ -207,7 +213,16 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles, int nbh) {
   wait_vmem();
   __syncthreads();
 
-  for (int t = 0; t < n_kt; ++t) {
+  // Key tiles [0, n_full) are seen whole by every row of the workgroup (its
+  // first row has the smallest key limit; rows past Sq have lse2 = +inf and
+  // give 0 either way). They run a loop without the mask: vector-ALU work
+  // does not overlap the matrix cores' on a SIMD, and the per-element key
+  // index, compare and select were 40% of this loop's VALU work. The few
+  // tiles at the diagonal or the Sk tail run the masked copy. Each tile ends
+  // in one barrier, in either loop.
+  const int lim_wg = a.causal ? min(Sk - 1, q0 + off) : Sk - 1;
+  const int n_full = max(0, min(n_kt, (lim_wg + 1) / kBc));
+  auto tile = [&](int t, auto masked) {
     if (t + 1 < n_kt) {
       load_rows(k_rs, (t + 1) * kBc, k_lds + ((t + 1) & 1) * kTile, wave, lane);
       load_rows(v_rs, (t + 1) * kBc, v_lds + ((t + 1) & 1) * kTile, wave, lane);
@@ -227,21 +242,28 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles, int nbh) {
         dp[h2] = kk == 0 ? mfma32_first(va, dreg[kk]) : mfma32(va, dreg[kk], dp[h2]);
       }
     }
-    // P^T = exp2(S^T c - lse2) with the causal / ragged-tail mask, dS^T.
-    const int lim = a.causal ? min(Sk - 1, qrow + off) : Sk - 1;
+    // P^T = exp2(S^T c - lse2) with the causal / ragged-tail mask (masked
+    // tiles only), dS^T.
     bf16x8_t dsf[4];
+    auto ds_tile = [&](auto masked) {
+      const int lim = a.causal ? min(Sk - 1, qrow + off) : Sk - 1;
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+      for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = t * kBc + 32 * h2 + 16 * (i >> 3) + 8 * hi + (i & 7);
-        // Masked entries get a -inf argument (exp2 -> 0): a select, not a branch per element.
-        const float p = fast_exp2(key > lim ? kNegInf : __builtin_fmaf(s[h2][i], c, -lse2));
-        s[h2][i] = p * (dp[h2][i] - dl);
+        for (int i = 0; i < 16; ++i) {
+          float arg = __builtin_fmaf(s[h2][i], c, -lse2);
+          if constexpr (decltype(masked)::value) {
+            const int key = t * kBc + 32 * h2 + 16 * (i >> 3) + 8 * hi + (i & 7);
+            // Masked entries get a -inf argument (exp2 -> 0): a select, not a branch per element.
+            arg = key > lim ? kNegInf : arg;
+          }
+          s[h2][i] = fast_exp2(arg) * (dp[h2][i] - dl);
+        }
+        dsf[2 * h2] = pack8(s[h2], 0);
+        dsf[2 * h2 + 1] = pack8(s[h2], 8);
       }
-      dsf[2 * h2] = pack8(s[h2], 0);
-      dsf[2 * h2 + 1] = pack8(s[h2], 8);
-    }
+    };
+    ds_tile(masked);
     // dQ^T += K^T dS^T (k = keys 16*ks + 8*hi + e).
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
@@ -252,7 +274,9 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles, int nbh) {
       }
     wait_vmem();
     __syncthreads();
-  }
+  };
+  for (int t = 0; t < n_full; ++t) tile(t, std::false_type{});
+  for (int t = n_full; t < n_kt; ++t) tile(t, std::true_type{});
   if (qrow < Sq) store_rows(a.dq + (bh * Sq + qrow) * kD, acc, hi, a.scale);
 }
 
@@ -332,7 +356,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
     load_rows<KW>(ds, qt * kBc, o_lds + buf * kTile, wave, lane);
     if (wave_u == 0) {
       const __amdgpu_buffer_rsrc_t ls = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<float*>(a.lse + bh * (size_t)Sq), (short)0, Sq * 4, 0x00020000);
+          a.lse2 + bh * (size_t)Sq, (short)0, Sq * 4, 0x00020000);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ls, (__attribute__((address_space(3))) void*)(&st_lse[buf][0]), 4,
                                                (qt * kBc + lane) * 4, 0, 0, 0);
     } else if (wave_u == 1) {
@@ -390,13 +414,14 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
         // get a -inf argument (exp2 -> 0), and a row without keys (LSE -inf)
         // a +inf one: selects, where the per-element conditional form
         // compiled to a divergent branch for every element.
+        // The staged LSE is already in log2 units (+inf for a row without
+        // keys), formed once per row by the dQ kernel.
         const int xlo = a.causal ? key - off - (q0 + rb) : 0;
         const int xhi = key < Sk ? Sq - (q0 + rb) : 0;
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           const int i = 8 * h8 + x;
-          const float l2 = lv[x] == kNegInf ? __builtin_inff() : lv[x] * kLog2e;
-          const float p = fast_exp2((x >= xlo) & (x < xhi) ? __builtin_fmaf(s[i], c, -l2) : kNegInf);
+          const float p = fast_exp2((x >= xlo) & (x < xhi) ? __builtin_fmaf(s[i], c, -lv[x]) : kNegInf);
           s[i] = p;
           dp[i] = p * (dp[i] - dvv[x]);
         }
@@ -436,6 +461,7 @@ hipError_t launch_attention_bwd(const BwdLaunch& l, hipStream_t s) {
   a.dO = reinterpret_cast<const uint16_t*>(l.dO);
   a.lse = l.lse;
   a.delta = l.delta;
+  a.lse2 = l.lse2;
   a.dq = reinterpret_cast<uint16_t*>(l.dq);
   a.dk = reinterpret_cast<uint16_t*>(l.dk);
   a.dv = reinterpret_cast<uint16_t*>(l.dv);
