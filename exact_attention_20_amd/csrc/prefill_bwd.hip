@@ -340,30 +340,64 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
   const int qt0 = a.causal ? max(0, (kt * BK - off) / kBc) : 0;
   const int per_head = max(0, n_qt - qt0);
   const int n_steps = per_head * G;
+  // Query tiles [q_lo, q_hi) are seen whole by every key of the workgroup
+  // (no causal cut inside, no row past Sq, no key past Sk); their steps run a
+  // loop without the mask, after the masked steps of the other tiles (the
+  // diagonal band and the Sq tail). Step s < G*n_mask is masked tile
+  // s % n_mask of query head s / n_mask; later steps take the whole tiles
+  // head by head.
+  const int klast = kt * BK + BK - 1;
+  int q_lo = qt0, q_hi = qt0;
+  if (klast < Sk) {
+    const int need = klast - off;  // a whole tile starts at a row >= need
+    const int qf = a.causal ? max(qt0, need <= 0 ? 0 : (need + kBc - 1) / kBc) : qt0;
+    const int qe = Sq / kBc;  // tiles wholly below Sq
+    if (qf < qe) {
+      q_lo = qf;
+      q_hi = qe;
+    }
+  }
+  const int n_full = q_hi - q_lo, n_mask = per_head - n_full;
+  const int n_mask_steps = G * n_mask;
+  auto step_tile = [&](int step, int& jh, int& qt) {
+    if (step < n_mask_steps) {
+      jh = step / n_mask;
+      const int i = step % n_mask;
+      qt = i < q_lo - qt0 ? qt0 + i : q_hi + (i - (q_lo - qt0));
+    } else {
+      jh = (step - n_mask_steps) / n_full;
+      qt = q_lo + (step - n_mask_steps) % n_full;
+    }
+  };
 
   int r_base = row_base(kperm(col), hi);
   int t_base[2];
   tr_bases(lane, t_base);
 
   auto issue = [&](int step, int buf) {
-    const int jh = step / per_head, qt = qt0 + step % per_head;
+    int jh, qt;
+    step_tile(step, jh, qt);
+    // The lane's load offsets are re-formed here on every call: hoisted out
+    // of the step loops by the compiler, they were spilled and reloaded.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
     const size_t bh = (size_t)b * a.Hq + g * G + jh;
     const __amdgpu_buffer_rsrc_t qs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(a.q + bh * (size_t)Sq * kD), (short)0, Sq * kRow, 0x00020000);
     const __amdgpu_buffer_rsrc_t ds = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(a.dO + bh * (size_t)Sq * kD), (short)0, Sq * kRow, 0x00020000);
-    load_rows<KW>(qs, qt * kBc, q_lds + buf * kTile, wave, lane);
-    load_rows<KW>(ds, qt * kBc, o_lds + buf * kTile, wave, lane);
+    load_rows<KW>(qs, qt * kBc, q_lds + buf * kTile, wave_u, ln);
+    load_rows<KW>(ds, qt * kBc, o_lds + buf * kTile, wave_u, ln);
     if (wave_u == 0) {
       const __amdgpu_buffer_rsrc_t ls = __builtin_amdgcn_make_buffer_rsrc(
           a.lse2 + bh * (size_t)Sq, (short)0, Sq * 4, 0x00020000);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ls, (__attribute__((address_space(3))) void*)(&st_lse[buf][0]), 4,
-                                               (qt * kBc + lane) * 4, 0, 0, 0);
+                                               (qt * kBc + ln) * 4, 0, 0, 0);
     } else if (wave_u == 1) {
       const __amdgpu_buffer_rsrc_t dsr = __builtin_amdgcn_make_buffer_rsrc(
           a.delta + bh * (size_t)Sq, (short)0, Sq * 4, 0x00020000);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(dsr, (__attribute__((address_space(3))) void*)(&st_d[buf][0]), 4,
-                                               (qt * kBc + lane) * 4, 0, 0, 0);
+                                               (qt * kBc + ln) * 4, 0, 0, 0);
     }
   };
 
@@ -371,13 +405,15 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
   wait_vmem();
   __syncthreads();
 
-  for (int st = 0; st < n_steps; ++st) {
+  auto step = [&](int st, auto masked) {
     // The per-step offsets base ^ const are cheap to form where they are
     // used; kept from outside the loop they would be spilled.
     asm volatile("" : "+v"(r_base), "+v"(v_base), "+v"(t_base[0]), "+v"(t_base[1]));
     const int buf = st & 1;
     if (st + 1 < n_steps) issue(st + 1, buf ^ 1);
-    const int q0 = (qt0 + st % per_head) * kBc;
+    int jh_unused, qt_cur;
+    step_tile(st, jh_unused, qt_cur);
+    const int q0 = qt_cur * kBc;
     const char* ql = q_lds + buf * kTile;
     const char* ol = o_lds + buf * kTile;
 #pragma unroll
@@ -416,14 +452,24 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
         // compiled to a divergent branch for every element.
         // The staged LSE is already in log2 units (+inf for a row without
         // keys), formed once per row by the dQ kernel.
-        const int xlo = a.causal ? key - off - (q0 + rb) : 0;
-        const int xhi = key < Sk ? Sq - (q0 + rb) : 0;
+        if constexpr (!decltype(masked)::value) {
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const int i = 8 * h8 + x;
-          const float p = fast_exp2((x >= xlo) & (x < xhi) ? __builtin_fmaf(s[i], c, -lv[x]) : kNegInf);
-          s[i] = p;
-          dp[i] = p * (dp[i] - dvv[x]);
+          for (int x = 0; x < 8; ++x) {
+            const int i = 8 * h8 + x;
+            const float p = fast_exp2(__builtin_fmaf(s[i], c, -lv[x]));
+            s[i] = p;
+            dp[i] = p * (dp[i] - dvv[x]);
+          }
+        } else {
+          const int xlo = a.causal ? key - off - (q0 + rb) : 0;
+          const int xhi = key < Sk ? Sq - (q0 + rb) : 0;
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const int i = 8 * h8 + x;
+            const float p = fast_exp2((x >= xlo) & (x < xhi) ? __builtin_fmaf(s[i], c, -lv[x]) : kNegInf);
+            s[i] = p;
+            dp[i] = p * (dp[i] - dvv[x]);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -443,7 +489,9 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
     }
     wait_vmem();
     __syncthreads();
-  }
+  };
+  for (int st = 0; st < n_mask_steps; ++st) step(st, std::true_type{});
+  for (int st = n_mask_steps; st < n_steps; ++st) step(st, std::false_type{});
   if (key < Sk) {
     store_rows(a.dk + (bgk * Sk + key) * kD, dk, hi, a.scale);
     store_rows(a.dv + (bgk * Sk + key) * kD, dv, hi, 1.f);
