@@ -222,6 +222,19 @@ def test_plan_is_deterministic(lib):
     assert np.array_equal(a[0].numpy(), b[0].numpy()) and a[2:] == b[2:]
 
 
+def test_backward_workspace_size(lib):
+    """The backward's first kernel leaves two fp32 values per query row for the second (the
+    row term D and the LSE in log2 units), each array starting on a 256-byte boundary; the
+    size covers both and rejects shapes the entry point rejects."""
+    for B, Hq, Sq in ((1, 1, 1), (4, 32, 4096), (2, 3, 257), (1, 8, 0)):
+        n = lib.fa_prefill_bwd_workspace_size(B, Hq, Sq)
+        one = -(-4 * B * Hq * Sq // 256) * 256
+        assert n >= 2 * one, (B, Hq, Sq, n)
+    assert lib.fa_prefill_bwd_workspace_size(0, 1, 1) == 0
+    assert lib.fa_prefill_bwd_workspace_size(1, 0, 1) == 0
+    assert lib.fa_prefill_bwd_workspace_size(1, 1, -1) == 0
+
+
 def test_workspace_size(lib):
     L = [100, 300, 0]
     n = fa.fa_decode_workspace_size(L, 8, 2, 128, 0, 16)
