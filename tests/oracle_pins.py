@@ -193,6 +193,136 @@ def pin_brute_force():
 
 
 # --------------------------------------------------------------------------
+# Subsets of rows, heads and requests, and the row-block loop. The full-size
+# parity checks and the CPU baseline compute only some rows, heads or
+# requests, so these paths are pinned on their own: against brute force read
+# slot by slot, against the full call, and against a library routine.
+# --------------------------------------------------------------------------
+
+def pin_subset_rows_brute_force():
+    """attention_head(rows=R) on a head with Sq != Sk equals brute force on
+    those rows (R unsorted, both ends, one row twice) and rows R of the full call."""
+    g = _rng(40)
+    Sq, Sk, D = 13, 21, 3
+    q, k, v = g.standard_normal((Sq, D)), g.standard_normal((Sk, D)), g.standard_normal((Sk, D))
+    R = np.array([12, 0, 7, 3, 7, 1])
+    for causal in (False, True):
+        bo, bl = _brute(q.tolist(), k.tolist(), v.tolist(), 0.6, causal)
+        so, sl = A.attention_head(q, k, v, 0.6, causal, rows=R)
+        _close(so, bo[R], 1e-13, f"rows subset vs brute O causal={causal}")
+        _close(sl, bl[R], 1e-13, f"rows subset vs brute LSE causal={causal}")
+        fo, fl = A.attention_head(q, k, v, 0.6, causal)
+        _close(so, fo[R], 1e-13, f"rows subset vs full O causal={causal}")
+        _close(sl, fl[R], 1e-13, f"rows subset vs full LSE causal={causal}")
+
+
+def pin_subset_heads_rows_prefill():
+    """prefill(heads=H, rows=R) equals the full prefill at those (b, h) and
+    rows, for an unsorted head list across batches and GQA groups, unsorted
+    rows, and a row block much smaller than the rows asked for (the block
+    loop runs several times and its last block is ragged); the whole tensor
+    computed in small row blocks equals the one-block result."""
+    g = _rng(41)
+    B, Hq, Hkv, Sq, Sk, D = 2, 6, 2, 45, 60, 4
+    q = g.standard_normal((B, Hq, Sq, D))
+    k = g.standard_normal((B, Hkv, Sk, D))
+    v = g.standard_normal((B, Hkv, Sk, D))
+    H = [(1, 5), (0, 0), (1, 2), (0, 3)]
+    R = g.permutation(Sq)[:31]
+    for causal in (False, True):
+        fo, fl = A.prefill(q, k, v, 0.5, causal)
+        so, sl = A.prefill(q, k, v, 0.5, causal, row_block=7, heads=H, rows=R)
+        assert so.shape == (len(H), len(R), D) and sl.shape == (len(H), len(R))
+        for n, (b, h) in enumerate(H):
+            _close(so[n], fo[b, h][R], 1e-13, f"head subset O {b},{h} causal={causal}")
+            _close(sl[n], fl[b, h][R], 1e-13, f"head subset LSE {b},{h} causal={causal}")
+        bo, bl = A.prefill(q, k, v, 0.5, causal, row_block=4)
+        _close(bo, fo, 1e-13, f"row blocks of 4 O causal={causal}")
+        _close(bl, fl, 1e-13, f"row blocks of 4 LSE causal={causal}")
+    # one subset head against brute force, so the comparison is not only oracle vs oracle
+    b, h = H[0]
+    bo, bl = _brute(q[b, h].tolist(), k[b, h // 3].tolist(), v[b, h // 3].tolist(), 0.5, True)
+    so, sl = A.prefill(q, k, v, 0.5, True, row_block=7, heads=[(b, h)], rows=R)
+    _close(so[0], bo[R], 1e-13, "head subset vs brute O")
+    _close(sl[0], bl[R], 1e-13, "head subset vs brute LSE")
+
+
+def pin_row_blocks_torch_sdpa():
+    """S = 1100 rows, more than the default row block (512) and many times a
+    small one (64): O equals torch's scaled_dot_product_attention and LSE
+    equals torch.logsumexp, in float64, causal and not."""
+    g = _rng(42)
+    B, Hq, Hkv, S, D = 1, 2, 1, 1100, 8
+    q = g.standard_normal((B, Hq, S, D))
+    k = g.standard_normal((B, Hkv, S, D))
+    v = g.standard_normal((B, Hkv, S, D))
+    tq = torch.from_numpy(q)
+    ke = torch.from_numpy(np.repeat(k, Hq // Hkv, axis=1))
+    ve = torch.from_numpy(np.repeat(v, Hq // Hkv, axis=1))
+    for causal in (False, True):
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, ke, ve, is_causal=causal, scale=0.3).numpy()
+        s = 0.3 * tq @ ke.transpose(2, 3)
+        if causal:
+            s = s.masked_fill(~torch.ones(S, S, dtype=torch.bool).tril(), float("-inf"))
+        ref_lse = torch.logsumexp(s, dim=3).numpy()
+        for row_block in (512, 64):
+            O, LSE = A.prefill(q, k, v, 0.3, causal, row_block=row_block)
+            _close(O, ref, 1e-12, f"sdpa S=1100 block {row_block} causal={causal}")
+            _close(LSE, ref_lse, 1e-12, f"logsumexp S=1100 block {row_block} causal={causal}")
+
+
+def pin_subset_requests_decode():
+    """paged_decode(requests=S) for an unsorted subset equals brute force over
+    each request's tokens read slot by slot through the table, and those
+    requests of the full call."""
+    g = _rng(43)
+    B, Hq, Hkv, D = 4, 4, 2, 3
+    L = np.array([70, 1, 129, 64])
+    n = (L + 63) // 64
+    P = int(n.sum()) + 1
+    perm = g.permutation(P)
+    table = np.full((B, 3), -1)
+    off = 0
+    for b in range(B):
+        table[b, :n[b]] = perm[off:off + n[b]]
+        off += n[b]
+    kp, vp = g.standard_normal((P, Hkv, 64, D)), g.standard_normal((P, Hkv, 64, D))
+    q = g.standard_normal((B, Hq, D))
+    S = [2, 0, 3]
+    so, sl = A.paged_decode(q, kp, vp, table, L, 0.55, requests=S)
+    fo, fl = A.paged_decode(q, kp, vp, table, L, 0.55)
+    assert so.shape == (len(S), Hq, D)
+    for i, b in enumerate(S):
+        _close(so[i], fo[b], 1e-13, f"request subset O b={b}")
+        _close(sl[i], fl[b], 1e-13, f"request subset LSE b={b}")
+        for h in range(Hq):
+            gg = h * Hkv // Hq
+            ks = [kp[table[b][t // 64], gg, t % 64].tolist() for t in range(L[b])]
+            vs = [vp[table[b][t // 64], gg, t % 64].tolist() for t in range(L[b])]
+            bo, bl = _brute([q[b, h].tolist()], ks, vs, 0.55, False)
+            _close(so[i, h], bo[0], 1e-13, f"request subset vs brute O b={b} h={h}")
+            _close(sl[i, h], bl[0], 1e-13, f"request subset vs brute LSE b={b} h={h}")
+
+
+def pin_subset_rows_paged_prefill():
+    """paged_prefill_request(rows=R) equals rows R of the hand-indexed brute
+    force and of the full call (R unsorted, first and last new token)."""
+    Hq, Hkv, D = 4, 2, 3
+    nq, pre = [9, 70], [66, 3]
+    q, kn, vn, kp, vp, table, L, cu = _ragged_case(44, Hq, Hkv, D, nq, pre)
+    kp, vp = A.kv_append(kp, vp, table, L, cu, kn, vn)
+    bo, bl = _brute_ragged(q, kp, vp, table, L, cu, 0.65, Hkv)
+    for b, R in ((0, np.array([8, 0, 4])), (1, np.array([69, 2, 0, 63, 64]))):
+        s, e = int(cu[b]), int(cu[b + 1])
+        so, sl = A.paged_prefill_request(q[s:e], kp, vp, table[b], int(L[b]), 0.65, rows=R)
+        fo, fl = A.paged_prefill_request(q[s:e], kp, vp, table[b], int(L[b]), 0.65)
+        _close(so, bo[s:e][R], 1e-13, f"paged rows subset vs brute O b={b}")
+        _close(sl, bl[s:e][R], 1e-13, f"paged rows subset vs brute LSE b={b}")
+        _close(so, fo[R], 1e-13, f"paged rows subset vs full O b={b}")
+        _close(sl, fl[R], 1e-13, f"paged rows subset vs full LSE b={b}")
+
+
+# --------------------------------------------------------------------------
 # Invariants
 # --------------------------------------------------------------------------
 

@@ -13,7 +13,8 @@ from oracle import attention as A
 
 _orig = {n: getattr(A, n) for n in ("scores", "causal_allowed", "softmax_rows", "attention_head",
                                     "kv_head_of", "e4m3fn_to_float", "gather_pages", "lse_merge",
-                                    "kv_append", "paged_prefill_request", "paged_prefill",
+                                    "kv_append", "paged_prefill_request", "paged_prefill", "prefill",
+                                    "paged_decode",
                                     "attention_head_backward", "prefill_backward")}
 
 
@@ -235,6 +236,85 @@ def _bwd_gqa_first_head(q, k, v, do, scale, causal):
     return dq, dk, dv
 
 
+def _head_rows_reindexed(q, k, v, scale, causal=False, rows=None):
+    # the mask built from the positions 0..R-1 of the selected rows, not the rows themselves
+    Sq, Sk = q.shape[0], k.shape[0]
+    rows = np.arange(Sq) if rows is None else np.asarray(rows)
+    s = A.scores(q[rows], k, scale)
+    if causal:
+        s = np.where(A.causal_allowed(np.arange(len(rows)), Sq, Sk), s, -np.inf)
+    P, m, l = A.softmax_rows(s)
+    o = P @ v
+    lse = np.where(np.isfinite(m), m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
+    return o, lse
+
+
+def _prefill_block_positions(q, k, v, scale, causal, kv_head_map=None, row_block=512, heads=None, rows=None):
+    # each row block computes the rows at its positions r0.. instead of the requested rows there
+    B, Hq, Sq, D = q.shape
+    Hkv = k.shape[1]
+    rows = np.arange(Sq) if rows is None else np.asarray(rows)
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
+    O = np.zeros((len(pairs), len(rows), v.shape[3]))
+    LSE = np.zeros((len(pairs), len(rows)))
+    for n, (b, h) in enumerate(pairs):
+        g = A.kv_head_of(h, Hq, Hkv, kv_head_map)
+        for r0 in range(0, len(rows), row_block):
+            rr = np.arange(r0, min(r0 + row_block, len(rows)))
+            O[n, r0:r0 + len(rr)], LSE[n, r0:r0 + len(rr)] = A.attention_head(q[b, h], k[b, g], v[b, g], scale,
+                                                                               causal, rr)
+    if heads is None:
+        O, LSE = O.reshape(B, Hq, len(rows), -1), LSE.reshape(B, Hq, len(rows))
+    return O, LSE
+
+
+def _prefill_heads_sorted(q, k, v, scale, causal, kv_head_map=None, row_block=512, heads=None, rows=None):
+    # the requested (b, h) pairs computed in sorted order instead of the order given
+    return _orig["prefill"](q, k, v, scale, causal, kv_head_map, row_block,
+                            None if heads is None else sorted(heads), rows)
+
+
+def _prefill_last_block_dropped(q, k, v, scale, causal, kv_head_map=None, row_block=512, heads=None, rows=None):
+    # the row-block loop stops one block early when the rows do not fill whole blocks
+    B, Hq, Sq, D = q.shape
+    rows = np.arange(Sq) if rows is None else np.asarray(rows)
+    O, LSE = _orig["prefill"](q, k, v, scale, causal, kv_head_map, row_block, heads, rows)
+    cut = (len(rows) // row_block) * row_block
+    if 0 < cut < len(rows):
+        O[..., cut:, :] = 0.0
+        LSE[..., cut:] = 0.0
+    return O, LSE
+
+
+def _decode_len_by_slot(q, k_pages, v_pages, page_table, seqlens, scale, k_scale=None, v_scale=None,
+                        requests=None):
+    # the n-th requested request read with the length of request n
+    reqs = range(len(seqlens)) if requests is None else list(requests)
+    mixed = np.array(seqlens, copy=True)
+    for n, b in enumerate(reqs):
+        mixed[b] = seqlens[n]
+    return _orig["paged_decode"](q, k_pages, v_pages, page_table, mixed, scale, k_scale, v_scale, requests)
+
+
+def _ragged_rows_before_mask(q_b, k_pages, v_pages, table_row, L, scale, rows=None):
+    # the rows selected from q first, then masked as if they were new tokens 0..R-1
+    q_b = np.asarray(q_b, dtype=np.float64)
+    rows = np.arange(q_b.shape[0]) if rows is None else np.asarray(rows)
+    n = q_b.shape[0]
+    sub = q_b[rows]
+    Hq, Hkv = q_b.shape[1], k_pages.shape[1]
+    O, LSE = np.zeros((len(rows), Hq, v_pages.shape[3])), np.zeros((len(rows), Hq))
+    for h in range(Hq):
+        g = A.kv_head_of(h, Hq, Hkv)
+        kb = A.gather_pages(k_pages, table_row, L, g)
+        vb = A.gather_pages(v_pages, table_row, L, g)
+        s = A.scores(sub[:, h], kb, scale)
+        s = np.where(np.arange(L)[None, :] <= (L - n + np.arange(len(rows)))[:, None], s, -np.inf)
+        P, m, l = A.softmax_rows(s)
+        O[:, h], LSE[:, h] = P @ vb, m + np.log(l)
+    return O, LSE
+
+
 MUTANTS = {
     "scores_no_scale": ("scores", _scores_no_scale),
     "scores_sqrt_scale": ("scores", _scores_sqrt_scale),
@@ -266,6 +346,12 @@ MUTANTS = {
     "bwd_no_scale": ("attention_head_backward", _bwd_variant("no_scale")),
     "bwd_dk_from_p": ("attention_head_backward", _bwd_variant("dk_from_p")),
     "bwd_gqa_first_head": ("prefill_backward", _bwd_gqa_first_head),
+    "head_rows_reindexed": ("attention_head", _head_rows_reindexed),
+    "prefill_block_positions": ("prefill", _prefill_block_positions),
+    "prefill_heads_sorted": ("prefill", _prefill_heads_sorted),
+    "prefill_last_block_dropped": ("prefill", _prefill_last_block_dropped),
+    "decode_len_by_slot": ("paged_decode", _decode_len_by_slot),
+    "ragged_rows_before_mask": ("paged_prefill_request", _ragged_rows_before_mask),
 }
 
 
