@@ -45,7 +45,9 @@ class FAError(RuntimeError):
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, "libfa.so")
+    """The in-tree libfa.so; FA_LIBRARY names another build of the same ABI
+    (the CPU tests use it for a sanitizer build of the host code)."""
+    return os.environ.get("FA_LIBRARY") or os.path.join(_HERE, "libfa.so")
 
 
 def load():

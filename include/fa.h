@@ -424,10 +424,15 @@ int fa_decode_plan_cascade_host(const int32_t* seqlens_host, int B, int max_page
 
 /*
  * fa_debug_gather_kv -- copy the L_b logical tokens of one request and KV
- * head out of a paged pool, through the same page-table indexing the decode
- * kernel uses, into dst [L_b, D] (same element type as the pool). For the
- * bit-exact gather test. max_pages_per_req and num_pages as for the plan;
- * ids outside [0, num_pages) leave their tokens' dst rows untouched.
+ * head out of a paged pool into dst [L_b, D] (same element type as the
+ * pool): logical token t is slot t mod 64 of physical page
+ * page_table[b][t / 64] ("Flash Attention & Paged Attention" blog,
+ * "2. PagedAttention": a logical-to-physical table over fixed-size pages;
+ * "FlashAttention breakthrough architecture", paged storage: 64-token
+ * blocks). A small kernel of its own, for the bit-exact test of the page
+ * layout; the attention kernels do their own lookups. max_pages_per_req and
+ * num_pages as for the plan; ids outside [0, num_pages) leave their tokens'
+ * dst rows untouched.
  */
 int fa_debug_gather_kv(const void* pages, int kv_dtype, const int32_t* page_table,
                        int max_pages_per_req, int num_pages, int Hkv, int D, int b, int L_b,

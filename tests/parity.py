@@ -42,7 +42,8 @@ def metrics(o_gpu, o_ref, lse_gpu, lse_ref):
     d = np.abs(o_gpu - o_ref)
     rms = float(np.sqrt(np.sum((o_gpu - o_ref) ** 2)) / max(np.sqrt(np.sum(o_ref ** 2)), 1e-300))
     both_ninf = np.isneginf(lse_gpu) & np.isneginf(lse_ref)
-    dl = np.where(both_ninf, 0.0, np.abs(lse_gpu - lse_ref))
+    with np.errstate(invalid="ignore"):  # -inf - -inf on rows with no key; masked just below
+        dl = np.where(both_ninf, 0.0, np.abs(lse_gpu - lse_ref))
     return dict(max_abs=float(d.max(initial=0.0)) if np.all(np.isfinite(d)) else float("inf"),
                 rel_rms=rms if np.isfinite(rms) else float("inf"),
                 lse_abs=float(dl.max(initial=0.0)) if np.all(np.isfinite(dl)) else float("inf"))
