@@ -5,30 +5,37 @@
                     [--decode-workload 4|5]
 
 One step = one pass of the whole path over one synthetic batch:
-  * prefill: fa_prefill_fwd on the causal bf16 workload (default: B=4, 32 heads,
-    4096 tokens, head dim 128), and
+  * prefill: fa_prefill_fwd on the long-context causal GQA bf16 workload
+    (B=1, 32 query heads over 8 KV heads, 32768 tokens, head dim 128): the
+    headline ``value``, ``roofline`` and ``cpu_baseline``; and
   * decode: fa_decode_run (split-KV kernel + LSE merge) on the paged bf16
-    workload (default: 64 requests, 32/8 heads, lengths U[512, 16384]),
-    planned once beforehand (the host plan is timed separately and reported).
-A third leg, reported as its own ``ragged_prefill`` object and not part of
-the step, measures the ragged paged prefill: fa_kv_append of 16 requests'
-new tokens (256..2048 each) into their paged caches, then fa_prefill_paged_run
-of those tokens over prefix + new keys (prefixes 0..16384), each timed on
-its own. A fourth, the ``shared_prefix_decode`` object, times the cascade
-decode of 64 requests sharing an 8192-token prefix (suffixes 256..4096)
-against plain split-KV decode of the same batch. A fifth, ``fp8_prefill``,
-times the fp8 (e4m3) causal prefill of the 4 x 32-head x 4096 shape, and a
-sixth, ``backward``, the gradients (dQ, dK, dV) of the bf16 prefill workload.
-Inputs are resident in HBM
-before timing. Each leg first runs untimed for
+    workload (64 requests, 32/8 heads, lengths U[512, 16384]), planned once
+    beforehand (the host plan is timed separately and reported).
+Two more legs of the same two steps are timed on their own, each with its
+own roofline and CPU baseline, and are not part of ``ms_per_step``: the
+causal bf16 prefill of B=4 x 32 heads x 4096 tokens, and the long ragged
+decode with fp8 (e4m3fn) KV (8 requests, log-uniform lengths in
+[4096, 131072]; four copies of its pools rotate so that the 256 MB
+last-level cache cannot serve it). ``prefill`` and ``decode`` hold one object
+per workload, keyed by workload name.
+A further leg, reported as its own ``ragged_prefill`` object, measures the
+ragged paged prefill: fa_kv_append of 16 requests' new tokens (256..2048
+each) into their paged caches, then fa_prefill_paged_run of those tokens over
+prefix + new keys (prefixes 0..16384), each timed on its own. The
+``shared_prefix_decode`` object times the cascade decode of 64 requests
+sharing an 8192-token prefix (suffixes 256..4096) against plain split-KV
+decode of the same batch; ``fp8_prefill`` times the fp8 (e4m3) causal prefill
+of the 4 x 32-head x 4096 shape, and ``backward`` the gradients (dQ, dK, dV)
+of that bf16 shape.
+Inputs are resident in HBM before timing. Each leg first runs untimed for
 --prewarm-s seconds (default 1 s: GPU clocks and power reach steady state)
 and --warmup more times; each timed call is then bracketed by HIP events on
-the stream it runs on, and the step time is the sum of the legs' means.
+the stream it runs on.
 
-Prints ONE JSON line. ``value`` is the prefill throughput in TFLOP/s
-(algorithmic FLOPs 4*B*H*D*S(S+1)/2 over the measured time); the ``decode``
-object carries the decode HBM throughput (algorithmic bytes over the measured
-time). ``roofline`` is for the dominant kernel (the MFMA prefill), and
+Prints ONE JSON line. ``value`` is the headline prefill throughput in
+TFLOP/s (algorithmic FLOPs 4*B*H*D*S(S+1)/2 over the measured time); decode
+legs carry HBM throughput (algorithmic bytes over the measured time).
+``roofline`` is for the dominant kernel (the MFMA prefill), and
 ``cpu_baseline`` times the fp64 oracle on a bounded sample on the host cores.
 """
 from __future__ import annotations
@@ -171,33 +178,58 @@ def time_calls(fn, steps, warmup, stream, prewarm_s=0.0):
 
 
 def cpu_baseline_prefill(w, q, k, v, budget_s=15.0):
-    """fp64 oracle on whole heads of the prefill workload, threads over heads."""
+    """fp64 oracle on the prefill workload, threads over jobs. Whole heads
+    when S <= 8192; for longer sequences, seeded 64-row blocks of random heads
+    (the first and last block of a head, the blocks on either side of a
+    256-row tile boundary, and random blocks), each with all its causal keys."""
     import concurrent.futures as cf
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
     cores = max(1, min(len(os.sched_getaffinity(0)), 16))
-    qn = q.double().numpy()
-    kn = k.double().numpy()
-    vn = v.double().numpy()
+    G = w.Hq // w.Hkv
     heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    whole = w.S <= 8192
+    if whole:
+        jobs = [(b, h, None) for b, h in heads]
+    else:
+        g = np.random.default_rng(0)
+        nblk = w.S // 64
+        jobs = []
+        for i in g.permutation(len(heads)):
+            b, h = heads[i]
+            bd = 4 * int(g.integers(1, nblk // 4))
+            jobs += [(b, h, 0), (b, h, nblk - 1), (b, h, bd - 1), (b, h, bd), (b, h, int(g.integers(0, nblk)))]
 
-    def one(bh):
-        oracle.prefill(qn, kn, vn, w.scale, True, heads=[bh])
+    def one(job):
+        b, h, blk = job
+        gg = h // G
+        qh = q[b:b + 1, h:h + 1].float().numpy()
+        kh = k[b:b + 1, gg:gg + 1].float().numpy()
+        vh = v[b:b + 1, gg:gg + 1].float().numpy()
+        rows = None if blk is None else np.arange(64 * blk, 64 * blk + 64)
+        oracle.prefill(qh, kh, vh, w.scale, True, rows=rows)
+        r = np.arange(w.S) if rows is None else rows
+        return 4.0 * w.D * float(np.sum(r + 1))
 
-    done = 0
+    done, flops = 0, 0.0
     t0 = time.perf_counter()
     with threadpool_limits(limits=1), cf.ThreadPoolExecutor(cores) as ex:
-        while done < len(heads) and time.perf_counter() - t0 < budget_s:
-            batch = heads[done:done + cores]
-            list(ex.map(one, batch))
+        while done < len(jobs) and time.perf_counter() - t0 < budget_s:
+            batch = jobs[done:done + cores]
+            flops += sum(ex.map(one, batch))
             done += len(batch)
     dt = time.perf_counter() - t0
-    flops = 4.0 * w.D * (w.S * (w.S + 1) // 2) * done
+    if whole:
+        sample = f"{done} of {len(jobs)} whole heads (all {w.S} causal rows)"
+    else:
+        sample = (f"{done} 64-row blocks (of {w.S // 64} per head; first, last, either side of a 256-row "
+                  f"tile boundary and random, seeded) across {len(set((b, h) for b, h, _ in jobs[:done]))} "
+                  f"of {len(heads)} heads, each row with all its causal keys")
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} of {len(heads)} whole heads (all {w.S} causal rows) of the prefill workload, "
-                      f"{dt:.1f} s wall, fp64 numpy, BLAS 1 thread per worker"}
+            "sample": f"{sample} of the prefill workload {w.name}, {dt:.1f} s wall, fp64 numpy, "
+                      f"BLAS 1 thread per worker"}
 
 
 def cpu_baseline_decode(w, kv, budget_s=10.0):
@@ -516,7 +548,7 @@ def summarize_profiles(d):
             # pass (and the merge after it) belongs to the cascade, the others
             # to the plain-decode comparison.
             disp = sorted(csv.DictReader(open(tr[0])), key=lambda r: int(r["Start_Timestamp"]))
-            leg, prev, per = "prefill", "", {}
+            leg, prev, per, dsub = "prefill", "", {}, "decode"
             for r in disp:
                 m = re.search(r"::(\w+(?:<[^>]*>)?)\(", r["Kernel_Name"])
                 k = m.group(1) if m else r["Kernel_Name"][:60]
@@ -537,6 +569,14 @@ def summarize_profiles(d):
                     elif k.startswith("lse_merge"):
                         sub = leg
                 dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                if leg == "prefill" and k == "prefill_bf16_kernel<8, 1, 0>":
+                    # two prefill workloads share the kernel: the 32K-token GQA launch
+                    # runs ~8 ms, the 4 x 4096-token one well under 2 ms
+                    sub = "prefill (B1 Hq32/Hkv8 S32768)" if dur > 2000.0 else "prefill (B4 H32 S4096)"
+                if leg == "decode" and k.startswith(("decode_", "lse_merge")):
+                    if k.startswith("decode_"):
+                        dsub = "decode (fp8 KV, 8 long requests)" if ", true," in k else "decode (bf16 KV, 64 requests)"
+                    sub = dsub
                 per.setdefault((sub, k), []).append(dur)
                 prev = k
             lines.append("# per leg (dispatches attributed by order): leg | kernel | calls | average us")
@@ -548,9 +588,10 @@ def summarize_profiles(d):
             if txt:
                 b = json.loads(txt[-1])
                 lines.append("# the same run's bench line, HIP-event means per launch:")
-                lines.append(f"bench prefill launch_ms_mean: {b['roofline'].get('launch_ms_mean')}")
-                if "decode" in b:
-                    lines.append(f"bench decode step ms_mean: {b['decode'].get('ms_mean')}")
+                for name, o in b.get("prefill", {}).items():
+                    lines.append(f"bench prefill {name} launch ms_mean: {o.get('ms_mean')}")
+                for name, o in b.get("decode", {}).items():
+                    lines.append(f"bench decode {name} step ms_mean: {o.get('ms_mean')}")
                 if "shared_prefix_decode" in b:
                     lines.append(f"bench shared-prefix decode step ms_mean: {b['shared_prefix_decode'].get('ms_mean')}")
                 if "backward" in b:
@@ -580,8 +621,10 @@ def main():
     ap.add_argument("--no-plain-compare", action="store_true",
                     help="shared-prefix leg: skip timing plain decode of the same batch")
     ap.add_argument("--only", choices=["prefill", "decode", "ragged", "cascade", "fp8", "bwd", "copy"], default=None)
-    ap.add_argument("--prefill-workload", type=int, default=2, choices=[2, 3])
-    ap.add_argument("--decode-workload", type=int, default=4, choices=[4, 5])
+    ap.add_argument("--prefill-workload", type=int, default=None, choices=[2, 3],
+                    help="time only this prefill workload (default: 3, the headline, then 2)")
+    ap.add_argument("--decode-workload", type=int, default=None, choices=[4, 5],
+                    help="time only this decode workload (default: 4, in the step, then 5)")
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
                     help="write profiles/*.txt from rocprofv3 output under DIR (no GPU needed)")
     ap.add_argument("--print-profile-commands", metavar="DIR", default=None)
@@ -613,58 +656,65 @@ def main():
         copy_calibration(args.steps, args.warmup)
         return
 
-    res = {}
-    wp = workloads.WORKLOADS[args.prefill_workload]
-    wd = workloads.WORKLOADS[args.decode_workload]
+    res = {"prefill": [], "decode": []}
+    pws = [args.prefill_workload] if args.prefill_workload else [3, 2]
+    dws = [args.decode_workload] if args.decode_workload else [4, 5]
 
     if args.only in (None, "prefill"):
-        log(f"[bench] generating prefill workload {wp.name}")
-        q, k, v = workloads.workload_prefill_inputs(wp)
-        qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
-        out = torch.empty_like(qd)
-        lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=qd.device)
-        pf = lambda: fa.fa_prefill_fwd(qd, kd, vd, out, lse, True, wp.scale, None, stream)  # noqa: E731
-        t = time_calls(pf, args.steps, args.warmup, stream, args.prewarm_s)
-        res["prefill_ms"] = t
-        log(f"[bench] prefill median {statistics.median(t):.4f} ms min {min(t):.4f} ms")
-        res["prefill_cpu"] = None if args.no_cpu_baseline else cpu_baseline_prefill(wp, q, k, v)
-        del qd, kd, vd, out, lse
+        for wid in pws:
+            wp = workloads.WORKLOADS[wid]
+            log(f"[bench] generating prefill workload {wp.name}")
+            q, k, v = workloads.workload_prefill_inputs(wp)
+            qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+            out = torch.empty_like(qd)
+            lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=qd.device)
+            pf = lambda: fa.fa_prefill_fwd(qd, kd, vd, out, lse, True, wp.scale, None, stream)  # noqa: E731
+            t = time_calls(pf, args.steps, args.warmup, stream, args.prewarm_s)
+            log(f"[bench] prefill {wp.name} median {statistics.median(t):.4f} ms min {min(t):.4f} ms")
+            del qd, kd, vd, out, lse
+            cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(wp, q, k, v)
+            res["prefill"].append(dict(w=wp, t=t, cpu=cpu))
+            del q, k, v
 
     if args.only in (None, "decode"):
-        log(f"[bench] generating decode workload {wd.name}")
-        kv = workloads.workload_paged_inputs(wd, nan_tails=True)
-        dt = fa.BF16 if wd.kv_dtype == "bf16" else fa.FP8_E4M3FN
-        d = dict(q=kv.q.cuda(), k=kv.k_pages.cuda(), v=kv.v_pages.cuda(), pt=kv.page_table.cuda(),
-                 sl=kv.seqlens.cuda(), ks=None if kv.k_scale is None else kv.k_scale.cuda(),
-                 vs=None if kv.v_scale is None else kv.v_scale.cuda())
-        t0 = time.perf_counter()
-        plan = fa.fa_decode_plan(kv.seqlens, kv.page_table, kv.num_pages, wd.Hq, wd.Hkv, wd.D, dt, 0)
-        plan_ms = (time.perf_counter() - t0) * 1e3
-        items, _, chunk = plan.items()
-        out = torch.empty_like(d["q"])
-        lse = torch.empty(d["q"].shape[:2], dtype=torch.float32, device=d["q"].device)
-        # Rotate copies of the KV pools when they would fit in the 256 MB
-        # last-level cache, so every step reads from HBM.
-        pool_bytes = d["k"].numel() * d["k"].element_size() * 2
-        n_copies = 1 if pool_bytes > 1024 ** 3 else 4
-        pools = [(d["k"], d["v"])] + [(d["k"].clone(), d["v"].clone()) for _ in range(n_copies - 1)]
-        it = [0]
+        for wid in dws:
+            wd = workloads.WORKLOADS[wid]
+            log(f"[bench] generating decode workload {wd.name}")
+            kv = workloads.workload_paged_inputs(wd, nan_tails=True)
+            dt = fa.BF16 if wd.kv_dtype == "bf16" else fa.FP8_E4M3FN
+            d = dict(q=kv.q.cuda(), k=kv.k_pages.cuda(), v=kv.v_pages.cuda(), pt=kv.page_table.cuda(),
+                     sl=kv.seqlens.cuda(), ks=None if kv.k_scale is None else kv.k_scale.cuda(),
+                     vs=None if kv.v_scale is None else kv.v_scale.cuda())
+            t0 = time.perf_counter()
+            plan = fa.fa_decode_plan(kv.seqlens, kv.page_table, kv.num_pages, wd.Hq, wd.Hkv, wd.D, dt, 0)
+            plan_ms = (time.perf_counter() - t0) * 1e3
+            items, _, chunk = plan.items()
+            out = torch.empty_like(d["q"])
+            lse = torch.empty(d["q"].shape[:2], dtype=torch.float32, device=d["q"].device)
+            # Rotate copies of the KV pools when they would fit in the 256 MB
+            # last-level cache, so every step reads from HBM.
+            pool_bytes = d["k"].numel() * d["k"].element_size() * 2
+            n_copies = 1 if pool_bytes > 1024 ** 3 else 4
+            pools = [(d["k"], d["v"])] + [(d["k"].clone(), d["v"].clone()) for _ in range(n_copies - 1)]
+            it = [0]
 
-        def dec():
-            kk, vv = pools[it[0] % n_copies]
-            it[0] += 1
-            fa.fa_decode_run(plan, d["q"], kk, vv, d["pt"], d["sl"], plan.num_splits, out, lse,
-                             d["ks"], d["vs"], wd.scale, stream)
+            def dec():
+                kk, vv = pools[it[0] % n_copies]
+                it[0] += 1
+                fa.fa_decode_run(plan, d["q"], kk, vv, d["pt"], d["sl"], plan.num_splits, out, lse,
+                                 d["ks"], d["vs"], wd.scale, stream)
 
-        t = time_calls(dec, args.steps, args.warmup, stream, args.prewarm_s)
-        res["decode_ms"] = t
-        res["decode_bytes"] = decode_bytes(kv.seqlens.numpy(), wd)
-        res["decode_plan"] = dict(plan_ms=round(plan_ms, 3), items=int(len(items)), chunk_pages=chunk,
-                                  num_splits=plan.num_splits, pages=int(kv.num_pages),
-                                  pool_copies_rotated=n_copies)
-        log(f"[bench] decode median {statistics.median(t):.4f} ms min {min(t):.4f} ms plan {plan_ms:.2f} ms")
-        res["decode_cpu"] = None if args.no_cpu_baseline else cpu_baseline_decode(wd, kv)
-        del d, pools
+            t = time_calls(dec, args.steps, args.warmup, stream, args.prewarm_s)
+            log(f"[bench] decode {wd.name} median {statistics.median(t):.4f} ms min {min(t):.4f} ms "
+                f"plan {plan_ms:.2f} ms")
+            del d, pools, out, lse
+            cpu = None if args.no_cpu_baseline else cpu_baseline_decode(wd, kv)
+            res["decode"].append(dict(w=wd, t=t, bytes=decode_bytes(kv.seqlens.numpy(), wd), cpu=cpu,
+                                      total_tokens=int(kv.seqlens.sum()),
+                                      plan=dict(plan_ms=round(plan_ms, 3), items=int(len(items)),
+                                                chunk_pages=chunk, num_splits=plan.num_splits,
+                                                pages=int(kv.num_pages), pool_copies_rotated=n_copies)))
+            del kv
 
     if args.only in (None, "ragged"):
         wr = workloads.WORKLOADS[6]
@@ -736,7 +786,7 @@ def main():
         del d
 
     if args.only in (None, "bwd"):
-        wb = workloads.WORKLOADS[args.prefill_workload]
+        wb = workloads.WORKLOADS[2]
         log(f"[bench] generating backward inputs for {wb.name}")
         q, k, v, do = workloads.backward_inputs(wb.B, wb.Hq, wb.Hkv, wb.S, wb.S, wb.D, wb.wid)
         qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
@@ -754,37 +804,56 @@ def main():
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic"}
     ms_step = 0.0
-    if "prefill_ms" in res:
-        t_pf = statistics.mean(res["prefill_ms"])
-        ms_step += t_pf
+    pre_objs, dec_objs = {}, {}
+    for i, g in enumerate(res["prefill"]):
+        wp = g["w"]
+        t_pf = statistics.mean(g["t"])
         flops = prefill_flops(wp)
         tflops = flops / (t_pf * 1e-3) / 1e12
-        line.update(value=round(tflops, 2), unit="TFLOP/s")
-        line["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                            "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                            "traffic": read_traffic(f"prefill_bf16_wl{wp.wid}_traffic.txt",
-                                                    "exact_attention_20_amd/csrc/prefill_bf16.hip"),
-                            "kernel": "prefill_bf16_kernel",
-                            "launch_ms_mean": round(t_pf, 5), "launch_ms_median": round(statistics.median(res["prefill_ms"]), 5),
-                            "flops_per_launch": flops}
-        line["cpu_baseline"] = res["prefill_cpu"]
-    if "decode_ms" in res:
-        t_dc = statistics.mean(res["decode_ms"])
-        ms_step += t_dc
-        gbs = res["decode_bytes"] / (t_dc * 1e-3) / 1e9
-        dec = {"metric": "paged decode HBM GB/s (split-KV + LSE merge)", "value": round(gbs, 1),
-               "unit": "GB/s", "ms_mean": round(t_dc, 5), "ms_median": round(statistics.median(res["decode_ms"]), 5),
-               "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                            "frac": round(gbs / PEAK_HBM_GBS, 4),
-                            "traffic": read_traffic(f"decode_wl{wd.wid}_traffic.txt", DECODE_SRC),
-                            "kernel": "decode_mfma_kernel + lse_merge_kernel",
-                            "bytes_per_launch": res["decode_bytes"]},
-               "plan": res["decode_plan"], "cpu_baseline": res["decode_cpu"]}
-        line["decode"] = dec
-        if "value" not in line:
-            line.update(value=dec["value"], unit="GB/s")
-            line["roofline"] = dec["roofline"]
-            line["cpu_baseline"] = dec["cpu_baseline"]
+        pre_objs[wp.name] = {
+            "metric": "causal bf16 prefill TFLOP/s", "value": round(tflops, 2), "unit": "TFLOP/s",
+            "ms_mean": round(t_pf, 5), "ms_median": round(statistics.median(g["t"]), 5),
+            "in_step": i == 0,
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                         "traffic": read_traffic(f"prefill_bf16_wl{wp.wid}_traffic.txt",
+                                                 "exact_attention_20_amd/csrc/prefill_bf16.hip"),
+                         "kernel": "prefill_bf16_kernel", "launch_ms_mean": round(t_pf, 5),
+                         "launch_ms_median": round(statistics.median(g["t"]), 5), "flops_per_launch": flops,
+                         "algorithmic_bytes_per_launch": prefill_bytes(wp)},
+            "cpu_baseline": g["cpu"],
+            "config": {"workload": wp.name, "B": wp.B, "Hq": wp.Hq, "Hkv": wp.Hkv, "S": wp.S, "D": wp.D,
+                       "causal": True, "dtype": "bf16"}}
+        if i == 0:
+            ms_step += t_pf
+            line.update(value=round(tflops, 2), unit="TFLOP/s")
+            line["roofline"] = pre_objs[wp.name]["roofline"]
+            line["cpu_baseline"] = g["cpu"]
+    for i, g in enumerate(res["decode"]):
+        wd = g["w"]
+        t_dc = statistics.mean(g["t"])
+        gbs = g["bytes"] / (t_dc * 1e-3) / 1e9
+        dec_objs[wd.name] = {
+            "metric": "paged decode HBM GB/s (split-KV + LSE merge)", "value": round(gbs, 1), "unit": "GB/s",
+            "ms_mean": round(t_dc, 5), "ms_median": round(statistics.median(g["t"]), 5), "in_step": i == 0,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": read_traffic(f"decode_wl{wd.wid}_traffic.txt", DECODE_SRC),
+                         "kernel": "decode_mfma_kernel + lse_merge_kernel", "bytes_per_launch": g["bytes"]},
+            "plan": g["plan"], "cpu_baseline": g["cpu"],
+            "config": {"workload": wd.name, "B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "D": wd.D,
+                       "kv_dtype": wd.kv_dtype, "page": 64, "lengths": list(wd.lengths),
+                       "total_tokens": g["total_tokens"]}}
+        if i == 0:
+            ms_step += t_dc
+            if "value" not in line:
+                line.update(value=round(gbs, 1), unit="GB/s")
+                line["roofline"] = dec_objs[wd.name]["roofline"]
+                line["cpu_baseline"] = g["cpu"]
+    if pre_objs:
+        line["prefill"] = pre_objs
+    if dec_objs:
+        line["decode"] = dec_objs
     if "ragged" in res:
         g = res["ragged"]
         wr = g["w"]
@@ -885,17 +954,22 @@ def main():
             line["cpu_baseline"] = bwo["cpu_baseline"]
             ms_step = tb
     line["ms_per_step"] = round(ms_step, 5)
-    cfg = {"workload": " + ".join(
-        ([wp.name] if "prefill_ms" in res else []) + ([wd.name] if "decode_ms" in res else [])
-        + ([res["ragged"]["w"].name] if "ragged" in res and "prefill_ms" not in res
-           and "decode_ms" not in res else [])
-        + ([res["cascade"]["w"].name] if "cascade" in res and "prefill_ms" not in res
-           and "decode_ms" not in res and "ragged" not in res else []))}
-    if "prefill_ms" in res:
+    step_names = ([res["prefill"][0]["w"].name] if res["prefill"] else []) + \
+                 ([res["decode"][0]["w"].name] if res["decode"] else [])
+    if not step_names:
+        for key in ("ragged", "cascade", "fp8", "bwd"):
+            if key in res:
+                step_names = [res[key]["w"].name + (" (backward)" if key == "bwd" else "")]
+                break
+    cfg = {"workload": " + ".join(step_names)}
+    if res["prefill"]:
+        wp = res["prefill"][0]["w"]
         cfg["prefill"] = dict(B=wp.B, Hq=wp.Hq, Hkv=wp.Hkv, S=wp.S, D=wp.D, causal=True, dtype="bf16")
-    if "decode_ms" in res:
+    if res["decode"]:
+        g = res["decode"][0]
+        wd = g["w"]
         cfg["decode"] = dict(B=wd.B, Hq=wd.Hq, Hkv=wd.Hkv, D=wd.D, kv_dtype=wd.kv_dtype, page=64,
-                             lengths=list(wd.lengths), total_tokens=int(kv.seqlens.sum()))
+                             lengths=list(wd.lengths), total_tokens=g["total_tokens"])
     line["config"] = cfg
     print(json.dumps(line), flush=True)
 

@@ -129,3 +129,11 @@ def test_full_workload_sampled(wid):
     og = np.stack([f64(out[b, h, rows]) for b, h in heads])
     lg = np.stack([f64(lse[b, h, rows]) for b, h in heads])
     check(f"workload {wid} sampled {len(heads)} heads x {len(rows)} rows", og, O, lg, L, "bf16")
+    # every (b, h): first and last row, and both sides of the 256-row tile boundaries at the
+    # start, middle and end (the XCD-ordered head enumeration covers all B * Hq heads)
+    few = np.array(sorted({0, 255, 256, w.S // 2 - 1, w.S // 2, w.S - 257, w.S - 256, w.S - 1}))
+    every = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    O2, L2 = oracle.prefill(qn, kn, vn, w.scale, True, heads=every, rows=few)
+    og2 = f64(out[:, :, few]).reshape(len(every), len(few), -1)
+    lg2 = f64(lse[:, :, few]).reshape(len(every), len(few))
+    check(f"workload {wid} all {len(every)} heads x {len(few)} rows", og2, O2, lg2, L2, "bf16")
