@@ -28,6 +28,7 @@ __all__ = [
     "fa_prefill_paged_plan_host", "fa_prefill_paged_workspace_size", "prefill_paged",
     "fa_decode_plan_cascade", "fa_decode_plan_cascade_host", "fa_decode_cascade_workspace_size",
     "fa_prefill_fp8_fwd", "prefill_fp8", "fa_prefill_bwd", "fa_prefill_bwd_workspace_size", "prefill_bwd",
+    "fa_prefill_bwd_noalloc",
 ]
 
 F32, BF16, FP8_E4M3FN = 0, 1, 2
@@ -98,6 +99,8 @@ def load():
     lib.fa_prefill_bwd_workspace_size.restype = csz
     lib.fa_prefill_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, vp, csz, vp]
     lib.fa_prefill_bwd.restype = ci
+    lib.fa_prefill_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, vp]
+    lib.fa_prefill_bwd_noalloc.restype = ci
     lib.fa_prefill_fp8_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, vp]
     lib.fa_prefill_fp8_fwd.restype = ci
     lib.fa_decode_cascade_workspace_size.argtypes = [i32p, ci, ci, ci, ci, ci, i32p, i32p, ci, ci]
@@ -538,6 +541,24 @@ def fa_prefill_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal=True, scale=0.0, wo
     _check(lib.fa_prefill_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                               _ptr(dv), B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), float(scale or 0.0),
                               _ptr(workspace), workspace.numel(), _stream(stream)))
+    return dq, dk, dv
+
+
+def fa_prefill_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, causal=True, scale=0.0, stream=None):
+    """fa_prefill_bwd with the library's static device scratch in place of a workspace
+    (for callers that cannot allocate); same outputs, written into dq, dk, dv."""
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, n, torch.bfloat16)
+    _need(lse, "lse", torch.float32)
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    if k.shape != (B, Hkv, Sk, D) or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape \
+            or dq.shape != q.shape or dk.shape != k.shape or dv.shape != k.shape or lse.shape != (B, Hq, Sq):
+        raise FAError(1, "inconsistent shapes")
+    _check(lib.fa_prefill_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                      _ptr(dk), _ptr(dv), B, Hq, Hkv, Sq, Sk, D, int(bool(causal)),
+                                      float(scale or 0.0), _stream(stream)))
     return dq, dk, dv
 
 

@@ -153,25 +153,28 @@ size_t fa_prefill_bwd_workspace_size(int B, int Hq, int Sq) {
   return 2 * (((size_t)B * Hq * (size_t)Sq * sizeof(float) + 255) / 256 * 256) + 256;
 }
 
-int fa_prefill_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                   const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk,
-                   int D, int causal, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+// Argument checks shared by the two backward entry points; FA_OK when a launch is needed.
+static int check_bwd(const char* who, const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv,
+                     int Sq, int Sk, int D, int causal, float scale) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 0 || Sk < 0)
-    return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_bwd: need B,Hq,Hkv >= 1 and Sq,Sk >= 0");
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: need B,Hq,Hkv >= 1 and Sq,Sk >= 0", who);
   if (Hq > fa::kMaxHeads || Hkv > fa::kMaxHeads)
-    return fail(FA_ERR_UNSUPPORTED, "fa_prefill_bwd: Hq and Hkv must be <= %d", fa::kMaxHeads);
-  if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_bwd: Hq %% Hkv != 0 (%d, %d)", Hq, Hkv);
-  if (D != 128) return fail(FA_ERR_UNSUPPORTED, "fa_prefill_bwd: D=%d not supported (128)", D);
-  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_bwd: causal must be 0 or 1");
-  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_bwd: scale is not finite");
+    return fail(FA_ERR_UNSUPPORTED, "%s: Hq and Hkv must be <= %d", who, fa::kMaxHeads);
+  if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARGUMENT, "%s: Hq %% Hkv != 0 (%d, %d)", who, Hq, Hkv);
+  if (D != 128) return fail(FA_ERR_UNSUPPORTED, "%s: D=%d not supported (128)", who, D);
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "%s: causal must be 0 or 1", who);
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARGUMENT, "%s: scale is not finite", who);
   if ((long long)std::max(Sq, Sk) * 256 > 0x7fffffffLL)
-    return fail(FA_ERR_UNSUPPORTED, "fa_prefill_bwd: Sq and Sk must be below 2^23");
-  if (Sq == 0 && Sk == 0) return ok();
+    return fail(FA_ERR_UNSUPPORTED, "%s: Sq and Sk must be below 2^23", who);
   if ((Sq > 0 && (!q || !o || !lse || !dout || !dq)) || (Sk > 0 && (!k || !v || !dk || !dv)))
-    return fail(FA_ERR_INVALID_ARGUMENT, "fa_prefill_bwd: null tensor pointer");
-  const size_t need = fa_prefill_bwd_workspace_size(B, Hq, Sq);
-  if (!workspace || workspace_bytes < need)
-    return fail(FA_ERR_WORKSPACE, "fa_prefill_bwd: workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s: null tensor pointer", who);
+  return FA_OK;
+}
+
+static int launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk,
+                      int D, int causal, float scale, void* workspace, const char* who, void* stream) {
   fa::BwdLaunch l;
   l.q = q; l.k = k; l.v = v; l.o = o; l.dO = dout; l.lse = lse;
   l.delta = (float*)workspace;
@@ -180,8 +183,41 @@ int fa_prefill_bwd(const void* q, const void* k, const void* v, const void* o, c
   l.B = B; l.Hq = Hq; l.Hkv = Hkv; l.Sq = Sq; l.Sk = Sk; l.causal = causal;
   l.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)D));
   hipError_t e = fa::launch_attention_bwd(l, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "fa_prefill_bwd launch");
+  if (e != hipSuccess) return hip_fail(e, who);
   return ok();
+}
+
+int fa_prefill_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk,
+                   int D, int causal, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_bwd("fa_prefill_bwd", q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Sq, Sk, D, causal, scale);
+  if (st != FA_OK) return st;
+  if (Sq == 0 && Sk == 0) return ok();
+  const size_t need = fa_prefill_bwd_workspace_size(B, Hq, Sq);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "fa_prefill_bwd: workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  return launch_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Sq, Sk, D, causal, scale, workspace,
+                    "fa_prefill_bwd launch", stream);
+}
+
+int fa_prefill_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                           const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
+                           int Sk, int D, int causal, float scale, void* stream) {
+  int st = check_bwd("fa_prefill_bwd_noalloc", q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Sq, Sk, D, causal,
+                     scale);
+  if (st != FA_OK) return st;
+  if (Sq == 0 && Sk == 0) return ok();
+  const size_t need = fa_prefill_bwd_workspace_size(B, Hq, Sq);
+  if (need > fa::kBwdScratchBytes)
+    return fail(FA_ERR_WORKSPACE,
+                "fa_prefill_bwd_noalloc: needs %zu bytes of scratch, more than the static %zu "
+                "(B*Hq*Sq <= %zu rows); use fa_prefill_bwd with a workspace",
+                need, fa::kBwdScratchBytes, (fa::kBwdScratchBytes - 768) / 8);
+  void* ws = nullptr;
+  hipError_t e = fa::bwd_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e, "fa_prefill_bwd_noalloc: scratch address");
+  return launch_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Sq, Sk, D, causal, scale, ws,
+                    "fa_prefill_bwd_noalloc launch", stream);
 }
 
 static int check_decode_shape(int B, int Hq, int Hkv, int D) {

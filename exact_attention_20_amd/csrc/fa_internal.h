@@ -59,6 +59,12 @@ struct BwdLaunch {
 };
 hipError_t launch_attention_bwd(const BwdLaunch& l, hipStream_t s);
 
+// Static device scratch that stands in for the backward's workspace in the
+// entry point for callers that cannot allocate: its size, and its address
+// on the current device (looked up once per device).
+constexpr size_t kBwdScratchBytes = size_t(32) << 20;
+hipError_t bwd_scratch(void** ptr);
+
 // Query rows per work item of the bf16 prefill kernel (ragged plan unit).
 constexpr int kPrefillRows = 256;
 hipError_t launch_prefill_paged_bf16(const PrefillArgs& a, int n_items, hipStream_t s);

@@ -25,6 +25,7 @@
 //    reads.
 // S and dP are computed in both kernels (7 products instead of 5) in exchange
 // for no atomic accumulation of dQ.
+#include <mutex>
 #include <type_traits>
 
 #include "bf16_mfma.h"
@@ -499,6 +500,40 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
 }
 
 }  // namespace
+
+// Per-row arrays of the backward (D_i, then LSE_i in log2 units) for the entry
+// point that allocates nothing. Each GPU the library runs on holds its own
+// copy until the process ends; every call on that GPU shares it, so calls
+// that overlap on one GPU race. The dQ kernel writes every row < Sq before
+// the dK/dV kernel reads any, and reads past Sq return zeros through the
+// buffer bounds, so nothing in it needs clearing between calls.
+static __device__ __align__(256) char scratch[kBwdScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxScratchDevices] = {};
+}  // namespace
+
+// Device address of `scratch` on the current device. In host code the array's
+// name is only a host-side handle, so the address is asked of the runtime once
+// per device, with that device current, and kept.
+hipError_t bwd_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255) != 0) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = p;
+  }
+  *ptr = g_scratch_addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_attention_bwd(const BwdLaunch& l, hipStream_t s) {
   BwdArgs a;

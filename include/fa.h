@@ -149,6 +149,26 @@ int fa_prefill_bwd(const void* q, const void* k, const void* v, const void* o, c
                    size_t workspace_bytes, void* stream);
 
 /*
+ * fa_prefill_bwd_noalloc -- fa_prefill_bwd without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving or training loops, harnesses that forbid hipMalloc). The two
+ * per-row arrays the workspace would hold live in a static device array of
+ * 32 MiB (one per GPU, held until the process ends), so
+ * fa_prefill_bwd_workspace_size(B, Hq, Sq) must not exceed 32 MiB:
+ * B * Hq * Sq up to about 4.19M rows. Larger calls return FA_ERR_WORKSPACE
+ * and launch nothing. Arguments, results and errors are otherwise those of
+ * fa_prefill_bwd, and the same kernels run. This call allocates nothing: no
+ * hipMalloc, no hipFree, no library allocation. Every call on a GPU shares
+ * that GPU's array; calls that overlap on one GPU (two streams, two threads)
+ * race and must be serialised by the caller. The array's address is looked
+ * up on the first call on each device (FA_ERR_HIP if that fails).
+ */
+int fa_prefill_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                           int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale,
+                           void* stream);
+
+/*
  * Paged Flash-Decoding: plan once per batch composition, then run.
  * ("FIA / FlashAttention" Q&A, section 2: plan preprocesses ragged lengths
  * and balances load, run executes the batch; "Flash Attention & Paged

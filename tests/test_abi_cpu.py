@@ -235,6 +235,23 @@ def test_backward_workspace_size(lib):
     assert lib.fa_prefill_bwd_workspace_size(1, 1, -1) == 0
 
 
+def test_backward_noalloc_rejects_before_the_device(lib):
+    """The static-scratch backward checks its arguments and its 32 MiB limit on the host:
+    bad shapes and calls whose per-row arrays would not fit return an error and launch
+    nothing (no device is touched, so this runs on the CPU)."""
+    p = C.c_void_p(256)
+    args = lambda B, Hq, Hkv, Sq, Sk, D=128: (p, p, p, p, p, p, p, p, p, B, Hq, Hkv, Sq, Sk, D, 1, 0.0, None)  # noqa: E731
+    assert lib.fa_prefill_bwd_noalloc(*args(0, 1, 1, 8, 8)) == 1
+    assert lib.fa_prefill_bwd_noalloc(*args(1, 6, 4, 8, 8)) == 1
+    assert lib.fa_prefill_bwd_noalloc(*args(1, 2, 2, 8, 8, D=64)) == 2
+    assert lib.fa_prefill_bwd_noalloc(*args(1, 1, 1, 0, 0)) == 0      # nothing to do
+    # 32 heads x 131072 rows = 4.19M rows need 2 x 16 MiB + 256 B: just over the limit
+    assert lib.fa_prefill_bwd_noalloc(*args(1, 32, 8, 131072, 16)) == 3
+    assert b"static" in lib.fa_last_error()
+    assert lib.fa_prefill_bwd_workspace_size(1, 32, 131072) > 32 << 20
+    assert lib.fa_prefill_bwd_workspace_size(1, 32, 131064) <= 32 << 20
+
+
 def test_workspace_size(lib):
     L = [100, 300, 0]
     n = fa.fa_decode_workspace_size(L, 8, 2, 128, 0, 16)
