@@ -82,8 +82,14 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   constexpr int KBUF = kBc * kRow;            // bytes per K buffer
   constexpr int VBUF = kBc * kRow;            // bytes per V buffer
   constexpr int BLK = (kBc * kRow / 1024) / NW;  // 1 KB direct-load blocks per wave per tile
-  __shared__ __attribute__((aligned(16))) char k_lds[2 * KBUF];
-  __shared__ __attribute__((aligned(16))) char v_lds[2 * VBUF];
+  // Two K and two V tile buffers, each its own LDS variable: the compiler
+  // then tags every access with the variable it touches, and a tile's reads
+  // of one buffer need not wait for the loads still filling another (see
+  // lds_step).
+  __shared__ __attribute__((aligned(16))) char k_lds0[KBUF];
+  __shared__ __attribute__((aligned(16))) char k_lds1[KBUF];
+  __shared__ __attribute__((aligned(16))) char v_lds0[VBUF];
+  __shared__ __attribute__((aligned(16))) char v_lds1[VBUF];
 
   constexpr bool PAGED = MODE != kContig;
   const int tid = threadIdx.x;
@@ -250,20 +256,23 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
           rs, (__attribute__((address_space(3))) void*)(buf + j * 1024), 16, (k0 + r) * kRow + unit * 16, 0, 0, 0);
     }
   };
-  auto load_k = [&](int t) {
+  // Key tile t lives in K buffer t & 1, value tile t in V buffer t & 1.
+  auto kbuf = [&](int t) { return (t & 1) ? k_lds1 : k_lds0; };
+  auto vbuf = [&](int t) { return (t & 1) ? v_lds1 : v_lds0; };
+  auto load_k = [&](int t, char* dst) {
     if constexpr (PAGED)
-      load_tile(page_rsrc(a.k, t), 0, k_lds + (t & 1) * KBUF, false);
+      load_tile(page_rsrc(a.k, t), 0, dst, false);
     else
-      load_tile(k_rs, t * kBc, k_lds + (t & 1) * KBUF, false);
+      load_tile(k_rs, t * kBc, dst, false);
   };
-  auto load_v = [&](int t) {
+  auto load_v = [&](int t, char* dst) {
     if constexpr (PAGED)
-      load_tile(page_rsrc(a.v, t), 0, v_lds + (t & 1) * VBUF, true);
+      load_tile(page_rsrc(a.v, t), 0, dst, true);
     else
-      load_tile(v_rs, t * kBc, v_lds + (t & 1) * VBUF, true);
+      load_tile(v_rs, t * kBc, dst, true);
   };
-  // This wavefront's direct loads have landed in LDS (the compiler does not
-  // track them, so the wait is explicit; the following barrier publishes them).
+  // This wavefront's direct loads have landed in LDS (waited for explicitly
+  // before the barrier that publishes them).
   auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   // Per-lane LDS read addresses.
@@ -295,8 +304,7 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   auto any_active = [&](int t) { return blk_active(t, QB - 1); };
 
   // S^T for every query block from K buffer kbuf.
-  auto qk = [&](int kbuf, f32x16_t (&s)[QB][2]) {
-    const char* kl = k_lds + kbuf * KBUF;
+  auto qk = [&](const char* kl, f32x16_t (&s)[QB][2]) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(kl + k_off[kk]);
@@ -357,13 +365,11 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   // scores of the next tile are computed from K buffer kb in the same
   // straight-line block, so the scheduler can interleave those MFMAs with
   // this tile's exponentials.
-  auto exp_pv_qk = [&](int vbuf, const f32x16_t (&s)[QB][2], const bool (&use)[QB], int kb,
-                       f32x16_t (&n)[QB][2]) {
+  auto exp_pv_qk = [&](const char* vl, const f32x16_t (&s)[QB][2], const bool (&use)[QB], const char* kl,
+                       bool next_qk, f32x16_t (&n)[QB][2]) {
     float mu[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mu[qb] = (m[qb] == kNegInf) ? 0.f : m[qb];
-    const char* vl = v_lds + vbuf * VBUF;
-    const char* kl = k_lds + (kb < 0 ? 0 : kb) * KBUF;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       bf16x8_t pf[QB];
@@ -393,7 +399,7 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
         for (int qb = 0; qb < QB; ++qb)
           if (use[qb]) o[qb][db] = mfma32(va, pf[qb], o[qb][db]);
       }
-      if (kb >= 0) {
+      if (next_qk) {
 #pragma unroll
         for (int kk = 2 * ks; kk < 2 * ks + 2; ++kk) {
           const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(kl + k_off[kk]);
@@ -409,11 +415,18 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
     }
   };
 
-  // Start the loads of K(t+2) over K(t) and of V(t+1) over V(t-1): both
-  // buffers were last read in iteration t-1, before its closing barrier.
-  auto prefetch = [&](int t) {
-    if (t + 2 < n_kt) load_k(t + 2);
-    if (t + 1 < n_kt) load_v(t + 1);
+  // One tile's LDS traffic: start the loads of K(t+2) over K(t) and of
+  // V(t+1) over V(t-1) (both buffers were last read in iteration t-1, before
+  // its closing barrier), then run `body` on the buffers this tile reads,
+  // V(t) and K(t+1). The four buffers are distinct (separate LDS variables,
+  // and restrict here): when the compiler cannot tell that the loads just
+  // started write other addresses than a read, it makes the tile's first
+  // transposing LDS read wait for them, which exposes their whole latency.
+  auto lds_step = [&](int t, const char* __restrict__ vl, const char* __restrict__ kl, char* __restrict__ kw,
+                      char* __restrict__ vw, auto&& body) {
+    if (t + 2 < n_kt) load_k(t + 2, kw);
+    if (t + 1 < n_kt) load_v(t + 1, vw);
+    body(vl, kl);
   };
 
   // Tiles below the whole workgroup's diagonal and inside Sk need no mask
@@ -425,13 +438,13 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   // ---- prologue: K(0), K(1), V(0) in LDS, then S(0).
   f32x16_t sc[QB][2];
   if (n_kt > 0) {
-    load_k(0);
-    load_v(0);
-    if (n_kt > 1) load_k(1);
+    load_k(0, kbuf(0));
+    load_v(0, vbuf(0));
+    if (n_kt > 1) load_k(1, kbuf(1));
   }
   wait_loads();
   __syncthreads();  // K(0), K(1), V(0) visible to every wavefront
-  if (n_kt > 0 && any_active(0)) qk(0, sc);
+  if (n_kt > 0 && any_active(0)) qk(kbuf(0), sc);
   __syncthreads();  // every wavefront has read K(0) before K(2) replaces it
 
   bool all[QB];
@@ -444,10 +457,12 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   // to keep this block free of branches.
   auto main_step = [&](auto par, int t, f32x16_t (&cur)[QB][2], f32x16_t (&nxt)[QB][2]) {
     constexpr int PAR = decltype(par)::value;
-    prefetch(t);
+    lds_step(t, PAR ? v_lds1 : v_lds0, PAR ? k_lds0 : k_lds1, PAR ? k_lds1 : k_lds0, PAR ? v_lds0 : v_lds1,
+             [&](const char* vl, const char* kl) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) update_max(qb, cur[qb][0], cur[qb][1]);
-    exp_pv_qk(PAR, cur, all, 1 - PAR, nxt);
+               for (int qb = 0; qb < QB; ++qb) update_max(qb, cur[qb][0], cur[qb][1]);
+               exp_pv_qk(vl, cur, all, kl, true, nxt);
+             });
     wait_loads();
     __syncthreads();
   };
@@ -472,23 +487,24 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   }
   for (; t < n_kt; ++t) {
     f32x16_t sn[QB][2];
-    prefetch(t);
     const bool next = t + 1 < n_kt && any_active(t + 1);
-    bool use[QB];
-    bool any = false;
+    lds_step(t, vbuf(t), kbuf(t + 1), kbuf(t), vbuf(t + 1), [&](const char* vl, const char* kl) {
+      bool use[QB];
+      bool any = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      use[qb] = blk_active(t, qb);
-      any |= use[qb];
-      if (use[qb]) {
-        mask(t, qb, sc[qb][0], sc[qb][1]);
-        update_max(qb, sc[qb][0], sc[qb][1]);
+      for (int qb = 0; qb < QB; ++qb) {
+        use[qb] = blk_active(t, qb);
+        any |= use[qb];
+        if (use[qb]) {
+          mask(t, qb, sc[qb][0], sc[qb][1]);
+          update_max(qb, sc[qb][0], sc[qb][1]);
+        }
       }
-    }
-    if (any)
-      exp_pv_qk(t & 1, sc, use, next ? (t + 1) & 1 : -1, sn);
-    else if (next)
-      qk((t + 1) & 1, sn);
+      if (any)
+        exp_pv_qk(vl, sc, use, kl, next, sn);
+      else if (next)
+        qk(kl, sn);
+    });
     if (next) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -545,7 +561,7 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
     // stored in 16-byte unit 4*db + gq (XOR-swizzled by row & 15, which
     // keeps both the writes and the row reads free of bank conflicts). A
     // wavefront's LDS operations complete in order, so no barrier is needed.
-    char* st = (wave < 4 ? k_lds : v_lds) + (wave & 3) * (32 * kRow);
+    char* st = (wave < 2 ? k_lds0 : wave < 4 ? k_lds1 : wave < 6 ? v_lds0 : v_lds1) + (wave & 1) * (32 * kRow);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
