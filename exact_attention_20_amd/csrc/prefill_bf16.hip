@@ -61,6 +61,7 @@ constexpr int kD = 128;        // head dim
 constexpr int kBc = 64;        // keys per tile
 constexpr int kRow = kD * 2;   // K/V row in LDS: 256 B, unpadded, 16-byte units XOR-swizzled
 constexpr float kTau = 8.0f;   // lazy max threshold (log2 units)
+constexpr float kSumBound = 256.0f;  // 2^kTau: a tile sum at or below it bounds every weight
 
 // Modes of the kernel:
 //  kContig  contiguous [B, H, S, D] tensors, one work unit per (query tile, b, h);
@@ -74,7 +75,16 @@ constexpr float kTau = 8.0f;   // lazy max threshold (log2 units)
 //           group's prefix pages, no mask; results go to partial slots.
 constexpr int kContig = 0, kRagged = 1, kPrefix = 2;
 
-template <int NW, int QB, int MODE>
+#ifndef FA_PREFILL_PINGPONG
+#define FA_PREFILL_PINGPONG 1
+#endif
+constexpr bool kPingPong = FA_PREFILL_PINGPONG != 0;
+#ifndef FA_PREFILL_KV_DEPTH
+#define FA_PREFILL_KV_DEPTH 3
+#endif
+constexpr int kKvDepth = FA_PREFILL_KV_DEPTH;  // K and V tile buffers each (ping-pong schedule)
+
+template <int NW, int QB, int MODE, bool PP>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   constexpr int NT = 64 * NW;                 // threads
@@ -90,6 +100,12 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   __shared__ __attribute__((aligned(16))) char k_lds1[KBUF];
   __shared__ __attribute__((aligned(16))) char v_lds0[VBUF];
   __shared__ __attribute__((aligned(16))) char v_lds1[VBUF];
+  // Two more of each for the ping-pong schedule's deeper prefetch (unused,
+  // and so not allocated, by the other schedule).
+  __shared__ __attribute__((aligned(16))) char k_lds2[KBUF];
+  __shared__ __attribute__((aligned(16))) char k_lds3[KBUF];
+  __shared__ __attribute__((aligned(16))) char v_lds2[VBUF];
+  __shared__ __attribute__((aligned(16))) char v_lds3[VBUF];
 
   constexpr bool PAGED = MODE != kContig;
   const int tid = threadIdx.x;
@@ -435,85 +451,342 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   if (causal) n_main = min(n_main, max(0, (q0 + off + 1) / kBc));
   n_main = min(n_main, n_kt);
 
-  // ---- prologue: K(0), K(1), V(0) in LDS, then S(0).
-  f32x16_t sc[QB][2];
-  if (n_kt > 0) {
-    load_k(0, kbuf(0));
-    load_v(0, vbuf(0));
-    if (n_kt > 1) load_k(1, kbuf(1));
-  }
-  wait_loads();
-  __syncthreads();  // K(0), K(1), V(0) visible to every wavefront
-  if (n_kt > 0 && any_active(0)) qk(kbuf(0), sc);
-  __syncthreads();  // every wavefront has read K(0) before K(2) replaces it
+  if constexpr (PP) {
+    static_assert(QB == 1 && NW == 8, "the ping-pong schedule pairs two 32-row wavefronts per SIMD");
+    // ---- Ping-pong schedule. Waves 0-3 (group A) and 4-7 (group B) put one
+    // wavefront of each group on every SIMD. A wavefront alternates a matrix
+    // phase M(j) -- O^T += V^T P^T of tile j-1, then S^T = K Q^T of tile j --
+    // with a vector phase V(j): mask, running max and P = exp2(S c - m) of
+    // tile j in bf16 with both normalisers. The two groups run one phase
+    // apart with a barrier between phases: in slot 2j group A runs M(j) while
+    // B runs V(j-1), in slot 2j+1 A runs V(j) while B runs M(j). So on every
+    // SIMD one wavefront issues matrix instructions while the other runs the
+    // softmax; the matrix core then executes one wavefront's MFMAs while the
+    // other's vector instructions issue, which one wavefront's dependent
+    // chain (scores -> max -> exponentials -> P V) cannot do on its own.
+    // Loads of K(j+1) and V(j) start in slot 2j (their buffers were last
+    // read in slots 2j-2 and 2j-1) and are waited for at the end of slot
+    // 2j+1, one slot before their first reader.
+    const bool grp_a = __builtin_amdgcn_readfirstlane(wave) < 4;
+    f32x16_t s0, s1;    // S^T of a tile between its M and V phases (keys 0-31, 32-63)
+    uint32_t pw[4][4];  // P^T of a tile between its V phase and the next M phase: [k step][pair]
 
-  bool all[QB];
+    auto m_phase = [&](int j, const char* vl, const char* kl) __attribute__((always_inline)) {
+      const bool pv = j >= 1 && blk_active(j - 1, 0);
+      const bool sq = j < n_kt && blk_active(j, 0);
+      auto pv_step = [&](int ks) __attribute__((always_inline)) {
+        const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(pw[ks][0], pw[ks][1], pw[ks][2], pw[ks][3]));
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) all[qb] = true;
-  // One tile of the main loop with buffer parity PAR known at compile time
-  // (LDS offsets become immediates); the scores of tile t arrive in `cur`
-  // and those of tile t+1 leave in `nxt`. The next tile's scores are
-  // computed even past the last tile (from a stale buffer, then discarded)
-  // to keep this block free of branches.
-  auto main_step = [&](auto par, int t, f32x16_t (&cur)[QB][2], f32x16_t (&nxt)[QB][2]) {
-    constexpr int PAR = decltype(par)::value;
-    lds_step(t, PAR ? v_lds1 : v_lds0, PAR ? k_lds0 : k_lds1, PAR ? k_lds1 : k_lds0, PAR ? v_lds0 : v_lds1,
-             [&](const char* vl, const char* kl) {
+        for (int db = 0; db < 4; ++db) {
+          const char* vp = vl + v_off[db] + 16 * ks * kRow;
+          const uint2 v0 = lds_read_tr16(vp);
+          const uint2 v1 = lds_read_tr16(vp + 4 * kRow);
+          const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
+          o[0][db] = mfma32(va, pf, o[0][db]);
+        }
+      };
+      auto qk_step = [&](int kk) __attribute__((always_inline)) {
+        const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(kl + k_off[kk]);
+        const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(kl + k_off[kk] + 32 * kRow);
+        const bf16x8_t qf = qreg[0][kk];
+        s0 = kk == 0 ? mfma32_first(a0, qf) : mfma32(a0, qf, s0);
+        s1 = kk == 0 ? mfma32_first(a1, qf) : mfma32(a1, qf, s1);
+      };
+      if (pv && sq) {
+        // Eight blocks of four MFMAs: block b is k step b of S^T (two
+        // 32-key halves) and two of the four 32-dim blocks of O^T for k step
+        // b/2 of P V. Each block's LDS operands are read one block ahead
+        // (their latency hides behind the previous block's MFMAs), and the
+        // scheduling barriers keep that order, so that no more than two
+        // blocks' operands are live at once.
+        struct Ops {
+          bf16x8_t k0, k1, v0, v1;
+        };
+        auto read_ops = [&](int b) __attribute__((always_inline)) {
+          Ops r;
+          r.k0 = *reinterpret_cast<const bf16x8_t*>(kl + k_off[b]);
+          r.k1 = *reinterpret_cast<const bf16x8_t*>(kl + k_off[b] + 32 * kRow);
+          const int ks = b >> 1, db = 2 * (b & 1);
+          const char* vp0 = vl + v_off[db] + 16 * ks * kRow;
+          const char* vp1 = vl + v_off[db + 1] + 16 * ks * kRow;
+          const uint2 a0 = lds_read_tr16(vp0), a1 = lds_read_tr16(vp0 + 4 * kRow);
+          const uint2 b0 = lds_read_tr16(vp1), b1 = lds_read_tr16(vp1 + 4 * kRow);
+          r.v0 = __builtin_bit_cast(bf16x8_t, make_uint4(a0.x, a0.y, a1.x, a1.y));
+          r.v1 = __builtin_bit_cast(bf16x8_t, make_uint4(b0.x, b0.y, b1.x, b1.y));
+          return r;
+        };
+        Ops cur = read_ops(0);
 #pragma unroll
-               for (int qb = 0; qb < QB; ++qb) update_max(qb, cur[qb][0], cur[qb][1]);
-               exp_pv_qk(vl, cur, all, kl, true, nxt);
-             });
-    wait_loads();
-    __syncthreads();
-  };
-  // Unrolled by two so the two score arrays swap roles instead of being
-  // copied, and t starts at 0, so tile t uses buffer t & 1 = its position.
-  int t = 0;
-  {
-    f32x16_t sn[QB][2];
-    for (; t + 1 < n_main; t += 2) {
-      main_step(std::integral_constant<int, 0>{}, t, sc, sn);
-      main_step(std::integral_constant<int, 1>{}, t + 1, sn, sc);
-    }
-    if (t < n_main) {
-      main_step(std::integral_constant<int, 0>{}, t, sc, sn);
+        for (int b = 0; b < 8; ++b) {
+          Ops nxt;
+          if (b < 7) nxt = read_ops(b + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          const bf16x8_t qf = qreg[0][b];
+          s0 = b == 0 ? mfma32_first(cur.k0, qf) : mfma32(cur.k0, qf, s0);
+          s1 = b == 0 ? mfma32_first(cur.k1, qf) : mfma32(cur.k1, qf, s1);
+          const int ks = b >> 1, db = 2 * (b & 1);
+          const bf16x8_t pf =
+              __builtin_bit_cast(bf16x8_t, make_uint4(pw[ks][0], pw[ks][1], pw[ks][2], pw[ks][3]));
+          o[0][db] = mfma32(cur.v0, pf, o[0][db]);
+          o[0][db + 1] = mfma32(cur.v1, pf, o[0][db + 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (b < 7) cur = nxt;
+        }
+      } else if (pv) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        sc[qb][0] = sn[qb][0];
-        sc[qb][1] = sn[qb][1];
+        for (int ks = 0; ks < 4; ++ks) pv_step(ks);
+      } else if (sq) {
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) qk_step(kk);
       }
-      ++t;
-    }
-  }
-  for (; t < n_kt; ++t) {
-    f32x16_t sn[QB][2];
-    const bool next = t + 1 < n_kt && any_active(t + 1);
-    lds_step(t, vbuf(t), kbuf(t + 1), kbuf(t), vbuf(t + 1), [&](const char* vl, const char* kl) {
-      bool use[QB];
-      bool any = false;
+    };
+
+    // P of the tile with the running max as it stands, and the tile's shares
+    // of both normalisers (tr: sum of bf16(p), te: fp32 sum of p).
+    auto exps = [&](float (&tr)[4], float (&te)[4]) __attribute__((always_inline)) {
+      const float mu = m[0] == kNegInf ? 0.f : m[0];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        use[qb] = blk_active(t, qb);
-        any |= use[qb];
-        if (use[qb]) {
-          mask(t, qb, sc[qb][0], sc[qb][1]);
-          update_max(qb, sc[qb][0], sc[qb][1]);
+      for (int jj = 0; jj < 4; ++jj) tr[jj] = te[jj] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const f32x16_t& sv = (ks >> 1) ? s1 : s0;
+        const int base = 8 * (ks & 1);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float p0 = fast_exp2(__builtin_fmaf(sv[base + 2 * jj], c, -mu));
+          const float p1 = fast_exp2(__builtin_fmaf(sv[base + 2 * jj + 1], c, -mu));
+          pw[ks][jj] = pack_bf16x2(p0, p1);
+          tr[jj] = dot2_bf16(pw[ks][jj], 0x3f803f80u, tr[jj]);  // + bf16(p0) + bf16(p1)
+          te[jj] += p0 + p1;
         }
       }
-      if (any)
-        exp_pv_qk(vl, sc, use, kl, next, sn);
-      else if (next)
-        qk(kl, sn);
-    });
-    if (next) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        sc[qb][0] = sn[qb][0];
-        sc[qb][1] = sn[qb][1];
+    };
+    // The running max is lazy: it only has to keep every weight p = exp2(s c - m)
+    // at or below 2^kTau. The tile's weights are first formed with the max as it
+    // stands; a lane's fp32 tile sum bounds each of its weights, so if no lane's
+    // sum exceeds 2^kTau the tile is kept without ever forming its row max. Else
+    // (the first tile of a row, or scores that rose past the max by about kTau)
+    // the tile is redone the long way: row max, lazy move of the max with the
+    // rescale of O and the normalisers, weights again. This takes the max tree,
+    // its cross-lane exchange and the wave-wide vote off the common path, where
+    // they stood between the scores and the first exponential.
+    auto v_phase = [&](int j) __attribute__((always_inline)) {
+      if (j < 0 || j >= n_kt || !blk_active(j, 0)) return;
+      if (j >= n_main) mask(j, 0, s0, s1);
+      float tr[4], te[4];
+      bool redo = true;
+      if (__builtin_amdgcn_ballot_w64(m[0] == kNegInf) == 0) {
+        exps(tr, te);
+        const float big = fmaxf(fmaxf(te[0], te[1]), fmaxf(te[2], te[3]));
+        redo = __builtin_amdgcn_ballot_w64(!(big <= kSumBound)) != 0;
       }
+      if (__builtin_expect(redo, 0)) {
+        update_max(0, s0, s1);
+        exps(tr, te);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        lr[0][jj] += tr[jj];
+        le[0][jj] += te[jj];
+      }
+    };
+
+    // Barrier between the two slots of an iteration: it only keeps the
+    // groups in step (nothing in LDS changes hands there), so no memory
+    // fence, and the scheduler moves no work across it.
+    auto phase_barrier = [] __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // K and V each have NB buffers; tile t lives in buffer t % NB. Iteration j
+    // reads K(j) and V(j-1) and starts the loads of K(j+NB-1) and V(j+NB-2),
+    // whose buffers held K(j-1) and V(j-2), last read in iteration j-1. So a
+    // tile's loads have NB-1 iterations to land. Every iteration starts the
+    // same number of loads (tiles past the last one read through an empty
+    // buffer resource: no memory access, zeros), so the wait at its end is
+    // one count: the loads of the last NB-2 iterations may still be in flight.
+    constexpr int NB = kKvDepth;
+    static_assert(NB >= 2 && NB <= 4, "two to four K and V buffers");
+    static_assert(BLK == 2, "the vmcnt arithmetic below counts 2 + 2 loads per iteration");
+    const __amdgpu_buffer_rsrc_t none_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(a.k)), (short)0, 0, 0x00020000);
+    auto kb = [&](auto i) __attribute__((always_inline)) -> char* {
+      constexpr int I = ((decltype(i)::value % NB) + NB) % NB;
+      if constexpr (I == 0) return k_lds0;
+      else if constexpr (I == 1) return k_lds1;
+      else if constexpr (I == 2) return k_lds2;
+      else return k_lds3;
+    };
+    auto vb = [&](auto i) __attribute__((always_inline)) -> char* {
+      constexpr int I = ((decltype(i)::value % NB) + NB) % NB;
+      if constexpr (I == 0) return v_lds0;
+      else if constexpr (I == 1) return v_lds1;
+      else if constexpr (I == 2) return v_lds2;
+      else return v_lds3;
+    };
+    auto load_kt = [&](int t, char* dst) __attribute__((always_inline)) {
+      if (t >= 0 && t < n_kt) load_k(t, dst);
+      else load_tile(none_rs, 0, dst, false);
+    };
+    auto load_vt = [&](int t, char* dst) __attribute__((always_inline)) {
+      if (t >= 0 && t < n_kt) load_v(t, dst);
+      else load_tile(none_rs, 0, dst, true);
+    };
+    // End of an iteration: this wavefront's loads for the next iteration have
+    // landed (the 4 loads of each of the NB-2 later iterations may still be
+    // in flight) and its LDS reads are done; the barrier publishes both. No
+    // memory fence: a workgroup fence would also wait for those later loads.
+    auto iter_barrier = [] __attribute__((always_inline)) {
+      if constexpr (NB == 2)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      else if constexpr (NB == 3)
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+    };
+    // Iteration j: slot 2j then slot 2j+1. Each group has a loop of its own
+    // (the branch is outside the loop), so that the registers of each are
+    // allocated for its own order of phases.
+    auto slots = [&](auto grp, int j, const char* __restrict__ vl, const char* __restrict__ kl,
+                     char* __restrict__ kw, char* __restrict__ vw) __attribute__((always_inline)) {
+      constexpr bool A = decltype(grp)::value;
+      load_kt(j + NB - 1, kw);
+      load_vt(j + NB - 2, vw);
+      if constexpr (A)
+        m_phase(j, vl, kl);
+      else
+        v_phase(j - 1);
+      phase_barrier();
+      if constexpr (A)
+        v_phase(j);
+      else
+        m_phase(j, vl, kl);
+      iter_barrier();
+    };
+    // Unrolled by NB so that every buffer is a fixed LDS variable; the
+    // iterations past n_kt do nothing but keep the barriers in step.
+    auto iter = [&](auto grp, auto r, int j) __attribute__((always_inline)) {
+      constexpr int R = decltype(r)::value;  // j % NB
+      slots(grp, j, vb(std::integral_constant<int, R - 1>{}), kb(std::integral_constant<int, R>{}),
+            kb(std::integral_constant<int, R - 1>{}), vb(std::integral_constant<int, R - 2>{}));
+    };
+    auto run = [&](auto grp) __attribute__((always_inline)) {
+      for (int j = 0; j <= n_kt; j += NB) {
+        iter(grp, std::integral_constant<int, 0>{}, j);
+        iter(grp, std::integral_constant<int, 1>{}, j + 1);
+        if constexpr (NB > 2) iter(grp, std::integral_constant<int, 2>{}, j + 2);
+        if constexpr (NB > 3) iter(grp, std::integral_constant<int, 3>{}, j + 3);
+      }
+    };
+    // Prologue: the loads that iterations 1-NB .. -1 would have started,
+    // K(0) .. K(NB-2) and V(-1) .. V(NB-3) (V(-1) empty), then K(0) is waited for.
+    load_kt(0, kb(std::integral_constant<int, 0>{}));
+    load_vt(-1, vb(std::integral_constant<int, -1>{}));
+    if constexpr (NB > 2) {
+      load_kt(1, kb(std::integral_constant<int, 1>{}));
+      load_vt(0, vb(std::integral_constant<int, 0>{}));
     }
+    if constexpr (NB > 3) {
+      load_kt(2, kb(std::integral_constant<int, 2>{}));
+      load_vt(1, vb(std::integral_constant<int, 1>{}));
+    }
+    iter_barrier();
+    if (grp_a)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
+    // Every load has landed (the last ones were of empty tiles, writing zeros)
+    // before the epilogue reuses the buffers.
     wait_loads();
     __syncthreads();
+  } else {
+    // ---- prologue: K(0), K(1), V(0) in LDS, then S(0).
+    f32x16_t sc[QB][2];
+    if (n_kt > 0) {
+      load_k(0, kbuf(0));
+      load_v(0, vbuf(0));
+      if (n_kt > 1) load_k(1, kbuf(1));
+    }
+    wait_loads();
+    __syncthreads();  // K(0), K(1), V(0) visible to every wavefront
+    if (n_kt > 0 && any_active(0)) qk(kbuf(0), sc);
+    __syncthreads();  // every wavefront has read K(0) before K(2) replaces it
+
+    bool all[QB];
+  #pragma unroll
+    for (int qb = 0; qb < QB; ++qb) all[qb] = true;
+    // One tile of the main loop with buffer parity PAR known at compile time
+    // (LDS offsets become immediates); the scores of tile t arrive in `cur`
+    // and those of tile t+1 leave in `nxt`. The next tile's scores are
+    // computed even past the last tile (from a stale buffer, then discarded)
+    // to keep this block free of branches.
+    auto main_step = [&](auto par, int t, f32x16_t (&cur)[QB][2], f32x16_t (&nxt)[QB][2]) {
+      constexpr int PAR = decltype(par)::value;
+      lds_step(t, PAR ? v_lds1 : v_lds0, PAR ? k_lds0 : k_lds1, PAR ? k_lds1 : k_lds0, PAR ? v_lds0 : v_lds1,
+               [&](const char* vl, const char* kl) {
+  #pragma unroll
+                 for (int qb = 0; qb < QB; ++qb) update_max(qb, cur[qb][0], cur[qb][1]);
+                 exp_pv_qk(vl, cur, all, kl, true, nxt);
+               });
+      wait_loads();
+      __syncthreads();
+    };
+    // Unrolled by two so the two score arrays swap roles instead of being
+    // copied, and t starts at 0, so tile t uses buffer t & 1 = its position.
+    int t = 0;
+    {
+      f32x16_t sn[QB][2];
+      for (; t + 1 < n_main; t += 2) {
+        main_step(std::integral_constant<int, 0>{}, t, sc, sn);
+        main_step(std::integral_constant<int, 1>{}, t + 1, sn, sc);
+      }
+      if (t < n_main) {
+        main_step(std::integral_constant<int, 0>{}, t, sc, sn);
+  #pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          sc[qb][0] = sn[qb][0];
+          sc[qb][1] = sn[qb][1];
+        }
+        ++t;
+      }
+    }
+    for (; t < n_kt; ++t) {
+      f32x16_t sn[QB][2];
+      const bool next = t + 1 < n_kt && any_active(t + 1);
+      lds_step(t, vbuf(t), kbuf(t + 1), kbuf(t), vbuf(t + 1), [&](const char* vl, const char* kl) {
+        bool use[QB];
+        bool any = false;
+  #pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          use[qb] = blk_active(t, qb);
+          any |= use[qb];
+          if (use[qb]) {
+            mask(t, qb, sc[qb][0], sc[qb][1]);
+            update_max(qb, sc[qb][0], sc[qb][1]);
+          }
+        }
+        if (any)
+          exp_pv_qk(vl, sc, use, kl, next, sn);
+        else if (next)
+          qk(kl, sn);
+      });
+      if (next) {
+  #pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          sc[qb][0] = sn[qb][0];
+          sc[qb][1] = sn[qb][1];
+        }
+      }
+      wait_loads();
+      __syncthreads();
+    }
+
   }
 
   // ---- epilogue: O = O^T / sum(bf16 p), LSE = (m + log2 sum(p)) ln 2
@@ -590,7 +863,8 @@ hipError_t launch_cfg(const PrefillArgs& a, hipStream_t s) {
   const int nbh = a.B * a.Hq;
   const long long blocks = (long long)n_qtiles * nbh;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_bf16_kernel<NW, QB, kContig>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a, n_qtiles, nbh);
+  hipLaunchKernelGGL((prefill_bf16_kernel<NW, QB, kContig, kPingPong>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a,
+                     n_qtiles, nbh);
   return hipGetLastError();
 }
 
@@ -600,7 +874,8 @@ hipError_t launch_paged_cfg(const PrefillArgs& a, int n_items, hipStream_t s) {
   const long long blocks = (long long)n_items * a.Hq;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_bf16_kernel<NW, QB, kRagged>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a, 0, 0);
+  hipLaunchKernelGGL((prefill_bf16_kernel<NW, QB, kRagged, kPingPong>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, a,
+                     0, 0);
   return hipGetLastError();
 }
 
@@ -608,7 +883,7 @@ template <int NW, int QB>
 hipError_t launch_prefix_cfg(const PrefillArgs& a, int n_items, hipStream_t s) {
   static_assert(32 * NW * QB == kPrefillRows, "the plan's tile height must match the kernel's");
   if (n_items == 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_bf16_kernel<NW, QB, kPrefix>), dim3((unsigned)n_items), dim3(64 * NW), 0, s, a, 0, 0);
+  hipLaunchKernelGGL((prefill_bf16_kernel<NW, QB, kPrefix, false>), dim3((unsigned)n_items), dim3(64 * NW), 0, s, a, 0, 0);
   return hipGetLastError();
 }
 

@@ -141,8 +141,13 @@ __device__ __forceinline__ void store_rows(uint16_t* dst, const f32x16_t (&acc)[
 // ---------------------------------------------------------------- dQ
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a, int n_qtiles, int nbh) {
-  __shared__ __attribute__((aligned(16))) char k_lds[2 * kTile];
-  __shared__ __attribute__((aligned(16))) char v_lds[2 * kTile];
+  // Two K and two V tile buffers, each its own LDS variable: the compiler can
+  // then tell a tile's LDS reads from the loads filling the other pair and
+  // does not make the reads wait for them.
+  __shared__ __attribute__((aligned(16))) char k_lds0[kTile];
+  __shared__ __attribute__((aligned(16))) char k_lds1[kTile];
+  __shared__ __attribute__((aligned(16))) char v_lds0[kTile];
+  __shared__ __attribute__((aligned(16))) char v_lds1[kTile];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, col = lane & 31;
   constexpr int BR = 32 * NW;
 
@@ -208,8 +213,8 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles, int nbh) {
   tr_offsets(lane, t_off);
 
   if (n_kt > 0) {
-    load_rows(k_rs, 0, k_lds, wave, lane);
-    load_rows(v_rs, 0, v_lds, wave, lane);
+    load_rows(k_rs, 0, k_lds0, wave, lane);
+    load_rows(v_rs, 0, v_lds0, wave, lane);
   }
   wait_vmem();
   __syncthreads();
@@ -223,13 +228,20 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles, int nbh) {
   // in one barrier, in either loop.
   const int lim_wg = a.causal ? min(Sk - 1, q0 + off) : Sk - 1;
   const int n_full = max(0, min(n_kt, (lim_wg + 1) / kBc));
-  auto tile = [&](int t, auto masked) {
+  auto tile = [&](int t, auto masked, auto par) {
+    constexpr int PAR = decltype(par)::value;  // t & 1
+    // The lane offsets pass through here unchanged: otherwise the compiler
+    // forms a copy of them per buffer outside the loop, which spills.
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) asm volatile("" : "+v"(r_off[kk]));
+#pragma unroll
+    for (int db = 0; db < 4; ++db) asm volatile("" : "+v"(t_off[db][0]), "+v"(t_off[db][1]));
     if (t + 1 < n_kt) {
-      load_rows(k_rs, (t + 1) * kBc, k_lds + ((t + 1) & 1) * kTile, wave, lane);
-      load_rows(v_rs, (t + 1) * kBc, v_lds + ((t + 1) & 1) * kTile, wave, lane);
+      load_rows(k_rs, (t + 1) * kBc, PAR ? k_lds0 : k_lds1, wave, lane);
+      load_rows(v_rs, (t + 1) * kBc, PAR ? v_lds0 : v_lds1, wave, lane);
     }
-    const char* kl = k_lds + (t & 1) * kTile;
-    const char* vl = v_lds + (t & 1) * kTile;
+    const char* kl = PAR ? k_lds1 : k_lds0;
+    const char* vl = PAR ? v_lds1 : v_lds0;
     // S^T = K Q^T and dP^T = V dO^T: register i of lane l, half h2, is key
     // 32*h2 + 16*(i/8) + 8*hi + (i%8) of the tile, query row `qrow`.
     f32x16_t s[2], dp[2];
@@ -276,8 +288,22 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles, int nbh) {
     wait_vmem();
     __syncthreads();
   };
-  for (int t = 0; t < n_full; ++t) tile(t, std::false_type{});
-  for (int t = n_full; t < n_kt; ++t) tile(t, std::true_type{});
+  // Unrolled by two, so that every tile names its buffers at compile time.
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  int t = 0;
+  for (; t + 1 < n_full; t += 2) {
+    tile(t, std::false_type{}, P0{});
+    tile(t + 1, std::false_type{}, P1{});
+  }
+  for (; t < n_kt; ++t) {
+    if (t & 1)
+      tile(t, std::bool_constant<true>{}, P1{});
+    else if (t < n_full)
+      tile(t, std::false_type{}, P0{});
+    else
+      tile(t, std::true_type{}, P0{});
+  }
   if (qrow < Sq) store_rows(a.dq + (bh * Sq + qrow) * kD, acc, hi, a.scale);
 }
 
@@ -288,10 +314,17 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles, int nbh) {
 constexpr int KW = 8;
 __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(KW / 4, KW / 4)))
 void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
-  __shared__ __attribute__((aligned(16))) char q_lds[2 * kTile];
-  __shared__ __attribute__((aligned(16))) char o_lds[2 * kTile];  // dO
-  __shared__ __attribute__((aligned(16))) float st_lse[2][kBc];
-  __shared__ __attribute__((aligned(16))) float st_d[2][kBc];
+  // Double-buffered Q, dO, LSE and D tiles, each buffer its own LDS variable
+  // (named at compile time by the step loops, unrolled by two), so that a
+  // step's LDS reads do not wait for the loads filling the other buffers.
+  __shared__ __attribute__((aligned(16))) char q_lds0[kTile];
+  __shared__ __attribute__((aligned(16))) char q_lds1[kTile];
+  __shared__ __attribute__((aligned(16))) char o_lds0[kTile];  // dO
+  __shared__ __attribute__((aligned(16))) char o_lds1[kTile];
+  __shared__ __attribute__((aligned(16))) float st_lse0[kBc];
+  __shared__ __attribute__((aligned(16))) float st_lse1[kBc];
+  __shared__ __attribute__((aligned(16))) float st_d0[kBc];
+  __shared__ __attribute__((aligned(16))) float st_d1[kBc];
   __shared__ __attribute__((aligned(16))) char v_res[32 * KW * kRow];  // this workgroup's V rows
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, col = lane & 31;
   constexpr int BK = 32 * KW;  // keys per workgroup
@@ -375,7 +408,8 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
   int t_base[2];
   tr_bases(lane, t_base);
 
-  auto issue = [&](int step, int buf) {
+  auto issue = [&](int step, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     int jh, qt;
     step_tile(step, jh, qt);
     // The lane's load offsets are re-formed here on every call: hoisted out
@@ -387,36 +421,40 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
         const_cast<uint16_t*>(a.q + bh * (size_t)Sq * kD), (short)0, Sq * kRow, 0x00020000);
     const __amdgpu_buffer_rsrc_t ds = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(a.dO + bh * (size_t)Sq * kD), (short)0, Sq * kRow, 0x00020000);
-    load_rows<KW>(qs, qt * kBc, q_lds + buf * kTile, wave_u, ln);
-    load_rows<KW>(ds, qt * kBc, o_lds + buf * kTile, wave_u, ln);
+    load_rows<KW>(qs, qt * kBc, buf ? q_lds1 : q_lds0, wave_u, ln);
+    load_rows<KW>(ds, qt * kBc, buf ? o_lds1 : o_lds0, wave_u, ln);
     if (wave_u == 0) {
       const __amdgpu_buffer_rsrc_t ls = __builtin_amdgcn_make_buffer_rsrc(
           a.lse2 + bh * (size_t)Sq, (short)0, Sq * 4, 0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ls, (__attribute__((address_space(3))) void*)(&st_lse[buf][0]), 4,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ls, (__attribute__((address_space(3))) void*)(buf ? st_lse1 : st_lse0), 4,
                                                (qt * kBc + ln) * 4, 0, 0, 0);
     } else if (wave_u == 1) {
       const __amdgpu_buffer_rsrc_t dsr = __builtin_amdgcn_make_buffer_rsrc(
           a.delta + bh * (size_t)Sq, (short)0, Sq * 4, 0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(dsr, (__attribute__((address_space(3))) void*)(&st_d[buf][0]), 4,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(dsr, (__attribute__((address_space(3))) void*)(buf ? st_d1 : st_d0), 4,
                                                (qt * kBc + ln) * 4, 0, 0, 0);
     }
   };
 
-  if (n_steps > 0) issue(0, 0);
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  if (n_steps > 0) issue(0, P0{});
   wait_vmem();
   __syncthreads();
 
-  auto step = [&](int st, auto masked) {
+  auto step = [&](int st, auto masked, auto par) {
+    constexpr int buf = decltype(par)::value;  // st & 1
     // The per-step offsets base ^ const are cheap to form where they are
     // used; kept from outside the loop they would be spilled.
     asm volatile("" : "+v"(r_base), "+v"(v_base), "+v"(t_base[0]), "+v"(t_base[1]));
-    const int buf = st & 1;
-    if (st + 1 < n_steps) issue(st + 1, buf ^ 1);
+    if (st + 1 < n_steps) issue(st + 1, std::integral_constant<int, buf ^ 1>{});
     int jh_unused, qt_cur;
     step_tile(st, jh_unused, qt_cur);
     const int q0 = qt_cur * kBc;
-    const char* ql = q_lds + buf * kTile;
-    const char* ol = o_lds + buf * kTile;
+    const char* ql = buf ? q_lds1 : q_lds0;
+    const char* ol = buf ? o_lds1 : o_lds0;
+    const float* sl = buf ? st_lse1 : st_lse0;
+    const float* sd = buf ? st_d1 : st_d0;
 #pragma unroll
     for (int hq = 0; hq < 2; ++hq) {
       // S = Q K^T and dP = dO V^T for rows 32*hq .. +31 of the tile: register
@@ -440,10 +478,10 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
 #pragma unroll
       for (int h8 = 0; h8 < 2; ++h8) {
         const int rb = 32 * hq + 16 * h8 + 8 * hi;  // first row of these 8 registers
-        const float4 l0 = *reinterpret_cast<const float4*>(&st_lse[buf][rb]);
-        const float4 l1 = *reinterpret_cast<const float4*>(&st_lse[buf][rb + 4]);
-        const float4 d0 = *reinterpret_cast<const float4*>(&st_d[buf][rb]);
-        const float4 d1 = *reinterpret_cast<const float4*>(&st_d[buf][rb + 4]);
+        const float4 l0 = *reinterpret_cast<const float4*>(sl + rb);
+        const float4 l1 = *reinterpret_cast<const float4*>(sl + rb + 4);
+        const float4 d0 = *reinterpret_cast<const float4*>(sd + rb);
+        const float4 d1 = *reinterpret_cast<const float4*>(sd + rb + 4);
         const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
         const float dvv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
         // Rows x of these 8 that this lane's key sees: x in [xlo, xhi) (row
@@ -491,8 +529,25 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
     wait_vmem();
     __syncthreads();
   };
-  for (int st = 0; st < n_mask_steps; ++st) step(st, std::true_type{});
-  for (int st = n_mask_steps; st < n_steps; ++st) step(st, std::false_type{});
+  // Both loops unrolled by two (buffer = step & 1 at compile time).
+  int st = 0;
+  for (; st + 1 < n_mask_steps; st += 2) {
+    step(st, std::true_type{}, P0{});
+    step(st + 1, std::true_type{}, P1{});
+  }
+  if (st < n_mask_steps) {
+    step(st, std::true_type{}, P0{});
+    ++st;
+  }
+  if (st & 1) {
+    if (st < n_steps) step(st, std::false_type{}, P1{});
+    ++st;
+  }
+  for (; st + 1 < n_steps; st += 2) {
+    step(st, std::false_type{}, P0{});
+    step(st + 1, std::false_type{}, P1{});
+  }
+  if (st < n_steps) step(st, std::false_type{}, P0{});
   if (key < Sk) {
     store_rows(a.dk + (bgk * Sk + key) * kD, dk, hi, a.scale);
     store_rows(a.dv + (bgk * Sk + key) * kD, dv, hi, 1.f);
