@@ -200,7 +200,8 @@ def cpu_baseline_prefill(w, q, k, v, budget_s=15.0):
         for i in g.permutation(len(heads)):
             b, h = heads[i]
             bd = 4 * int(g.integers(1, nblk // 4))
-            jobs += [(b, h, 0), (b, h, nblk - 1), (b, h, bd - 1), (b, h, bd), (b, h, int(g.integers(0, nblk)))]
+            jobs += [(b, h, 0), (b, h, nblk - 1), (b, h, bd - 1), (b, h, bd)]
+        jobs += [(b, h, int(g.integers(0, nblk))) for b, h in (heads[i] for i in g.integers(0, len(heads), 4096))]
 
     def one(job):
         b, h, blk = job
@@ -431,6 +432,13 @@ PMC_LEGS = {
     "copy": ("--only copy", ["neg"], None),
 }
 PMC_RUN = "--steps 3 --warmup 1 --prewarm-s 0 --no-cpu-baseline"
+# Shader-sequencer counters of the 32K-token prefill (one pass): matrix-core
+# busy cycles, co-issue, shader-engine busy cycles (with the kernel time they
+# give the clock the chip held), wave time and waits.
+SQ_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_BUSY_CYCLES SQ_WAVE_CYCLES "
+               "SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU SQ_INSTS_MFMA")
+SQ_LEG = ("prefill_bf16_wl3_sq", "--only prefill --prefill-workload 3", "prefill_bf16_kernel")
+N_SE, N_SIMD = 32, 1024   # MI355X: 8 XCDs x 4 shader engines; 256 CUs x 4 SIMDs
 
 
 def profile_commands(d):
@@ -438,6 +446,8 @@ def profile_commands(d):
     for leg, (flags, _, _) in PMC_LEGS.items():
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             cmds.append(f"rocprofv3 --pmc {c} -f csv -d {d}/pmc_{leg}_{c} -o pmc -- python3 bench.py {flags} {PMC_RUN}")
+    cmds.append(f"rocprofv3 --pmc {SQ_COUNTERS} -f csv -d {d}/pmc_{SQ_LEG[0]} -o pmc -- python3 bench.py "
+                f"{SQ_LEG[1]} {PMC_RUN}")
     return cmds
 
 
@@ -464,6 +474,36 @@ def _pmc_means(path, names):
         total += statistics.mean(vals)
         counts.append(len(vals))
     return total, min(counts)
+
+
+def _pmc_means_one(path, kernel, counter):
+    """Mean per dispatch of one counter over the kernel's dispatches in a --pmc csv."""
+    import csv
+    import glob
+    f = glob.glob(os.path.join(path, "*counter_collection.csv"))[0]
+    per = {}
+    for r in csv.DictReader(open(f)):
+        if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return statistics.mean(per.values()) if per else float("nan")
+
+
+def _trace_mean_us(path, prefix, min_us=0.0):
+    """Mean duration (us) of the dispatches of kernels whose short name starts with
+    ``prefix`` and that run at least ``min_us``, from a --kernel-trace csv."""
+    import csv
+    import glob
+    f = glob.glob(os.path.join(path, "*kernel_trace.csv"))
+    if not f:
+        return None
+    ds = []
+    for r in csv.DictReader(open(f[0])):
+        m = re.search(r"::(\w+(?:<[^>]*>)?)\(", r["Kernel_Name"])
+        k = m.group(1) if m else r["Kernel_Name"]
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if k.startswith(prefix) and dur >= min_us:
+            ds.append(dur)
+    return statistics.mean(ds) if ds else None
 
 
 def summarize_profiles(d):
@@ -527,6 +567,28 @@ def summarize_profiles(d):
         path = os.path.join(out_dir, f"{leg}_traffic.txt")
         open(path, "w").write("\n".join(lines) + "\n")
         written.append(path)
+    sq_dir = f"{d}/pmc_{SQ_LEG[0]}"
+    if os.path.isdir(sq_dir):
+        names = SQ_COUNTERS.split()
+        vals = {n: _pmc_means_one(sq_dir, SQ_LEG[2], n) for n in names}
+        t_us = _trace_mean_us(f"{d}/kt", "prefill_bf16_kernel<8, 1, 0", min_us=2000.0)
+        lines = ["# Shader-sequencer counters of the 32K-token GQA prefill kernel, mean per dispatch",
+                 "# (rocprofv3 --pmc, one pass). SQ_BUSY_CYCLES is summed over the 32 shader engines, the",
+                 "# MFMA counters over the 1,024 SIMDs; wave counters are in quad-cycles.",
+                 *header, f"source_sha256_16: {source_sha('exact_attention_20_amd/csrc/prefill_bf16.hip')}"]
+        lines += [f"{n}: {vals[n]:.6g}" for n in names]
+        se_cycles = vals["SQ_BUSY_CYCLES"] / N_SE
+        mfma = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / N_SIMD
+        lines.append(f"cycles_per_shader_engine: {se_cycles:.6g}")
+        lines.append(f"mfma_busy_fraction_of_cycles: {mfma / se_cycles:.4f}")
+        lines.append(f"mfma_coexec_fraction_of_mfma_busy: {vals['SQ_VALU_MFMA_COEXEC_CYCLES'] / vals['SQ_VALU_MFMA_BUSY_CYCLES']:.4f}")
+        if t_us:
+            lines.append(f"kernel_us_from_kernel_trace: {t_us:.1f}")
+            lines.append(f"implied_clock_ghz: {se_cycles / (t_us * 1e3):.3f}")
+            lines.append(f"bf16_mfma_peak_at_that_clock_tflops: {2500.0 * se_cycles / (t_us * 1e3) / 2.4:.0f}")
+        path = os.path.join(out_dir, f"{SQ_LEG[0]}_counters.txt")
+        open(path, "w").write("\n".join(lines) + "\n")
+        written.append(path)
     kt = glob.glob(f"{d}/kt/*kernel_stats.csv")
     if kt:
         rows = list(csv.DictReader(open(kt[0])))
@@ -556,20 +618,21 @@ def summarize_profiles(d):
                     leg = "decode"
                 if k.startswith("kv_append"):
                     leg = "ragged"
-                if k == "prefill_bf16_kernel<8, 1, 2>":
+                if k.startswith("prefill_bf16_kernel<8, 1, 2"):
                     leg = "cascade"
                 if k.startswith("prefill_fp8"):
                     leg = "fp8"
-                if k.startswith("bwd_") or (k == "prefill_bf16_kernel<8, 1, 0>" and leg != "prefill"):
+                if k.startswith("bwd_") or (k.startswith("prefill_bf16_kernel<8, 1, 0") and leg != "prefill"):
                     leg = "backward"  # the backward leg starts with one forward call for O and LSE
                 sub = leg
                 if leg in ("cascade", "cascade (plain-decode comparison)"):
                     if k.startswith("decode_"):
-                        leg = sub = "cascade" if prev == "prefill_bf16_kernel<8, 1, 2>" else "cascade (plain-decode comparison)"
+                        leg = sub = ("cascade" if prev.startswith("prefill_bf16_kernel<8, 1, 2")
+                                     else "cascade (plain-decode comparison)")
                     elif k.startswith("lse_merge"):
                         sub = leg
                 dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-                if leg == "prefill" and k == "prefill_bf16_kernel<8, 1, 0>":
+                if leg == "prefill" and k.startswith("prefill_bf16_kernel<8, 1, 0"):
                     # two prefill workloads share the kernel: the 32K-token GQA launch
                     # runs ~8 ms, the 4 x 4096-token one well under 2 ms
                     sub = "prefill (B1 Hq32/Hkv8 S32768)" if dur > 2000.0 else "prefill (B4 H32 S4096)"
