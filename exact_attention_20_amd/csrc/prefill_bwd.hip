@@ -38,7 +38,7 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kBc = 64;       // keys per tile (dQ kernel), query rows per tile (dK/dV kernel)
-constexpr int kRow = kD * 2;  // 256 B per bf16 row; 16-byte units XOR-swizzled by row & 15
+constexpr int kRow = kD * 2;  // 256 B per bf16 row; 16-byte units XOR-swizzled by swz(row)
 constexpr int kTile = kBc * kRow;  // 16 KB
 constexpr int NW = 8;
 
@@ -58,6 +58,15 @@ struct BwdArgs {
   float scale;
 };
 
+// Unit c of row r sits at unit c ^ swz(r). The LDS serves 256 bytes (64
+// banks) per clock. swz is a bijection on every 16 aligned rows, so the 16
+// lanes of a row read (one unit of 16 different rows) hit 16 distinct
+// 16-byte bank groups. Its top two bits are r & 3, so the four consecutive
+// rows that a transposing read spans land in four distinct 64-byte blocks.
+// (With r & 15 those four rows only permuted units inside one block: four
+// lanes per bank.)
+__device__ __forceinline__ int swz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+
 // Direct HBM -> LDS load of a 64-row tile: 16 blocks of 1 KB shared by the
 // W wavefronts; lane l fills LDS unit (l & 15) of row 4j + (l >> 4) with the
 // global unit that the row's swizzle stores there.
@@ -67,7 +76,7 @@ __device__ __forceinline__ void load_rows(const __amdgpu_buffer_rsrc_t& rs, int 
   for (int i = 0; i < 16 / W; ++i) {
     const int j = wave * (16 / W) + i;
     const int r = 4 * j + (lane >> 4);
-    const int unit = (lane & 15) ^ (r & 15);
+    const int unit = (lane & 15) ^ swz(r);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(buf + j * 1024), 16,
                                              (r0 + r) * kRow + unit * 16, 0, 0, 0);
   }
@@ -79,12 +88,12 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 __device__ __forceinline__ void row_offsets(int col, int hi, int (&off)[8]) {
   const int R = kperm(col);
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) off[kk] = R * kRow + 16 * ((2 * kk + hi) ^ (R & 15));
+  for (int kk = 0; kk < 8; ++kk) off[kk] = R * kRow + 16 * ((2 * kk + hi) ^ swz(R));
 }
 // Transposing-read offsets (A operand rows = dims 32*db + lane%32, k = rows
 // 16*ks + 8*hi + e; add 16*ks rows): lane L of 16-lane group g addresses row
-// 8*(g>>1) + 4*r + (L>>2), dims 32*db + 16*(g&1) + 4*(L&3). With the row &
-// 15 swizzle the offset does not depend on ks.
+// 8*(g>>1) + 4*r + (L>>2), dims 32*db + 16*(g&1) + 4*(L&3). swz(r) depends
+// on r & 15 only, so the offset does not depend on ks.
 __device__ __forceinline__ void tr_offsets(int lane, int (&off)[4][2]) {
   const int g = lane >> 4, L = lane & 15;
 #pragma unroll
@@ -93,7 +102,7 @@ __device__ __forceinline__ void tr_offsets(int lane, int (&off)[4][2]) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const int u = 4 * db + 2 * (g & 1) + ((L & 3) >> 1);
-      off[db][r] = R * kRow + 16 * (u ^ (R & 15)) + 8 * (L & 1);
+      off[db][r] = R * kRow + 16 * (u ^ swz(R)) + 8 * (L & 1);
     }
   }
 }
@@ -104,11 +113,11 @@ __device__ __forceinline__ bf16x8_t tr_operand(const char* base, int off0, int o
   const uint2 v1 = lds_read_tr16(base + off1);
   return __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
 }
-// The same offsets in XOR form, one register each: with s = row & 15, unit
+// The same offsets in XOR form, one register each: with s = swz(row), unit
 // (2*kk + hi) ^ s sits at byte 32*(kk ^ (s>>1)) + 16*(hi ^ (s&1)), so the
 // kk-th row offset is X ^ (32*kk); the transposing offsets are Y_r ^ (64*db).
 __device__ __forceinline__ int row_base(int R, int hi) {
-  const int sw = R & 15;
+  const int sw = swz(R);
   return R * kRow + 32 * (sw >> 1) + 16 * (hi ^ (sw & 1));
 }
 __device__ __forceinline__ void tr_bases(int lane, int (&y)[2]) {
@@ -117,7 +126,7 @@ __device__ __forceinline__ void tr_bases(int lane, int (&y)[2]) {
   for (int r = 0; r < 2; ++r) {
     const int R = 8 * (g >> 1) + 4 * r + (L >> 2);
     const int c0 = 32 * (g & 1) + 16 * ((L & 3) >> 1);
-    y[r] = R * kRow + 8 * (L & 1) + (c0 ^ (16 * (R & 15)));
+    y[r] = R * kRow + 8 * (L & 1) + (c0 ^ (16 * swz(R)));
   }
 }
 
