@@ -82,6 +82,16 @@ __device__ __forceinline__ void load_rows(const __amdgpu_buffer_rsrc_t& rs, int 
   }
 }
 
+// This lane's index, formed where it is used. The asm is opaque, so the
+// compiler neither hoists it nor keeps a copy live across a loop (where such
+// a copy was spilled, and its reload waited for every load in flight).
+__device__ __forceinline__ int lane_here() {
+  int lo, id;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0" : "=v"(lo));
+  asm volatile("v_mbcnt_hi_u32_b32 %0, -1, %1" : "=v"(id) : "v"(lo));
+  return id;
+}
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Row-operand offsets (A operand rows in kperm order, dims 16*kk + 8*hi).
@@ -158,6 +168,7 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles, int nbh) {
   __shared__ __attribute__((aligned(16))) char v_lds0[kTile];
   __shared__ __attribute__((aligned(16))) char v_lds1[kTile];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, col = lane & 31;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy
   constexpr int BR = 32 * NW;
 
   const int L = blockIdx.x;
@@ -268,16 +279,25 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles, int nbh) {
     // tiles only), dS^T.
     bf16x8_t dsf[4];
     auto ds_tile = [&](auto masked) {
-      const int lim = a.causal ? min(Sk - 1, qrow + off) : Sk - 1;
+      // Key t*kBc + 8*hi + k is visible to this lane's row iff k <= rel, for
+      // k = 32*h2 + 16*(i/8) + i%8 (a constant per element). rel is formed
+      // here from the lane index, so nothing of it stays live across the
+      // loop (a per-lane key limit kept there was spilled with an operand).
+      int rel = 0;
+      if constexpr (decltype(masked)::value) {
+        const int lh = lane_here();
+        const int row = q0 + 32 * wave_s + (lh & 31);
+        const int lim = a.causal ? min(Sk - 1, row + off) : Sk - 1;
+        rel = lim - t * kBc - 8 * (lh >> 5);
+      }
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float arg = __builtin_fmaf(s[h2][i], c, -lse2);
           if constexpr (decltype(masked)::value) {
-            const int key = t * kBc + 32 * h2 + 16 * (i >> 3) + 8 * hi + (i & 7);
             // Masked entries get a -inf argument (exp2 -> 0): a select, not a branch per element.
-            arg = key > lim ? kNegInf : arg;
+            arg = 32 * h2 + 16 * (i >> 3) + (i & 7) > rel ? kNegInf : arg;
           }
           s[h2][i] = fast_exp2(arg) * (dp[h2][i] - dl);
         }
@@ -366,7 +386,6 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
 #pragma unroll
     for (int c4 = 0; c4 < BK / 64; ++c4) load_rows<KW>(vs, kt * BK + 64 * c4, v_res + c4 * kTile, wave, lane);
   }
-  int v_base = row_base(32 * wave + col, hi);  // this lane's V row in v_res
   f32x16_t dk[4], dv[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -423,8 +442,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
     step_tile(step, jh, qt);
     // The lane's load offsets are re-formed here on every call: hoisted out
     // of the step loops by the compiler, they were spilled and reloaded.
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
+    const int ln = lane_here();
     const size_t bh = (size_t)b * a.Hq + g * G + jh;
     const __amdgpu_buffer_rsrc_t qs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(a.q + bh * (size_t)Sq * kD), (short)0, Sq * kRow, 0x00020000);
@@ -455,7 +473,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
     constexpr int buf = decltype(par)::value;  // st & 1
     // The per-step offsets base ^ const are cheap to form where they are
     // used; kept from outside the loop they would be spilled.
-    asm volatile("" : "+v"(r_base), "+v"(v_base), "+v"(t_base[0]), "+v"(t_base[1]));
+    asm volatile("" : "+v"(r_base), "+v"(t_base[0]), "+v"(t_base[1]));
     if (st + 1 < n_steps) issue(st + 1, std::integral_constant<int, buf ^ 1>{});
     int jh_unused, qt_cur;
     step_tile(st, jh_unused, qt_cur);
@@ -476,6 +494,11 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
         const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(ql + ro);
         s = kk == 0 ? mfma32_first(qa, kreg[kk]) : mfma32(qa, kreg[kk], s);
       }
+      // This lane's V row in v_res, formed here from the lane index: kept
+      // across the loop, it was spilled, and its reload mid-step waited for
+      // the prefetch loads.
+      const int lh = lane_here();
+      const int v_base = row_base(32 * wave_u + (lh & 31), lh >> 5);
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         const int ro = (r_base ^ (32 * kk)) + 32 * hq * kRow;
@@ -509,12 +532,13 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
             dp[i] = p * (dp[i] - dvv[x]);
           }
         } else {
-          const int xlo = a.causal ? key - off - (q0 + rb) : 0;
-          const int xhi = key < Sk ? Sq - (q0 + rb) : 0;
+          const int key_h = kt * BK + 32 * wave_u + (lane_here() & 31);
+          const int xlo = a.causal ? key_h - off - (q0 + rb) : 0;
+          const int xhi = key_h < Sk ? Sq - (q0 + rb) : 0;
 #pragma unroll
           for (int x = 0; x < 8; ++x) {
             const int i = 8 * h8 + x;
-            const float p = fast_exp2((x >= xlo) & (x < xhi) ? __builtin_fmaf(s[i], c, -lv[x]) : kNegInf);
+            const float p = fast_exp2(((x >= xlo) & (x < xhi)) ? __builtin_fmaf(s[i], c, -lv[x]) : kNegInf);
             s[i] = p;
             dp[i] = p * (dp[i] - dvv[x]);
           }
