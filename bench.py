@@ -723,8 +723,9 @@ def main():
         summarize_profiles(args.summarize_profiles)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(the way it would shard is described in DESIGN.md).", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(prefill and decode would shard by request and KV-head group with no exchange).",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
