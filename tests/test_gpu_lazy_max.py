@@ -1,0 +1,84 @@
+"""Parity where the running max must move again and again.
+
+The kernels keep a lazy running max: it moves only when a tile's scores rise
+more than 2^8 (in exp2 units) above it, and O and the normalisers are then
+rescaled. Random inputs settle the max after the first tile or two. Here the
+scores of every row ramp with the key's logical position, about 0.25 natural
+units per key (about 23 exp2 units per 64-key tile or page), so the max moves
+on nearly every tile; a sawtooth variant lets it rise, fall back and rise
+above its old level. The oracle gets the same bf16 inputs, so an error in the
+rescale path shows up against it."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import check, f64, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+SCALE = float(np.float32(1 / np.sqrt(128)))
+RISE = 0.25    # natural-log units of score per key
+
+
+def offset(pos, shape):
+    """Score offset of the key at logical position pos (natural-log units)."""
+    pos = np.asarray(pos, np.float64)
+    if shape == "ramp":
+        return RISE * pos
+    # sawtooth: three pages up, then back down; each peak above the last
+    return RISE * (pos % 192) + 0.05 * pos
+
+
+def shape_query(q):
+    """Query dim 0 := 4 and the other dims scaled down, so dim 0 carries the score."""
+    q[..., 0] = 4.0
+    q[..., 1:] *= 0.1
+
+
+def key_dim0(pos, shape):
+    """Key dim 0 that gives the offset through a query dim 0 of 4."""
+    return torch.from_numpy((offset(pos, shape) / (4.0 * SCALE)).astype(np.float32))
+
+
+@pytest.mark.parametrize("shape", ["ramp", "sawtooth"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_moving_max(shape, causal):
+    fa = need_gpu()
+    B, Hq, Hkv, S, D = 1, 4, 2, 777, 128
+    say(f"[case] prefill moving max {shape} causal={causal}")
+    q, k, v = workloads.prefill_inputs(B, Hq, Hkv, S, S, D, "bf16", 61)
+    q, k = q.float(), k.float()
+    shape_query(q)
+    k[..., 0] = key_dim0(np.arange(S), shape)
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    out, lse = fa.prefill(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=SCALE)
+    torch.cuda.synchronize()
+    O, L = oracle.prefill(f64(q), f64(k), f64(v), SCALE, causal)
+    check(f"prefill moving max {shape} causal={causal}", f64(out), O, f64(lse), L, "bf16")
+
+
+@pytest.mark.parametrize("shape", ["ramp", "sawtooth"])
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+def test_decode_moving_max(shape, num_splits):
+    fa = need_gpu()
+    lengths = [1, 65, 700, 2049]
+    Hq, Hkv, D = 8, 2, 128
+    say(f"[case] decode moving max {shape} splits={num_splits}")
+    kv = workloads.paged_inputs(len(lengths), Hq, Hkv, D, "bf16", lengths, 62, nan_tails=False)
+    q, kp = kv.q.float(), kv.k_pages.float()
+    shape_query(q)
+    table = kv.page_table.numpy()
+    for b, n in enumerate(lengths):
+        t = np.arange(n)
+        # every KV head of the token's physical page slot
+        kp[table[b, t // 64], :, t % 64, 0] = key_dim0(t, shape)[:, None].expand(n, Hkv)
+    q, kp = q.to(torch.bfloat16), kp.to(torch.bfloat16)
+    plan = fa.fa_decode_plan(kv.seqlens, kv.page_table, kv.num_pages, Hq, Hkv, D, fa.BF16, num_splits)
+    out, lse = fa.decode(plan, q.cuda(), kp.cuda(), kv.v_pages.cuda(), kv.page_table.cuda(),
+                         kv.seqlens.cuda(), None, None, SCALE)
+    torch.cuda.synchronize()
+    O, L = oracle.paged_decode(f64(q), kp.float().numpy(), kv.v_pages.float().numpy(), kv.page_table.numpy(),
+                               kv.seqlens.numpy(), SCALE)
+    check(f"decode moving max {shape} splits={num_splits}", f64(out), O, f64(lse), L, "bf16")
