@@ -29,8 +29,9 @@ of the 4 x 32-head x 4096 shape, and ``backward`` the gradients (dQ, dK, dV)
 of that bf16 shape.
 Inputs are resident in HBM before timing. Each leg first runs untimed for
 --prewarm-s seconds (default 1 s: GPU clocks and power reach steady state)
-and --warmup more times; each timed call is then bracketed by HIP events on
-the stream it runs on.
+and --warmup more times; the timed calls then run back to back in up to five
+runs of at least 10 calls, each bracketed by HIP events on the stream it runs
+on (time per call = a run's duration over its calls).
 
 Prints ONE JSON line. ``value`` is the headline prefill throughput in
 TFLOP/s (algorithmic FLOPs 4*B*H*D*S(S+1)/2 over the measured time); decode
@@ -154,11 +155,18 @@ def read_traffic(name, src_rel):
         return None
 
 
-def time_calls(fn, steps, warmup, stream, prewarm_s=0.0):
-    """HIP-event time (ms) of each of `steps` calls of fn on `stream`, after
+def time_calls(fn, steps, warmup, stream, prewarm_s=0.0, runs=5):
+    """HIP-event time (ms) per call of `steps` calls of fn on `stream`, after
     running fn for at least `prewarm_s` seconds (GPU clocks and power reach
     their steady state; an idle GPU runs the first ~0.1 s of work up to 15%
-    slower) and then `warmup` more untimed calls."""
+    slower) and then `warmup` more untimed calls.
+
+    The timed calls run back to back in up to `runs` runs of at least 10
+    calls, each run bracketed by one pair of events on `stream`; a call's time is its
+    run's duration over the run's number of calls. So the mean is the average
+    launch duration over the timed region, and the median is taken over runs.
+    (An event pair around every call adds about 2.5 us of event overhead to
+    each: 8% of the 28 us KV append, against its kernel trace.)"""
     import torch
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < prewarm_s:
@@ -168,13 +176,19 @@ def time_calls(fn, steps, warmup, stream, prewarm_s=0.0):
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in evs:
+    runs = max(1, min(runs, steps // 10))   # at least 10 calls a run
+    sizes = [steps // runs + (1 if i < steps % runs else 0) for i in range(runs)]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(runs)]
+    for (a, b), n in zip(evs, sizes):
         a.record(stream)
-        fn()
+        for _ in range(n):
+            fn()
         b.record(stream)
     torch.cuda.synchronize()
-    return [a.elapsed_time(b) for a, b in evs]
+    out = []
+    for (a, b), n in zip(evs, sizes):
+        out += [a.elapsed_time(b) / n] * n
+    return out
 
 
 def cpu_baseline_prefill(w, q, k, v, budget_s=15.0):

@@ -8,15 +8,12 @@
 // t = L_b - n_b + i, stored in slot t % 64 of page page_table[b][t / 64].
 //
 // Pure data movement, bound by HBM: every byte of K_new and V_new is read
-// once and written once. One thread moves one 16-byte unit of K and the
-// matching unit of V; the 16 threads of a (token, KV head) cover its 256-byte
-// row, so reads are fully coalesced and each page row is written as one
-// contiguous 256-byte run. The source unit is the thread's index, so its
-// loads are issued before the destination lookup. For batches of up to
-// kStagedReqs requests each workgroup stages cu_seqlens_q and the lengths in
-// LDS with one coalesced read and searches there, so a thread waits for two
-// memory round trips (metadata with its data, then its page id) instead of
-// one per step of the search.
+// once and written once. One wavefront moves one new token: its lanes take
+// the token's Hkv 256-byte rows in 16-byte units (consecutive lanes,
+// consecutive units: reads and the page-row writes are contiguous runs).
+// The token's request, position and page are the same for every lane, so
+// they are found with scalar loads (binary search over cu_seqlens_q, then
+// one page-table entry) while the lanes' data loads are in flight.
 #include "fa_internal.h"
 #include "hip_common.h"
 
@@ -25,71 +22,81 @@ namespace fa {
 namespace {
 
 constexpr int kUnitsPerRow = 128 * 2 / 16;  // 16-byte units in one bf16 row of D = 128
-constexpr int kStagedReqs = 1024;           // largest batch whose metadata is staged in LDS
+typedef __attribute__((address_space(4))) const int32_t cint;
 
-template <bool STAGED>
+// P: 16-byte units per lane at a time (the token's Hkv * 16 units go over
+// the 64 lanes in chunks of 64 * P). The first chunk's loads are issued
+// before the lookup; with more than one chunk the rest follow it.
+template <int P>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
-  __shared__ int s_cu[STAGED ? kStagedReqs + 1 : 1];
-  __shared__ int s_len[STAGED ? kStagedReqs + 1 : 1];  // entry B repeats entry B - 1
-  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t units_per_tok = (int64_t)a.Hkv * kUnitsPerRow;
-  const bool live = u < (int64_t)a.T * units_per_tok;
-  // Source unit u is ((tk * Hkv + g) * 16 + c) of the packed [T, Hkv, D] rows.
-  u32x4_t kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-  if (live) {
-    kv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(a.k_new) + u);
-    vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(a.v_new) + u);
-  }
-  if constexpr (STAGED) {
-    for (int i = threadIdx.x; i <= a.B; i += 256) {
-      const int x = a.cu_q[i], y = a.seqlens[min(i, a.B - 1)];  // both loads in flight together
-      s_cu[i] = x;
-      s_len[i] = y;
+  const int lane = threadIdx.x & 63;
+  const int tk = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (tk >= a.T) return;
+  const int units = a.Hkv * kUnitsPerRow;
+  const size_t src0 = (size_t)tk * units;
+  u32x4_t kv[P], vv[P];
+  auto load = [&](int base) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int u = base + lane + 64 * p;
+      if (u < units) {
+        kv[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(a.k_new) + src0 + u);
+        vv[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(a.v_new) + src0 + u);
+      }
     }
-    __syncthreads();
-  }
-  if (!live) return;
-  const int tk = (int)(u / units_per_tok);
-  const int rem = (int)(u % units_per_tok);
-  const int g = rem / kUnitsPerRow, c = rem % kUnitsPerRow;
-  auto cu = [&](int i) { return STAGED ? s_cu[i] : a.cu_q[i]; };
-
+  };
+  load(0);
   // Request of packed token tk: the last b with cu[b] <= tk (empty requests
   // share their offset with the next one and are skipped by "last").
+  const cint* cu = (const cint*)a.cu_q;
   int lo = 0, hi = a.B;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (cu(mid) <= tk) lo = mid;
+    if (cu[mid] <= tk) lo = mid;
     else hi = mid;
   }
   const int b = lo;
-  const int c0 = cu(b), n = cu(b + 1) - c0;
+  const int c0 = cu[b], n = cu[b + 1] - c0;
   const int i = tk - c0;
   if (i < 0 || i >= n) return;
-  const int pos = (STAGED ? s_len[b] : a.seqlens[b]) - n + i;
+  const int pos = ((const cint*)a.seqlens)[b] - n + i;
   if (pos < 0) return;
   const int pg = pos / kPage;
   if (pg >= a.stride) return;
-  const int pid = a.page_table[(size_t)b * a.stride + pg];
+  const int pid = ((const cint*)a.page_table)[(size_t)b * a.stride + pg];
   if ((unsigned)pid >= (unsigned)a.num_pages) return;
+  const int slot = pos % kPage;
+  for (int base = 0; base < units; base += 64 * P) {
+    if (base > 0) load(base);
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int u = base + lane + 64 * p;
+      if (u < units) {
+        const int g = u / kUnitsPerRow, c = u % kUnitsPerRow;
+        const size_t dst = (((size_t)pid * a.Hkv + g) * kPage + slot) * kUnitsPerRow + c;
+        reinterpret_cast<u32x4_t*>(a.k_pages)[dst] = kv[p];
+        reinterpret_cast<u32x4_t*>(a.v_pages)[dst] = vv[p];
+      }
+    }
+  }
+}
 
-  const size_t dst = (((size_t)pid * a.Hkv + g) * kPage + pos % kPage) * kUnitsPerRow + c;
-  reinterpret_cast<u32x4_t*>(a.k_pages)[dst] = kv;
-  reinterpret_cast<u32x4_t*>(a.v_pages)[dst] = vv;
+template <int P>
+hipError_t launch_p(const AppendArgs& a, hipStream_t s) {
+  const int64_t blocks = ((int64_t)a.T + 3) / 4;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(kv_append_kernel<P>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s) {
-  const int64_t units = (int64_t)a.T * a.Hkv * kUnitsPerRow;
-  if (units == 0) return hipSuccess;
-  const int64_t blocks = (units + 255) / 256;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (a.B <= kStagedReqs)
-    hipLaunchKernelGGL(kv_append_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(kv_append_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, a);
-  return hipGetLastError();
+  if ((int64_t)a.T * a.Hkv == 0) return hipSuccess;
+  const int per = (a.Hkv * kUnitsPerRow + 63) / 64;
+  if (per <= 1) return launch_p<1>(a, s);
+  if (per <= 2) return launch_p<2>(a, s);
+  return launch_p<4>(a, s);
 }
 
 }  // namespace fa

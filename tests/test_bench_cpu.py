@@ -96,3 +96,31 @@ def test_pmc_dispatches_keeps_each_dispatch_apart(tmp_path):
     disp = bench._pmc_dispatches(str(tmp_path), "fa::k<1>")
     assert [c["SQ_BUSY_CYCLES"] for c, _ in disp] == [160.0, 320.0]
     assert [t for _, t in disp] == [2.0, 1.0]  # microseconds, from each dispatch's own timestamps
+
+
+def test_time_calls_divides_each_run_by_its_calls(monkeypatch):
+    # Fake events on a fake clock: each call advances it by the next duration.
+    import sys
+    durs = iter([1.0, 2.0] + [float(x) for x in range(3, 28)])
+    clock = [0.0]
+
+    class Ev:
+        def __init__(self, enable_timing=True):
+            self.t = None
+
+        def record(self, stream=None):
+            self.t = clock[0]
+
+        def elapsed_time(self, other):
+            return other.t - self.t
+
+    def fn():
+        clock[0] += next(durs)
+
+    fake = types.SimpleNamespace(cuda=types.SimpleNamespace(Event=Ev, synchronize=lambda: None))
+    monkeypatch.setitem(sys.modules, "torch", fake)
+    out = bench.time_calls(fn, steps=25, warmup=2, stream=None, prewarm_s=0.0, runs=5)
+    # warmup takes 1 and 2; 25 calls make two runs (at least 10 calls each) of
+    # 13 and 12 calls: 3..15 and 16..27
+    assert out == [9.0] * 13 + [21.5] * 12
+    assert sum(out) == sum(range(3, 28))     # the mean is total time over calls
