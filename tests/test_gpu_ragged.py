@@ -63,11 +63,29 @@ def test_append_bit_exact(case):
     assert np.array_equal(bits(d["v"]), vp), "V pool differs from the oracle's append"
 
 
+@pytest.mark.parametrize("Hkv", [12, 40])
+def test_append_many_kv_heads(Hkv):
+    """A token's Hkv rows go over the wavefront's 64 lanes in 16-byte units, up to 4 per lane
+    at a time: 12 KV heads fill 3 of the 4 (a ragged last unit), 40 heads take three rounds,
+    the last one partial."""
+    fa = need_gpu()
+    nq, pre = [1, 65, 130], [0, 63, 200]
+    say(f"[case] kv_append Hkv={Hkv} nq={nq} prefix={pre}")
+    r = workloads.ragged_inputs(Hkv, Hkv, 128, nq, pre, wid=53, extra_pages=2)
+    d = to_dev(r)
+    fa.fa_kv_append(d["kn"], d["vn"], d["k"], d["v"], d["pt"], d["sl"], d["cu"])
+    torch.cuda.synchronize()
+    kp, vp = oracle.kv_append(bits(r.k_pages), bits(r.v_pages), r.page_table.numpy(), r.seqlens.numpy(),
+                              r.cu_seqlens_q.numpy(), bits(r.k_new), bits(r.v_new))
+    assert np.array_equal(bits(d["k"]), kp), "K pool differs from the oracle's append"
+    assert np.array_equal(bits(d["v"]), vp), "V pool differs from the oracle's append"
+
+
 @pytest.mark.parametrize("B", [1024, 1100])
 def test_append_large_batches(B):
-    """Batches of up to 1024 requests have their lengths searched in on-chip memory; larger
-    ones search device memory. Both give the oracle's pools bit for bit (empty requests and
-    requests whose new tokens start mid-page included)."""
+    """Batches of over a thousand requests (the request of each token is a binary search over
+    cu_seqlens_q) give the oracle's pools bit for bit, empty requests and requests whose new
+    tokens start mid-page included."""
     fa = need_gpu()
     rng = np.random.default_rng(B)
     nq = rng.integers(0, 4, B)
