@@ -111,8 +111,24 @@ def load():
     lib.fa_decode_plan_cascade_host.argtypes = [i32p, ci, ci, ci, ci, i32p, i32p, ci, ci, i32p, ci, i32p, ci,
                                                 i32p, C.POINTER(ci), C.POINTER(ci)]
     lib.fa_decode_plan_cascade_host.restype = ci
+    lib.fa_device_status.argtypes = [C.POINTER(C.c_uint), ci]
+    lib.fa_device_status.restype = ci
     _LIB = lib
     return lib
+
+
+# Bits of the device status word (fa.h: FA_STATUS_*).
+STATUS_BAD_PAGE = 1
+STATUS_BAD_POSITION = 2
+
+
+def device_status(clear=True):
+    """The current device's status word: FA_STATUS_* bits the kernels set
+    when they met bad device page-table metadata (read as zeros or skipped).
+    Synchronizes the device; clears the word unless clear=False."""
+    v = C.c_uint(0)
+    _check(load().fa_device_status(C.byref(v), 1 if clear else 0))
+    return v.value
 
 
 def _check(status):

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 SOURCES = ["abi.cpp", "plan.cpp", "decode.hip", "decode_mfma.hip", "prefill_f32.hip", "prefill_bf16.hip",
-           "kv_append.hip", "prefill_fp8.hip", "prefill_bwd.hip"]
+           "kv_append.hip", "prefill_fp8.hip", "prefill_bwd.hip", "status.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

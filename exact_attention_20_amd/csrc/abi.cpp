@@ -75,6 +75,25 @@ extern "C" {
 
 const char* fa_last_error(void) { return g_err.c_str(); }
 
+int fa_device_status(unsigned int* flags_out, int clear) {
+  if (!flags_out) return fail(FA_ERR_INVALID_ARGUMENT, "fa_device_status: flags_out is null");
+  unsigned* p = nullptr;
+  hipError_t e = fa::device_status_ptr(&p);
+  if (e != hipSuccess) return hip_fail(e, "fa_device_status: device status word");
+  e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "fa_device_status: synchronize");
+  unsigned v = 0;
+  e = hipMemcpy(&v, p, sizeof v, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "fa_device_status: read");
+  if (clear && v != 0) {
+    const unsigned zero = 0;
+    e = hipMemcpy(p, &zero, sizeof zero, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "fa_device_status: clear");
+  }
+  *flags_out = v;
+  return ok();
+}
+
 int fa_abi_version(void) { return 2; }
 
 int fa_prefill_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,
@@ -405,8 +424,9 @@ int fa_decode_run(const fa_decode_plan_t* plan, const void* q, const void* k_pag
   a.part_o = (float*)(ws + plan->layout.part_o_off);
   a.part_lse = (float*)(ws + plan->layout.part_lse_off);
   a.out = out; a.lse = lse;
+  hipError_t e = fa::device_status_ptr(&a.status);
+  if (e != hipSuccess) return hip_fail(e, "fa_decode_run: device status word");
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = hipSuccess;
   if (!plan->prefix_items.empty()) {
     // Cascade plan: the shared prefixes first, into their partial slots.
     fa::PrefillArgs pa;
@@ -420,6 +440,7 @@ int fa_decode_run(const fa_decode_plan_t* plan, const void* q, const void* k_pag
     pa.group_reqs = (const int32_t*)(ws + plan->layout.group_reqs_off);
     pa.splits = a.splits_per_req;
     pa.part_o = a.part_o; pa.part_lse = a.part_lse; pa.num_splits = plan->num_splits;
+    pa.status = a.status;
     e = fa::launch_prefix_bf16(pa, (int)plan->prefix_items.size(), s);
     if (e != hipSuccess) return hip_fail(e, "fa_decode_run prefix launch");
   }
@@ -615,7 +636,9 @@ int fa_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_pa
   a.k_new = k_new; a.v_new = v_new; a.k_pages = k_pages; a.v_pages = v_pages;
   a.page_table = page_table; a.seqlens = seqlens; a.cu_q = cu_seqlens_q;
   a.B = B; a.T = total_q; a.stride = max_pages_per_req; a.num_pages = num_pages; a.Hkv = Hkv; a.D = D;
-  hipError_t e = fa::launch_kv_append(a, (hipStream_t)stream);
+  hipError_t e = fa::device_status_ptr(&a.status);
+  if (e != hipSuccess) return hip_fail(e, "fa_kv_append: device status word");
+  e = fa::launch_kv_append(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "fa_kv_append launch");
   return ok();
 }
@@ -716,7 +739,9 @@ int fa_prefill_paged_run(const fa_prefill_plan_t* plan, const void* q, const voi
   a.items = (const int32_t*)workspace;
   a.page_table = page_table; a.seqlens = seqlens; a.cu_q = cu_seqlens_q;
   a.stride = plan->stride; a.num_pages = plan->num_pages;
-  hipError_t e = fa::launch_prefill_paged_bf16(a, plan->n_items, (hipStream_t)stream);
+  hipError_t e = fa::device_status_ptr(&a.status);
+  if (e != hipSuccess) return hip_fail(e, "fa_prefill_paged_run: device status word");
+  e = fa::launch_prefill_paged_bf16(a, plan->n_items, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "fa_prefill_paged_run launch");
   return ok();
 }

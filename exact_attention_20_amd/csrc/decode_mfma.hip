@@ -192,9 +192,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     int w0 = p0;
     int tbl = -1;
     float kscl = 0.f, vscl = 0.f;
+    int bad_page = 0;  // per lane (a vector register: the scalar ones are all in use)
     auto load_window = [&]() {
       const int pp = w0 + lane;
       tbl = pp < p1 ? table[pp] : -1;
+      // A page id outside the pool reads as zeros (below); that it happened is
+      // noted here and reported once the item is done (no memory atomic in
+      // the page loop).
+      bad_page |= pp < p1 && (unsigned)tbl >= (unsigned)a.num_pages;
       if constexpr (FP8) {
         const bool ok = (unsigned)tbl < (unsigned)a.num_pages;
         kscl = ok ? a.k_scale[(size_t)tbl * a.Hkv + g] : 0.f;
@@ -368,6 +373,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     }
     __syncthreads();
     finish_work_item<G>(a, b, g, split, s_m, s_l, s_o);
+    if (__builtin_amdgcn_ballot_w64(bad_page != 0) != 0 && lane == 0) report_status(a.status, kStatusBadPage);
     __syncthreads();  // the next item reuses this workgroup's LDS
   }
 }

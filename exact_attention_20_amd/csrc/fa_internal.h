@@ -37,6 +37,7 @@ struct PrefillArgs {
   float* part_o;              // [B, Hq, num_splits, D]
   float* part_lse;            // [B, Hq, num_splits]
   int num_splits;
+  unsigned* status;           // device status word (paged modes report bad page ids)
   uint8_t kv_map[kMaxHeads];
 };
 
@@ -64,6 +65,15 @@ hipError_t launch_attention_bwd(const BwdLaunch& l, hipStream_t s);
 // on the current device (looked up once per device).
 constexpr size_t kBwdScratchBytes = size_t(32) << 20;
 hipError_t bwd_scratch(void** ptr);
+
+// ---------------------------------------------------------------- device status
+// One word per device that kernels OR bits into when they meet bad device
+// metadata and skip it (status.hip). The bits are those of fa.h's
+// fa_device_status.
+constexpr unsigned kStatusBadPage = 1u;      // a page-table entry outside [0, num_pages)
+constexpr unsigned kStatusBadPosition = 2u;  // an appended token past its page-table row
+// Device address of the current device's status word.
+hipError_t device_status_ptr(unsigned** ptr);
 
 // Query rows per work item of the bf16 prefill kernel (ragged plan unit).
 constexpr int kPrefillRows = 256;
@@ -96,6 +106,7 @@ struct AppendArgs {
   const int32_t* seqlens;     // [B]
   const int32_t* cu_q;        // [B + 1]
   int B, T, stride, num_pages, Hkv, D;
+  unsigned* status;           // device status word
 };
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
 
@@ -130,6 +141,7 @@ struct DecodeArgs {
   float* part_lse;                // [B, Hq, num_splits]
   void* out;                      // [B, Hq, D] bf16
   float* lse;                     // [B, Hq]
+  unsigned* status;               // device status word
 };
 
 hipError_t launch_decode_split(const DecodeArgs& a, int group, int fp8, hipStream_t s);

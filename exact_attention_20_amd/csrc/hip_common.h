@@ -60,4 +60,8 @@ __device__ __forceinline__ float shfl_xor_f32(float x, int m) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ORs `bits` into the device status word (one lane of the caller does it;
+// rare paths only: bad device metadata).
+__device__ __forceinline__ void report_status(unsigned* status, unsigned bits) { atomicOr(status, bits); }
+
 }  // namespace fa

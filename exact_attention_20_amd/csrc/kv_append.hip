@@ -60,11 +60,22 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   const int i = tk - c0;
   if (i < 0 || i >= n) return;
   const int pos = ((const cint*)a.seqlens)[b] - n + i;
-  if (pos < 0) return;
+  if (pos < 0) {  // more new tokens than the request's length: not written, reported
+    if (lane == 0) report_status(a.status, kStatusBadPosition);
+    return;
+  }
   const int pg = pos / kPage;
-  if (pg >= a.stride) return;
+  // Tokens past their page-table row, or whose page id lies outside the
+  // pool, are not written; either is reported in the device status word.
+  if (pg >= a.stride) {
+    if (lane == 0) report_status(a.status, kStatusBadPosition);
+    return;
+  }
   const int pid = ((const cint*)a.page_table)[(size_t)b * a.stride + pg];
-  if ((unsigned)pid >= (unsigned)a.num_pages) return;
+  if ((unsigned)pid >= (unsigned)a.num_pages) {
+    if (lane == 0) report_status(a.status, kStatusBadPage);
+    return;
+  }
   const int slot = pos % kPage;
   for (int base = 0; base < units; base += 64 * P) {
     if (base > 0) load(base);

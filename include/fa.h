@@ -65,6 +65,26 @@ typedef enum {
 /* Message for the last error on the calling thread ("" after success). */
 const char* fa_last_error(void);
 
+/* Bits of the device status word (fa_device_status). */
+enum {
+  FA_STATUS_BAD_PAGE = 1,     /* a page-table entry outside [0, num_pages) was met */
+  FA_STATUS_BAD_POSITION = 2  /* an appended token's position was negative or past its table row */
+};
+
+/*
+ * fa_device_status -- the bits the kernels OR-ed into the current device's
+ * status word, since it was last cleared, when they met bad DEVICE metadata
+ * in the logical-to-physical page table ("Flash Attention & Paged Attention"
+ * blog, "2. PagedAttention"). Host checks only see the host copies a plan is
+ * built from; the kernels read such a page as zeros (attention) or do not
+ * write it (KV append), and set a bit here.
+ *   flags_out  host; receives the word
+ *   clear      nonzero: reset the word to 0 after reading it
+ * Synchronizes the current device first, so every call enqueued before it
+ * has finished. One word per device, shared by every call on that device.
+ */
+int fa_device_status(unsigned int* flags_out, int clear);
+
 /* Library ABI version (bumped on any signature change). */
 int fa_abi_version(void);
 

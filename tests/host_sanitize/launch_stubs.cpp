@@ -15,6 +15,7 @@ hipError_t launch_prefill_fp8(const void*, const void*, const void*, const float
 }
 hipError_t launch_attention_bwd(const BwdLaunch&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t bwd_scratch(void**) { return hipErrorNoDevice; }
+hipError_t device_status_ptr(unsigned**) { return hipErrorNoDevice; }
 hipError_t launch_prefill_paged_bf16(const PrefillArgs&, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_prefix_bf16(const PrefillArgs&, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_kv_append(const AppendArgs&, hipStream_t) { return hipErrorNoDevice; }

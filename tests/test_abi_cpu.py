@@ -257,3 +257,9 @@ def test_workspace_size(lib):
     n = fa.fa_decode_workspace_size(L, 8, 2, 128, 0, 16)
     items, splits, ns, _, _ = fa.fa_decode_plan_host(L, 8, 8, 2, 0, 16)
     assert n >= len(items) * 16 + 3 * 4 + 3 * 8 * ns * 129 * 4
+
+
+def test_device_status_rejects_null(lib):
+    # Checked before any HIP call, so it runs without a GPU.
+    assert lib.fa_device_status(None, 0) == 1
+    assert b"flags_out" in lib.fa_last_error()
