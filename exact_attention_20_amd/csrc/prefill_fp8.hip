@@ -46,6 +46,7 @@ constexpr int kBc = 64;         // keys per tile
 constexpr int kRow = kD;        // bytes per fp8 row
 constexpr int kTile = kBc * kRow;  // 8 KB
 constexpr float kTau = 8.0f;    // lazy max threshold (log2 units): P <= 2^8 < 448
+constexpr float kSumBound = 256.0f;  // 2^kTau: a sum of weights at or below it bounds each of them
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
@@ -233,15 +234,15 @@ void prefill_fp8_kernel(Fp8Args a, int n_qtiles, int nbh) {
       m = mn;
     }
   };
-  // P = exp2(s*c - m) -> e4m3 bytes (byte 16*h2 + i), fp32 sums, O^T += V^T P^T;
-  // with kb >= 0 the next tile's S^T from K buffer kb is computed in the same
-  // straight-line block, one QK product after each PV product.
+  // P = exp2(s*c - m) -> e4m3 bytes (byte 16*h2 + i) with the running max as
+  // it stands, and the tile's fp32 sums te[w] (each over 8 of the lane's
+  // scores).
   // P bytes of the current tile, kept in one place across tiles: each
   // conversion below keeps the other half of its register, so giving it the
   // previous tile's word (overwritten in full by the pair of conversions)
   // saves a register clear or copy per word.
   int pw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  auto exp_pv_qk = [&](int vbuf, const f32x16_t (&s)[2], int kb, f32x16_t (&n)[2]) {
+  auto exps = [&](const f32x16_t (&s)[2], float (&te)[4]) {
     const float mu = m == kNegInf ? 0.f : m;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
@@ -253,8 +254,14 @@ void prefill_fp8_kernel(Fp8Args a, int n_qtiles, int nbh) {
         int& word = pw[4 * h2 + w];
         word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], word, false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
-        le[w] += (p[0] + p[1]) + (p[2] + p[3]);
+        const float g = (p[0] + p[1]) + (p[2] + p[3]);
+        te[w] = h2 == 0 ? g : te[w] + g;
       }
+  };
+  // O^T += V^T P^T; with kb >= 0 the next tile's S^T from K buffer kb is
+  // computed in the same straight-line block, one QK product after each PV
+  // product.
+  auto pv_qk = [&](int vbuf, int kb, f32x16_t (&n)[2]) {
     const i32x8_t pf = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
     const char* vl = v_lds + vbuf * kTile;
     const char* kl = k_lds + (kb < 0 ? 0 : kb) * kTile;
@@ -274,6 +281,10 @@ void prefill_fp8_kernel(Fp8Args a, int n_qtiles, int nbh) {
         n[h2] = kk == 0 ? mfma8_first(av, qreg[kk]) : mfma8(av, qreg[kk], n[h2]);
       }
     }
+  };
+  auto add_sums = [&](const float (&te)[4]) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) le[w] += te[w];
   };
 
   auto prefetch = [&](int t) {
@@ -304,8 +315,26 @@ void prefill_fp8_kernel(Fp8Args a, int n_qtiles, int nbh) {
   auto main_step = [&](auto par, int t, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
     constexpr int PAR = decltype(par)::value;
     prefetch(t);
-    update_max(cur);
-    exp_pv_qk(PAR, cur, 1 - PAR, nxt);
+    // The lazy max only has to keep every weight at or below 2^kTau, and a
+    // lane's sum of 8 weights bounds each of them: the tile's weights are
+    // first formed with the max as it stands, and only if some sum exceeds
+    // 2^kTau (the first tile of a row, or scores that rose by about kTau) is
+    // the tile redone with the row max and the lazy move of the max. That
+    // takes the max tree and its cross-lane exchange and vote off the common
+    // path, where they stood between the scores and the first exponential.
+    float te[4];
+    bool redo = true;
+    if (__builtin_amdgcn_ballot_w64(m == kNegInf) == 0) {
+      exps(cur, te);
+      const float big = fmaxf(fmaxf(te[0], te[1]), fmaxf(te[2], te[3]));
+      redo = __builtin_amdgcn_ballot_w64(!(big <= kSumBound)) != 0;
+    }
+    if (__builtin_expect(redo, 0)) {
+      update_max(cur);
+      exps(cur, te);
+    }
+    add_sums(te);
+    pv_qk(PAR, 1 - PAR, nxt);
     wait_loads();
     __syncthreads();
   };
@@ -332,7 +361,10 @@ void prefill_fp8_kernel(Fp8Args a, int n_qtiles, int nbh) {
     if (use) {
       mask(t, sc);
       update_max(sc);
-      exp_pv_qk(t & 1, sc, next ? (t + 1) & 1 : -1, sn);
+      float te[4];
+      exps(sc, te);
+      add_sums(te);
+      pv_qk(t & 1, next ? (t + 1) & 1 : -1, sn);
     } else if (next) {
       qk((t + 1) & 1, sn);
     }
