@@ -125,13 +125,18 @@ int fa_prefill_fwd(const void* q, const void* k, const void* v, void* out, float
  *   out  [B, Hq, Sq, 128] bf16 (nearest even), lse [B, Hq, Sq] fp32 natural log
  *   causal, scale as for fa_prefill_fwd (bottom-right mask; <= 0 selects 1/sqrt(128));
  *   query head h reads KV head h / (Hq / Hkv).
- * Both products run on the fp8 matrix cores with fp32 accumulation: the
- * scores are exact for the dequantised inputs up to fp32 rounding, the
- * softmax weights P are rounded to e4m3 (nearest even) for the P V product,
- * and O is divided by the fp32 sum of the unrounded weights. Each weight
- * carries a relative error of at most 2^-4 before normalisation, so
- * |O - O_exact| <= 2^-4 * sum_j w_j |v_j| (plus bf16 rounding) per element,
- * with w the exact weights; the LSE is exact up to fp32 rounding.
+ * Both products run on the fp8 matrix cores with fp32 accumulation. The
+ * matrix core sums each block of 64 products exactly when they are of
+ * similar size, but drops the low bits of products far below the largest of
+ * their block (measured on gfx950: error up to about 2^-12.4 of that largest
+ * product). So a score, and the LSE with it, carries an absolute error of up
+ * to about 2^-12 * scale * sum over its two blocks of max_d |q_d k_d|: below
+ * 1e-4 for inputs without outlier dims, but not small when one dim carries a
+ * large score. The softmax weights P are rounded to e4m3 (nearest even) for
+ * the P V product, and O is divided by the fp32 sum of the unrounded
+ * weights. Each weight carries a relative error of at most 2^-4 before
+ * normalisation, so |O - O_exact| <= 2^-4 * sum_j w_j |v_j| (plus bf16
+ * rounding and the score error above) per element, with w the exact weights.
  * Limits: D = 128; Sk * 128 < 2^31.
  */
 int fa_prefill_fp8_fwd(const void* q, const void* k, const void* v, const float* q_scale,

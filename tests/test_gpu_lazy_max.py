@@ -7,14 +7,18 @@ scores of every row ramp with the key's logical position, about 0.25 natural
 units per key (about 23 exp2 units per 64-key tile or page), so the max moves
 on nearly every tile; a sawtooth variant lets it rise, fall back and rise
 above its old level. The oracle gets the same bf16 inputs, so an error in the
-rescale path shows up against it."""
+rescale path shows up against it. The fp8 prefill gets the same offsets
+spread over all 128 dims, quantised per head to e4m3, against the oracle on
+the dequantised values (gfx950's fp8 matrix product drops the low bits of
+products far below the largest of their 64-product block, so the ramp is not
+carried by one dim there: every product of a score is then of similar size)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import workloads
-from parity import check, f64, need_gpu, say
+from parity import check, check_fp8_prefill, f64, fp8_weight_bound, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -82,3 +86,45 @@ def test_decode_moving_max(shape, num_splits):
     O, L = oracle.paged_decode(f64(q), kp.float().numpy(), kv.v_pages.float().numpy(), kv.page_table.numpy(),
                                kv.seqlens.numpy(), SCALE)
     check(f"decode moving max {shape} splits={num_splits}", f64(out), O, f64(lse), L, "bf16")
+
+
+def fp8_moving_max_inputs(B, Hq, Hkv, S, shape, wid=63):
+    """Float32 Q/K/V quantised per head: (q8, k8, v8, q_scale, k_scale,
+    v_scale), host tensors. Query dim d is sign_d (1 + 0.1 n) and key dim d of
+    position j is sign_d offset(j) / (D scale) + 0.1 n, with one random sign
+    per dim, so every score carries the offset of its key spread evenly over
+    the dims."""
+    D = 128
+    q = workloads.rng(wid, workloads.STREAM_Q).standard_normal(size=(B, Hq, S, D), dtype=np.float32)
+    k = workloads.rng(wid, workloads.STREAM_K).standard_normal(size=(B, Hkv, S, D), dtype=np.float32)
+    v = workloads.rng(wid, workloads.STREAM_V).standard_normal(size=(B, Hkv, S, D), dtype=np.float32)
+    sign = np.where(workloads.rng(wid, workloads.STREAM_PERM).random(D) < 0.5, -1.0, 1.0).astype(np.float32)
+    q = sign * (1.0 + 0.1 * q)
+    r = (offset(np.arange(S), shape) / (D * SCALE)).astype(np.float32)
+    k = sign * r[:, None] + 0.1 * k
+    q8, qs = workloads.quantise_heads_e4m3fn(q)
+    k8, ks = workloads.quantise_heads_e4m3fn(k)
+    v8, vs = workloads.quantise_heads_e4m3fn(v)
+    return q8, k8, v8, qs, ks, vs
+
+
+def dequantise(codes, scale):
+    return oracle.e4m3fn_to_float(codes.numpy()) * scale.numpy().astype(np.float64)[:, :, None, None]
+
+
+@pytest.mark.parametrize("shape", ["ramp", "sawtooth"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_prefill_moving_max(shape, causal):
+    fa = need_gpu()
+    B, Hq, Hkv, S = 1, 4, 2, 777
+    say(f"[case] fp8 prefill moving max {shape} causal={causal}")
+    q8, k8, v8, qs, ks, vs = fp8_moving_max_inputs(B, Hq, Hkv, S, shape)
+    out, lse = fa.prefill_fp8(q8.cuda(), k8.cuda(), v8.cuda(), qs.cuda(), ks.cuda(), vs.cuda(), causal, SCALE)
+    torch.cuda.synchronize()
+    qd, kd, vd = dequantise(q8, qs), dequantise(k8, ks), dequantise(v8, vs)
+    O, L = oracle.prefill(qd, kd, vd, SCALE, causal)
+    bound = np.zeros_like(O)
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        bound[0, h] = fp8_weight_bound(qd[0, h], kd[0, g], vd[0, g], SCALE, causal)
+    check_fp8_prefill(f"fp8 prefill moving max {shape} causal={causal}", f64(out), O, bound, f64(lse), L)
