@@ -128,3 +128,29 @@ def test_fp8_prefill_moving_max(shape, causal):
         g = h // (Hq // Hkv)
         bound[0, h] = fp8_weight_bound(qd[0, h], kd[0, g], vd[0, g], SCALE, causal)
     check_fp8_prefill(f"fp8 prefill moving max {shape} causal={causal}", f64(out), O, bound, f64(lse), L)
+
+
+@pytest.mark.parametrize("shape", ["ramp", "sawtooth"])
+def test_cascade_moving_max(shape):
+    """Shared-prefix decode: the prefix pass (prefill kernel over the group's
+    pages, rows = members x heads) and the suffix split kernel both see the
+    max move, and the merge combines their partials."""
+    fa = need_gpu()
+    groups, suffix, pp, Hq, Hkv = [0, 0, 0, -1, 1, 1], [5, 300, 900, 1200, 64, 0], [24, 9], 8, 2
+    say(f"[case] cascade moving max {shape}")
+    r = workloads.shared_prefix_inputs(Hq, Hkv, 128, groups, suffix, pp, wid=64, nan_tails=False)
+    q, kp = r.q.float(), r.k_pages.float()
+    shape_query(q)
+    table = r.page_table.numpy()
+    for b, n in enumerate(r.seqlens.tolist()):
+        t = np.arange(n)
+        kp[table[b, t // 64], :, t % 64, 0] = key_dim0(t, shape)[:, None].expand(n, Hkv)
+    q, kp = q.to(torch.bfloat16), kp.to(torch.bfloat16)
+    plan = fa.fa_decode_plan_cascade(r.seqlens, r.page_table, r.num_pages, Hq, Hkv, r.prefix_group,
+                                     r.prefix_pages.tolist())
+    out, lse = fa.decode(plan, q.cuda(), kp.cuda(), r.v_pages.cuda(), r.page_table.cuda(), r.seqlens.cuda(),
+                         scale=SCALE)
+    torch.cuda.synchronize()
+    O, L = oracle.paged_decode(f64(q), kp.float().numpy(), r.v_pages.float().numpy(), table, r.seqlens.numpy(),
+                               SCALE)
+    check(f"cascade moving max {shape}", f64(out), O, f64(lse), L, "bf16")
