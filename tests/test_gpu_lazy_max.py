@@ -154,3 +154,31 @@ def test_cascade_moving_max(shape):
     O, L = oracle.paged_decode(f64(q), kp.float().numpy(), r.v_pages.float().numpy(), table, r.seqlens.numpy(),
                                SCALE)
     check(f"cascade moving max {shape}", f64(out), O, f64(lse), L, "bf16")
+
+
+@pytest.mark.parametrize("shape", ["ramp", "sawtooth"])
+def test_ragged_prefill_moving_max(shape):
+    """Ragged paged prefill after the KV append: cached prefix keys and the
+    appended new keys carry the ramp of their logical positions."""
+    fa = need_gpu()
+    nq, pre, Hq, Hkv = [1, 300, 129, 700], [0, 100, 1500, 64], 8, 2
+    say(f"[case] ragged prefill moving max {shape}")
+    r = workloads.ragged_inputs(Hq, Hkv, 128, nq, pre, wid=65, poison=False)
+    q, kp, kn = r.q.float(), r.k_pages.float(), r.k_new.float()
+    shape_query(q)
+    table, cu = r.page_table.numpy(), r.cu_seqlens_q.numpy()
+    for b in range(len(nq)):
+        t = np.arange(pre[b])
+        kp[table[b, t // 64], :, t % 64, 0] = key_dim0(t, shape)[:, None].expand(len(t), Hkv)
+        kn[cu[b]:cu[b + 1], :, 0] = key_dim0(pre[b] + np.arange(nq[b]), shape)[:, None].expand(nq[b], Hkv)
+    r.q, r.k_pages, r.k_new = q.to(torch.bfloat16), kp.to(torch.bfloat16), kn.to(torch.bfloat16)
+    d = dict(q=r.q.cuda(), kn=r.k_new.cuda(), vn=r.v_new.cuda(), k=r.k_pages.cuda(), v=r.v_pages.cuda(),
+             pt=r.page_table.cuda(), sl=r.seqlens.cuda(), cu=r.cu_seqlens_q.cuda())
+    fa.fa_kv_append(d["kn"], d["vn"], d["k"], d["v"], d["pt"], d["sl"], d["cu"])
+    plan = fa.fa_prefill_paged_plan(r.seqlens, r.cu_seqlens_q, r.page_table, r.num_pages, Hq, Hkv)
+    out, lse = fa.prefill_paged(plan, d["q"], d["k"], d["v"], d["pt"], d["sl"], d["cu"], SCALE)
+    torch.cuda.synchronize()
+    kpo, vpo = oracle.kv_append(r.k_pages.float().numpy(), r.v_pages.float().numpy(), table, r.seqlens.numpy(),
+                                cu, r.k_new.float().numpy(), r.v_new.float().numpy())
+    O, L = oracle.paged_prefill(f64(r.q), kpo, vpo, table, r.seqlens.numpy(), cu, SCALE)
+    check(f"ragged prefill moving max {shape}", f64(out), O, f64(lse), L, "bf16")
