@@ -182,3 +182,31 @@ def test_ragged_prefill_moving_max(shape):
                                 cu, r.k_new.float().numpy(), r.v_new.float().numpy())
     O, L = oracle.paged_prefill(f64(r.q), kpo, vpo, table, r.seqlens.numpy(), cu, SCALE)
     check(f"ragged prefill moving max {shape}", f64(out), O, f64(lse), L, "bf16")
+
+
+@pytest.mark.parametrize("shape", ["ramp", "sawtooth"])
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_fp8_decode_moving_max(shape, num_splits):
+    """Paged decode over an fp8 cache (codes with one scale per page and KV
+    head), the same construction quantised after the ramp is set."""
+    fa = need_gpu()
+    lengths = [1, 65, 700, 2049]
+    Hq, Hkv, D = 8, 2, 128
+    say(f"[case] fp8 decode moving max {shape} splits={num_splits}")
+    kv = workloads.paged_inputs(len(lengths), Hq, Hkv, D, "bf16", lengths, 66, nan_tails=False)
+    q, kp = kv.q.float(), kv.k_pages.float()
+    shape_query(q)
+    table = kv.page_table.numpy()
+    for b, n in enumerate(lengths):
+        t = np.arange(n)
+        kp[table[b, t // 64], :, t % 64, 0] = key_dim0(t, shape)[:, None].expand(n, Hkv)
+    q = q.to(torch.bfloat16)
+    k8, ks = workloads._quantise_e4m3fn(kp.numpy().copy(), [], False)
+    v8, vs = workloads._quantise_e4m3fn(kv.v_pages.float().numpy().copy(), [], False)
+    plan = fa.fa_decode_plan(kv.seqlens, kv.page_table, kv.num_pages, Hq, Hkv, D, fa.FP8_E4M3FN, num_splits)
+    out, lse = fa.decode(plan, q.cuda(), k8.cuda(), v8.cuda(), kv.page_table.cuda(), kv.seqlens.cuda(),
+                         ks.cuda(), vs.cuda(), SCALE)
+    torch.cuda.synchronize()
+    O, L = oracle.paged_decode(f64(q), k8.numpy(), v8.numpy(), table, kv.seqlens.numpy(), SCALE,
+                               ks.numpy(), vs.numpy())
+    check(f"fp8 decode moving max {shape} splits={num_splits}", f64(out), O, f64(lse), L, "fp8")
