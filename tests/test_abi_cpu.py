@@ -263,3 +263,43 @@ def test_device_status_rejects_null(lib):
     # Checked before any HIP call, so it runs without a GPU.
     assert lib.fa_device_status(None, 0) == 1
     assert b"flags_out" in lib.fa_last_error()
+
+
+def test_host_calls_from_many_threads(lib):
+    """The host side is safe to call from several threads at once (ctypes
+    drops the GIL around each call): plans match the single-threaded ones,
+    and each thread reads back its own last error."""
+    import threading
+
+    rng = np.random.default_rng(11)
+    inputs = [rng.integers(1, 9000, size=int(rng.integers(200, 600))).astype(np.int32) for _ in range(8)]
+    ref = [fa.fa_decode_plan_host(sl, 160, 32, 8) for sl in inputs]
+    i32 = C.POINTER(C.c_int32)
+    failures = []
+
+    def worker(t):
+        try:
+            for _ in range(30):
+                items, splits, ns, ch, grid = fa.fa_decode_plan_host(inputs[t], 160, 32, 8)
+                r = ref[t]
+                if not (np.array_equal(items.numpy(), r[0].numpy()) and np.array_equal(splits.numpy(), r[1].numpy())
+                        and (ns, ch, grid) == r[2:]):
+                    failures.append(f"thread {t}: plan differs")
+                    return
+                # An error of this thread's own: Hq not a multiple of Hkv, with values naming the thread.
+                hq = 16 + 2 * t + 1
+                sl = inputs[t]
+                size = lib.fa_decode_workspace_size(C.cast(sl.ctypes.data, i32), len(sl), hq, 2, 128, 0, 256)
+                msg = lib.fa_last_error().decode()
+                if size != 0 or f"({hq}, 2)" not in msg:
+                    failures.append(f"thread {t}: size {size}, last error {msg!r}")
+                    return
+        except Exception as e:  # noqa: BLE001 - reported below
+            failures.append(f"thread {t}: {e!r}")
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not failures, failures

@@ -1,9 +1,12 @@
-"""The host half of the library under AddressSanitizer and UndefinedBehaviorSanitizer.
+"""The host half of the library under AddressSanitizer and UndefinedBehaviorSanitizer,
+and under ThreadSanitizer.
 
 abi.cpp and plan.cpp (argument checks, decode / ragged / cascade plans,
 workspace layouts) are built by the host compiler with -fsanitize=address,undefined
 and stub kernel launchers, then the CPU tests that drive them through the C ABI
-run against that build in a child process. Any sanitizer report fails the test.
+run against that build in a child process. A second build with
+-fsanitize=thread runs the test that calls the host side from eight threads at
+once. Any sanitizer report fails the test.
 """
 import os
 import shutil
@@ -24,13 +27,11 @@ def _runtime(name):
     return p if os.path.isabs(p) and os.path.exists(p) else None
 
 
-@pytest.fixture(scope="module")
-def san_lib(tmp_path_factory):
+def _host_build(d, name, flags):
     if shutil.which("g++") is None or not os.path.exists(os.path.join(ROCM, "include", "hip", "hip_runtime.h")):
         pytest.skip("g++ or the HIP headers are missing")
-    d = tmp_path_factory.mktemp("hostsan")
-    lib = str(d / "libfa_host_san.so")
-    cmd = ["g++", "-std=c++17", "-O1", "-g", "-shared", "-fPIC", *SAN, "-D__HIP_PLATFORM_AMD__",
+    lib = str(d / name)
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-shared", "-fPIC", *flags, "-D__HIP_PLATFORM_AMD__",
            "-I", os.path.join(ROCM, "include"), "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            os.path.join(CSRC, "abi.cpp"), os.path.join(CSRC, "plan.cpp"),
            os.path.join(ROOT, "tests", "host_sanitize", "launch_stubs.cpp"),
@@ -38,6 +39,11 @@ def san_lib(tmp_path_factory):
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, f"sanitizer build failed:\n{' '.join(cmd)}\n{r.stderr[-4000:]}"
     return lib
+
+
+@pytest.fixture(scope="module")
+def san_lib(tmp_path_factory):
+    return _host_build(tmp_path_factory.mktemp("hostsan"), "libfa_host_san.so", SAN)
 
 
 def test_host_code_under_asan_ubsan(san_lib, tmp_path):
@@ -65,3 +71,21 @@ def test_host_code_under_asan_ubsan(san_lib, tmp_path):
     chk = subprocess.run([sys.executable, "-c", "import exact_attention_20_amd as fa; fa.load(); print(fa.lib_path())"],
                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert chk.stdout.strip().endswith("libfa_host_san.so"), chk.stdout + chk.stderr
+
+
+def test_host_code_under_tsan(tmp_path):
+    tsan = _runtime("libtsan.so")
+    if tsan is None:
+        pytest.skip("ThreadSanitizer runtime not found")
+    lib = _host_build(tmp_path, "libfa_host_tsan.so", ["-fsanitize=thread", "-fno-omit-frame-pointer"])
+    logs = tmp_path / "reports"
+    logs.mkdir()
+    env = dict(os.environ)
+    env.update(FA_LIBRARY=lib, LD_PRELOAD=tsan, TSAN_OPTIONS=f"log_path={logs}/tsan", HIP_VISIBLE_DEVICES="")
+    r = subprocess.run([sys.executable, "-m", "pytest", "tests/test_abi_cpu.py", "-q", "-x", "-m", "not gpu",
+                        "-k", "many_threads", "-p", "no:cacheprovider"], cwd=ROOT, env=env, capture_output=True,
+                       text=True, timeout=600)
+    out = r.stdout + r.stderr
+    reports = sorted(logs.iterdir())
+    assert not reports, "sanitizer report:\n" + "\n".join(p.read_text()[-4000:] for p in reports)
+    assert r.returncode == 0 and "1 passed" in out, f"threaded test failed against the TSan build:\n{out[-6000:]}"
