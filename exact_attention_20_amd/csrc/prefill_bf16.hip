@@ -322,7 +322,10 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
   }
 
   // Tile t holds work for query block qb unless it lies wholly above its diagonal.
-  auto blk_active = [&](int t, int qb) { return !(causal && t * kBc > wq0[qb] + 31 + off); };
+  // A wavefront's query block takes part in tile t unless all its rows lie
+  // past Sq (the padding of a unit's last row tile) or, causal, before the
+  // tile's first key.
+  auto blk_active = [&](int t, int qb) { return wq0[qb] < Sq && !(causal && t * kBc > wq0[qb] + 31 + off); };
   auto any_active = [&](int t) { return blk_active(t, QB - 1); };
 
   // S^T for every query block from K buffer kbuf.
