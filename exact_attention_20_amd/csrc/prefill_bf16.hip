@@ -555,8 +555,6 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
     auto exps = [&](float (&tr)[4], float (&te)[4]) __attribute__((always_inline)) {
       const float mu = m[0] == kNegInf ? 0.f : m[0];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) tr[jj] = te[jj] = 0.f;
-#pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const f32x16_t& sv = (ks >> 1) ? s1 : s0;
         const int base = 8 * (ks & 1);
@@ -565,8 +563,9 @@ void prefill_bf16_kernel(PrefillArgs a, int n_qtiles, int nbh) {
           const float p0 = fast_exp2(__builtin_fmaf(sv[base + 2 * jj], c, -mu));
           const float p1 = fast_exp2(__builtin_fmaf(sv[base + 2 * jj + 1], c, -mu));
           pw[ks][jj] = pack_bf16x2(p0, p1);
-          tr[jj] = dot2_bf16(pw[ks][jj], 0x3f803f80u, tr[jj]);  // + bf16(p0) + bf16(p1)
-          te[jj] += p0 + p1;
+          // + bf16(p0) + bf16(p1); the first step starts both sums (no add of zero)
+          tr[jj] = dot2_bf16(pw[ks][jj], 0x3f803f80u, ks == 0 ? 0.f : tr[jj]);
+          te[jj] = ks == 0 ? p0 + p1 : te[jj] + (p0 + p1);
         }
       }
     };
