@@ -49,7 +49,7 @@ struct BwdArgs {
   const uint16_t* o;    // [B, Hq, Sq, D] forward output
   const uint16_t* dO;   // [B, Hq, Sq, D]
   const float* lse;     // [B, Hq, Sq] forward LSE (natural log)
-  float* delta;         // [B, Hq, Sq] D_i (written by the dQ kernel, read by dK/dV)
+  float* delta;         // [B, Hq, Sq] -D_i (written by the dQ kernel, read by dK/dV)
   float* lse2;          // [B, Hq, Sq] LSE * log2 e, +inf for a row without keys (likewise)
   uint16_t* dq;         // [B, Hq, Sq, D]
   uint16_t* dk;         // [B, Hkv, Sk, D]
@@ -212,7 +212,7 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles, int nbh) {
     const float l = a.lse[bh * Sq + qrow];
     lse2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
     if (hi == 0) {
-      a.delta[bh * Sq + qrow] = dl;
+      a.delta[bh * Sq + qrow] = -dl;  // negated: the dK/dV kernel starts dP from it
       a.lse2[bh * Sq + qrow] = lse2;
     }
   }
@@ -265,6 +265,15 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles, int nbh) {
     // S^T = K Q^T and dP^T = V dO^T: register i of lane l, half h2, is key
     // 32*h2 + 16*(i/8) + 8*hi + (i%8) of the tile, query row `qrow`.
     f32x16_t s[2], dp[2];
+    // dP^T starts from -D instead of zero: every accumulator register of this
+    // lane belongs to query row `qrow`, so the products leave dP - D directly
+    // (16 moves per tile in place of 32 subtractions). The splat is formed
+    // here each tile: kept across the loop it would hold 16 more registers.
+    float ndl1 = -dl;
+    asm volatile("" : "+v"(ndl1));
+    f32x16_t ndl;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ndl[i] = ndl1;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
 #pragma unroll
@@ -272,7 +281,7 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles, int nbh) {
         const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kl + r_off[kk] + 32 * h2 * kRow);
         const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(vl + r_off[kk] + 32 * h2 * kRow);
         s[h2] = kk == 0 ? mfma32_first(ka, qreg[kk]) : mfma32(ka, qreg[kk], s[h2]);
-        dp[h2] = kk == 0 ? mfma32_first(va, dreg[kk]) : mfma32(va, dreg[kk], dp[h2]);
+        dp[h2] = mfma32(va, dreg[kk], kk == 0 ? ndl : dp[h2]);
       }
     }
     // P^T = exp2(S^T c - lse2) with the causal / ragged-tail mask (masked
@@ -299,7 +308,7 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles, int nbh) {
             // Masked entries get a -inf argument (exp2 -> 0): a select, not a branch per element.
             arg = 32 * h2 + 16 * (i >> 3) + (i & 7) > rel ? kNegInf : arg;
           }
-          s[h2][i] = fast_exp2(arg) * (dp[h2][i] - dl);
+          s[h2][i] = fast_exp2(arg) * dp[h2][i];  // P (dP - D)
         }
         dsf[2 * h2] = pack8(s[h2], 0);
         dsf[2 * h2 + 1] = pack8(s[h2], 8);
@@ -499,12 +508,29 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
       // the prefetch loads.
       const int lh = lane_here();
       const int v_base = row_base(32 * wave_u + (lh & 31), lh >> 5);
+      // dP starts from the staged -D of each register's row, so the products
+      // leave dP - D directly (no subtraction per element).
+      f32x16_t nd;
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        const int rb = 32 * hq + 16 * h8 + 8 * hi;
+        const float4 d0 = *reinterpret_cast<const float4*>(sd + rb);
+        const float4 d1 = *reinterpret_cast<const float4*>(sd + rb + 4);
+        nd[8 * h8 + 0] = d0.x;
+        nd[8 * h8 + 1] = d0.y;
+        nd[8 * h8 + 2] = d0.z;
+        nd[8 * h8 + 3] = d0.w;
+        nd[8 * h8 + 4] = d1.x;
+        nd[8 * h8 + 5] = d1.y;
+        nd[8 * h8 + 6] = d1.z;
+        nd[8 * h8 + 7] = d1.w;
+      }
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         const int ro = (r_base ^ (32 * kk)) + 32 * hq * kRow;
         const bf16x8_t oa = *reinterpret_cast<const bf16x8_t*>(ol + ro);
         const bf16x8_t vb = *reinterpret_cast<const bf16x8_t*>(v_res + (v_base ^ (32 * kk)));
-        dp = kk == 0 ? mfma32_first(oa, vb) : mfma32(oa, vb, dp);
+        dp = mfma32(oa, vb, kk == 0 ? nd : dp);
       }
       // P and dS; rows past Sq, masked keys and keys past Sk give 0.
 #pragma unroll
@@ -512,10 +538,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
         const int rb = 32 * hq + 16 * h8 + 8 * hi;  // first row of these 8 registers
         const float4 l0 = *reinterpret_cast<const float4*>(sl + rb);
         const float4 l1 = *reinterpret_cast<const float4*>(sl + rb + 4);
-        const float4 d0 = *reinterpret_cast<const float4*>(sd + rb);
-        const float4 d1 = *reinterpret_cast<const float4*>(sd + rb + 4);
         const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-        const float dvv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
         // Rows x of these 8 that this lane's key sees: x in [xlo, xhi) (row
         // below Sq, causal key <= row + off, key below Sk). Masked entries
         // get a -inf argument (exp2 -> 0), and a row without keys (LSE -inf)
@@ -529,7 +552,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
             const int i = 8 * h8 + x;
             const float p = fast_exp2(__builtin_fmaf(s[i], c, -lv[x]));
             s[i] = p;
-            dp[i] = p * (dp[i] - dvv[x]);
+            dp[i] = p * dp[i];  // P (dP - D)
           }
         } else {
           const int key_h = kt * BK + 32 * wave_u + (lane_here() & 31);
@@ -540,7 +563,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
             const int i = 8 * h8 + x;
             const float p = fast_exp2(((x >= xlo) & (x < xhi)) ? __builtin_fmaf(s[i], c, -lv[x]) : kNegInf);
             s[i] = p;
-            dp[i] = p * (dp[i] - dvv[x]);
+            dp[i] = p * dp[i];  // P (dP - D)
           }
         }
         __builtin_amdgcn_sched_barrier(0);
