@@ -355,10 +355,14 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
   // Double-buffered Q, dO, LSE and D tiles, each buffer its own LDS variable
   // (named at compile time by the step loops, unrolled by two), so that a
   // step's LDS reads do not wait for the loads filling the other buffers.
-  __shared__ __attribute__((aligned(16))) char q_lds0[kTile];
-  __shared__ __attribute__((aligned(16))) char q_lds1[kTile];
-  __shared__ __attribute__((aligned(16))) char o_lds0[kTile];  // dO
-  __shared__ __attribute__((aligned(16))) char o_lds1[kTile];
+  // The Q/dO ring is read every step through row and transposing offsets.
+  // Its wider alignment places it first, below 64 KB, where a DS
+  // instruction's 16-bit offset holds each buffer's base; the resident V
+  // block follows it. The other way round every ring read took an add.
+  __shared__ __attribute__((aligned(1024))) char q_lds0[kTile];
+  __shared__ __attribute__((aligned(1024))) char q_lds1[kTile];
+  __shared__ __attribute__((aligned(1024))) char o_lds0[kTile];  // dO
+  __shared__ __attribute__((aligned(1024))) char o_lds1[kTile];
   __shared__ __attribute__((aligned(16))) float st_lse0[kBc];
   __shared__ __attribute__((aligned(16))) float st_lse1[kBc];
   __shared__ __attribute__((aligned(16))) float st_d0[kBc];
