@@ -168,7 +168,7 @@ int fa_prefill_fp8_fwd(const void* q, const void* k, const void* v, const float*
 
 size_t fa_prefill_bwd_workspace_size(int B, int Hq, int Sq) {
   if (B < 1 || Hq < 1 || Sq < 0) return 0;
-  // D_i, then LSE_i in log2 units, one fp32 array each.
+  // -D_i, then LSE_i in log2 units, one fp32 array each.
   return 2 * (((size_t)B * Hq * (size_t)Sq * sizeof(float) + 255) / 256 * 256) + 256;
 }
 

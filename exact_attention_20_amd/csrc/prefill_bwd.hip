@@ -616,7 +616,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles, int nbg) {
 
 }  // namespace
 
-// Per-row arrays of the backward (D_i, then LSE_i in log2 units) for the entry
+// Per-row arrays of the backward (-D_i, then LSE_i in log2 units) for the entry
 // point that allocates nothing. Each GPU the library runs on holds its own
 // copy until the process ends; every call on that GPU shares it, so calls
 // that overlap on one GPU race. The dQ kernel writes every row < Sq before

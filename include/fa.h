@@ -159,7 +159,7 @@ int fa_prefill_fp8_fwd(const void* q, const void* k, const void* v, const float*
  *   dk, dv    [B, Hkv, Sk, 128] bf16, written; a KV head's gradient sums the
  *             query heads h with h / (Hq / Hkv) equal to it
  *   workspace device buffer of >= fa_prefill_bwd_workspace_size(B, Hq, Sq)
- *             bytes (holds D_i = sum_d dO_id O_id and LSE_i in log2 units,
+ *             bytes (holds -D_i, D_i = sum_d dO_id O_id, and LSE_i in log2 units,
  *             written by the first kernel for the second)
  * dS = P * (dP - D) with P = exp(scale S - LSE), dP = dO V^T; dQ = scale dS K,
  * dK = scale dS^T Q, dV = P^T dO; fp32 accumulation, bf16 products (P and dS
